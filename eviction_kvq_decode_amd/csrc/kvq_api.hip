@@ -1,0 +1,76 @@
+// kvq_api.hip -- the extern "C" entry points declared in include/kvq.h:
+// host-side argument checks, workspace sizing, and kernel dispatch.  No
+// allocation, no synchronisation: every call only enqueues work on `stream`.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kvq_internal.h"
+
+namespace {
+
+kvq_status check_cache(const kvq_cache *c) {
+    if (!c) return KVQ_EINVAL;
+    if (c->head_dim != KVQ_HEAD_DIM) return KVQ_EUNSUPPORTED;
+    if (c->B < 1 || c->Hkv < 1 || c->Hq < 1 || c->Hq % c->Hkv != 0) return KVQ_EINVAL;
+    if (c->Hq / c->Hkv > KVQ_MAX_GQA || c->Hq > 256) return KVQ_EUNSUPPORTED;
+    if (c->max_blocks < 1 || c->n_cap < 1) return KVQ_EINVAL;
+    for (int p = 0; p < 3; ++p) {
+        if (c->pool_blocks[p] < 0 || c->pool_blocks[p] >= (1 << 30)) return KVQ_EINVAL;
+        if (c->pool_blocks[p] > 0 && (!c->kv[p] || !c->mask[p] || !c->pos[p] || !c->free_ids[p]))
+            return KVQ_EINVAL;
+    }
+    if (!c->table || !c->n_blocks || !c->seq_len || !c->free_top || !c->status) return KVQ_EINVAL;
+    return KVQ_OK;
+}
+
+kvq_status check_ws(const kvq_cache *c, const void *ws, size_t bytes) {
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) return KVQ_EINVAL;
+    return bytes >= kvq_workspace_bytes(c) ? KVQ_OK : KVQ_EINVAL;
+}
+
+}  // namespace
+
+extern "C" size_t kvq_region_bytes(int pool) {
+    if (pool < 0 || pool > 2) return 0;
+    return 512u * (8u >> pool) + 512u;
+}
+
+extern "C" size_t kvq_workspace_bytes(const kvq_cache *c) {
+    if (check_cache(c) != KVQ_OK) return 0;
+    return std::max({kvq::AppendWs::bytes(*c), kvq::DecodeWs::bytes(*c), kvq::EvictWs::bytes(*c)});
+}
+
+extern "C" kvq_status kvq_append_quantize(const kvq_cache *c, const void *k_new, const void *v_new,
+                                          const uint8_t *tags, void *ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (!k_new || !v_new || !tags) return KVQ_EINVAL;
+    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    return kvq::launch_append(*c, k_new, v_new, tags, ws, stream) ? KVQ_OK : KVQ_EHIP;
+}
+
+extern "C" kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, float *out,
+                                           float *mass, float *importance, float decay,
+                                           float sm_scale, void *ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (!q || !out || !mass) return KVQ_EINVAL;
+    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    return kvq::launch_decode(*c, q, out, mass, importance, decay, sm_scale, ws, stream) ? KVQ_OK
+                                                                                         : KVQ_EHIP;
+}
+
+extern "C" kvq_status kvq_evict_topk(const kvq_cache *c, const float *importance,
+                                     const int32_t *keep_k, int32_t q_window,
+                                     int32_t recent_window, void *ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (!importance || !keep_k || q_window < 0 || recent_window < 0) return KVQ_EINVAL;
+    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    return kvq::launch_evict(*c, importance, keep_k, q_window, recent_window, ws, stream) ? KVQ_OK
+                                                                                           : KVQ_EHIP;
+}

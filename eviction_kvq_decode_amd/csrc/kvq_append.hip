@@ -1,0 +1,219 @@
+// kvq_append.hip -- append one token per sequence into the typed, paged,
+// quantised cache.
+//
+// "ThinKV", Methodology, Thought-Adaptive Quantization (TBQ): the token's
+// thought type picks the precision (R 8 bit, E 4 bit, T 2 bit) and the
+// values are group-quantised.  Same page, System Implementation (Continuous
+// Thinking): a new token of a type overwrites an evicted slot of a block of
+// that type in place; only when none is free does a block come from the
+// type's free list.
+//
+// Two launches: append_plan (one workgroup per sequence) finds the slot or
+// decides on a pop; append_write (one wave per (sequence, kv head))
+// quantises K and V, packs the codes into the cache layout and updates the
+// block metadata.  Pops are ranked across sequences in batch order from a
+// copy of the free-stack tops taken by the plan, so no cross-workgroup
+// synchronisation is needed.
+#include <limits.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int PLAN_THREADS = 256;
+constexpr int PLAN_UNROLL = 4;
+
+__global__ __launch_bounds__(PLAN_THREADS) void append_plan(kvq_cache c, const uint8_t *tags,
+                                                            AppendWs ws) {
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
+    const int tag = tags[b];
+    if (tag == TAG_NONE || tag > 2 || c.seq_len[b] >= c.n_cap) {
+        if (tid == 0) {
+            ws.need[b] = -2;
+            if (tag != TAG_NONE) *c.status = tag > 2 ? KVQ_EINVAL : KVQ_ENOSPC;
+        }
+        return;
+    }
+    __shared__ int first;
+    if (tid == 0) first = INT_MAX;
+    __syncthreads();
+    const int nb = c.n_blocks[b];
+    const uint32_t *row = c.table + (size_t)b * c.max_blocks;
+    const uint16_t *mask = c.mask[tag];
+    // Scan the table in rounds; each thread issues PLAN_UNROLL independent
+    // loads per round so the dependent table -> mask chain overlaps.
+    for (int base = 0; base < nb; base += PLAN_THREADS * PLAN_UNROLL) {
+        uint32_t ent[PLAN_UNROLL];
+#pragma unroll
+        for (int u = 0; u < PLAN_UNROLL; ++u) {
+            const int e = base + u * PLAN_THREADS + tid;
+            ent[u] = e < nb ? row[e] : 0xffffffffu;
+        }
+        int mine = INT_MAX;
+#pragma unroll
+        for (int u = 0; u < PLAN_UNROLL; ++u) {
+            const int e = base + u * PLAN_THREADS + tid;
+            if (e < nb && (int)(ent[u] >> 30) == tag && mask[ent[u] & 0x3fffffffu] != 0xffff)
+                mine = min(mine, e);
+        }
+        if (mine != INT_MAX) atomicMin(&first, mine);
+        __syncthreads();
+        if (first != INT_MAX) break;
+    }
+    if (tid == 0) {
+        if (first != INT_MAX) {
+            const uint16_t m = mask[row[first] & 0x3fffffffu];
+            ws.need[b] = -1;
+            ws.entry[b] = first;
+            ws.slot[b] = __builtin_ctz(~(uint32_t)m);
+        } else if (nb >= c.max_blocks) {
+            ws.need[b] = -2;
+            *c.status = KVQ_ENOSPC;
+        } else {
+            ws.need[b] = tag;
+        }
+    }
+}
+
+// Group-quantise one 128-channel fp16 row held two channels per lane
+// (lane l owns channels 2l, 2l+1; 16 lanes per 32-channel group).
+// Matches the TBQ reading: zero = min, scale = least fp16 >= (max-min)/lv,
+// code = clamp(rint((x - zero)/scale)), all in fp32.
+__device__ inline void quantise_pair(const uint16_t *row, int bits, int lane, uint32_t &c0,
+                                     uint32_t &c1, uint32_t &scale_zero) {
+    const uint32_t two = reinterpret_cast<const uint32_t *>(row)[lane];
+    const float x0 = h2f((uint16_t)(two & 0xffff)), x1 = h2f((uint16_t)(two >> 16));
+    float mn = fminf(x0, x1), mx = fmaxf(x0, x1);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off));
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    if (mn == 0.0f) mn = fabsf(mn);  // -0 counts as +0
+    if (mx == 0.0f) mx = fabsf(mx);
+    const float lv = (float)((1 << bits) - 1);
+    const float s32 = (mx - mn) / lv;
+    uint16_t sh = f2h_rn(s32);
+    if (h2f(sh) < s32) sh = (uint16_t)(sh + 1);
+    const float sc = h2f(sh);
+    if (sc == 0.0f) {
+        c0 = c1 = 0;
+    } else {
+        float t0 = rintf((x0 - mn) / sc), t1 = rintf((x1 - mn) / sc);
+        c0 = (uint32_t)fminf(fmaxf(t0, 0.0f), lv);
+        c1 = (uint32_t)fminf(fmaxf(t1, 0.0f), lv);
+    }
+    scale_zero = (uint32_t)sh | ((uint32_t)f2h_rn(mn) << 16);
+}
+
+__global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *k_new,
+                                                   const uint16_t *v_new, AppendWs ws) {
+    const int b = blockIdx.x / c.Hkv, h = blockIdx.x % c.Hkv;
+    const int lane = threadIdx.x;
+    if (blockIdx.x == 0 && lane < 3) {
+        int cnt = 0;
+        for (int bb = 0; bb < c.B; ++bb) cnt += ws.need[bb] == lane;
+        c.free_top[lane] = ws.top[lane] - min(cnt, ws.top[lane]);
+    }
+    const int need = ws.need[b];
+    if (need == -2) return;
+    int pool, slot;
+    uint32_t id;
+    bool fresh = false;
+    if (need == -1) {
+        const uint32_t ent = c.table[(size_t)b * c.max_blocks + ws.entry[b]];
+        pool = (int)(ent >> 30);
+        id = ent & 0x3fffffffu;
+        slot = ws.slot[b];
+    } else {
+        pool = need;
+        int rank = 0;
+        for (int bb = lane; bb < b; bb += 64) rank += ws.need[bb] == pool;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) rank += __shfl_xor(rank, off);
+        const int top = ws.top[pool];
+        if (rank >= top) {
+            if (h == 0 && lane == 0) *c.status = KVQ_ENOSPC;
+            return;
+        }
+        id = c.free_ids[pool][top - 1 - rank];
+        slot = 0;
+        fresh = true;
+    }
+    const int bits = pool_bits(pool);
+    uint8_t *reg = region_ptr(c.kv[pool], id, c.Hkv, h, pool);
+
+    __shared__ uint8_t kcode[HD];  // by K-row code index
+    __shared__ uint8_t vcode[HD];  // by channel
+    const size_t row_off = ((size_t)b * c.Hkv + h) * HD;
+    uint32_t k0, k1, ksz, v0, v1, vsz;
+    quantise_pair(k_new + row_off, bits, lane, k0, k1, ksz);
+    quantise_pair(v_new + row_off, bits, lane, v0, v1, vsz);
+    kcode[k_row_index(bits, 2 * lane)] = (uint8_t)k0;
+    kcode[k_row_index(bits, 2 * lane + 1)] = (uint8_t)k1;
+    vcode[2 * lane] = (uint8_t)v0;
+    vcode[2 * lane + 1] = (uint8_t)v1;
+    if ((lane & 15) == 0) {
+        const int g = lane >> 4;
+        reinterpret_cast<uint32_t *>(reg + 512 * bits)[slot * NGRP + g] = ksz;
+        reinterpret_cast<uint32_t *>(reg + 512 * bits + 256)[slot * NGRP + g] = vsz;
+    }
+    __syncthreads();
+
+    // K row: 4*bits dwords, LSB-first.
+    const int per = 32 / bits;  // codes per dword
+    if (lane < 4 * bits) {
+        uint32_t w = 0;
+        for (int i = 0; i < per; ++i) w |= (uint32_t)kcode[lane * per + i] << (i * bits);
+        reinterpret_cast<uint32_t *>(reg + slot * 16 * bits)[lane] = w;
+    }
+    // V: the 16*bits dwords holding this token's codes; read-modify-write,
+    // other tokens' codes in the same dwords are preserved.
+    uint8_t *vbase = reg + 256 * bits;
+    const int tiles_per_dword = 8 / bits;
+    for (int qd = lane; qd < 16 * bits; qd += 64) {
+        const int j = qd & 15, w = qd >> 4;
+        const int d_first = 16 * (w * tiles_per_dword) + j;
+        uint32_t *dw = reinterpret_cast<uint32_t *>(vbase + v_dword_byte(bits, slot, d_first));
+        uint32_t val = *dw;
+        const uint32_t lvmask = (1u << bits) - 1;
+        for (int m = 0; m < tiles_per_dword; ++m) {
+            const int d = 16 * (w * tiles_per_dword + m) + j;
+            const int sh = v_code_slot(bits, slot, d) * bits;
+            val = (val & ~(lvmask << sh)) | ((uint32_t)vcode[d] << sh);
+        }
+        *dw = val;
+    }
+
+    if (h == 0 && lane == 0) {
+        if (fresh) {
+            const int nb = c.n_blocks[b];
+            c.table[(size_t)b * c.max_blocks + nb] = ((uint32_t)pool << 30) | id;
+            c.n_blocks[b] = nb + 1;
+            c.mask[pool][id] = 1;
+        } else {
+            c.mask[pool][id] = (uint16_t)(c.mask[pool][id] | (1u << slot));
+        }
+        const int p = c.seq_len[b];
+        c.pos[pool][(size_t)id * BLK + slot] = p;
+        c.seq_len[b] = p + 1;
+    }
+}
+
+}  // namespace
+
+bool launch_append(const kvq_cache &c, const void *k_new, const void *v_new, const uint8_t *tags,
+                   void *ws_ptr, hipStream_t s) {
+    AppendWs ws(ws_ptr, c);
+    hipLaunchKernelGGL(append_plan, dim3(c.B), dim3(PLAN_THREADS), 0, s, c, tags, ws);
+    hipLaunchKernelGGL(append_write, dim3(c.B * c.Hkv), dim3(64), 0, s, c,
+                       static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new), ws);
+    return hipGetLastError() == hipSuccess;
+}
+
+}  // namespace kvq

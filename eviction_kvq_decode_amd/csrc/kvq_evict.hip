@@ -1,0 +1,237 @@
+// kvq_evict.hip -- windowed top-k eviction with metadata-only compaction.
+//
+// "Dynamic Thinking-Token Selection ...", section 2.3: tokens of the
+// question window are never evicted, the local window of recent tokens is
+// kept, and inside the selection window the top-k by importance survive.
+// "ThinKV", Continuous Thinking: eviction only clears mask bits -- the KV
+// bytes never move; blocks that become empty leave the table and go back to
+// their pool's free list for in-place reuse.
+//
+// evict_select: one 1024-thread workgroup per sequence.  Candidate keys
+//   (order-preserving importance bits, then inverted position, so ties go to
+//   the lower position) are radix-selected for the k-th largest; losers'
+//   mask bits are cleared; the table row is compacted in order with a
+//   ballot prefix scan; freed entries are listed in table order.
+// evict_push: one workgroup per sequence pushes its freed ids at offsets
+//   ranked across sequences in batch order.
+#include <limits.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+
+__device__ inline uint32_t order_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (f == 0.0f) u = 0u;  // -0 counts as +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline uint64_t sel_key(float imp, int pos) {
+    return ((uint64_t)order_bits(imp) << 32) | (uint64_t)(0xffffffffu - (uint32_t)pos);
+}
+
+// Exclusive prefix count of `flag` over the workgroup (thread order) and the
+// total.  Uses per-wave ballots; all threads must call it.
+__device__ inline int block_prefix(bool flag, int *wave_tot, int &total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint64_t bal = __ballot(flag);
+    const int in_wave = __popcll(bal & ((1ull << lane) - 1));
+    if (lane == 0) wave_tot[wv] = __popcll(bal);
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) {
+        const int v = wave_tot[w];
+        before += w < wv ? v : 0;
+        total += v;
+    }
+    __syncthreads();
+    return before + in_wave;
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const float *importance,
+                                                            const int32_t *keep_k, int q_window,
+                                                            int recent_window, EvictWs ws) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
+    const int nb = c.n_blocks[b];
+    const int lo = q_window, hi = c.seq_len[b] - recent_window;
+    uint32_t *row = c.table + (size_t)b * c.max_blocks;
+    const float *imp = importance + (size_t)b * c.n_cap;
+    uint64_t *cand = ws.cand + (size_t)b * c.max_blocks * BLK;
+
+    __shared__ int n_cand;
+    __shared__ uint32_t hist[256];
+    __shared__ int s_digit, s_cum;
+    __shared__ int wave_tot[SEL_WAVES];
+    __shared__ int pool_cnt[4];
+    if (tid == 0) n_cand = 0;
+    if (tid < 4) pool_cnt[tid] = 0;
+    __syncthreads();
+
+    // 1. candidate keys (order of the list does not matter)
+    for (int e = tid; e < nb; e += SEL_THREADS) {
+        const uint32_t ent = row[e];
+        const int pool = (int)(ent >> 30);
+        const uint32_t id = ent & 0x3fffffffu;
+        const uint32_t m = c.mask[pool][id];
+        const int *pp = c.pos[pool] + (size_t)id * BLK;
+        for (int s = 0; s < BLK; ++s) {
+            if (!((m >> s) & 1)) continue;
+            const int p = pp[s];
+            if (p < lo || p >= hi) continue;
+            const int at = atomicAdd(&n_cand, 1);
+            cand[at] = sel_key(imp[p], p);
+        }
+    }
+    __syncthreads();
+    const int n = n_cand;
+    const int k = max(keep_k[b], 0);
+    const bool evicting = n > k;
+
+    // 2. radix-select the k-th largest key, 8 bits at a time, stopping as
+    //    soon as the boundary digit's whole bin is kept.
+    uint64_t thr = 0;
+    int thr_shift = 0;
+    if (evicting && k > 0) {
+        uint64_t prefix = 0;
+        uint32_t need = (uint32_t)k;
+        for (int shift = 56;; shift -= 8) {
+            for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
+            __syncthreads();
+            const uint64_t hmask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+            for (int i = tid; i < n; i += SEL_THREADS) {
+                const uint64_t key = cand[i];
+                if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 255], 1u);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                uint32_t cum = 0;
+                int dgt = 255;
+                for (; dgt > 0; --dgt) {
+                    if (cum + hist[dgt] >= need) break;
+                    cum += hist[dgt];
+                }
+                s_digit = dgt;
+                s_cum = (int)cum;
+            }
+            __syncthreads();
+            const int dgt = s_digit;
+            need -= (uint32_t)s_cum;
+            prefix |= (uint64_t)dgt << shift;
+            const bool done = hist[dgt] == need || shift == 0;
+            __syncthreads();
+            if (done) {
+                thr = prefix;
+                thr_shift = shift;
+                break;
+            }
+        }
+    }
+
+    // 3. clear losers, compact the table row, list freed entries
+    int kept_base = 0, freed_base = 0;
+    uint32_t *freed = ws.freed + (size_t)b * c.max_blocks;
+    for (int c0 = 0; c0 < nb; c0 += SEL_THREADS) {
+        const int e = c0 + tid;
+        const bool has = e < nb;
+        uint32_t ent = 0, newm = 0;
+        if (has) {
+            ent = row[e];
+            const int pool = (int)(ent >> 30);
+            const uint32_t id = ent & 0x3fffffffu;
+            const uint32_t m = c.mask[pool][id];
+            newm = m;
+            if (evicting) {
+                const int *pp = c.pos[pool] + (size_t)id * BLK;
+                for (int s = 0; s < BLK; ++s) {
+                    if (!((m >> s) & 1)) continue;
+                    const int p = pp[s];
+                    if (p < lo || p >= hi) continue;
+                    const bool keep = k > 0 && (sel_key(imp[p], p) >> thr_shift) >= (thr >> thr_shift);
+                    if (!keep) newm &= ~(1u << s);
+                }
+                if (newm != m) c.mask[pool][id] = (uint16_t)newm;
+            }
+        }
+        int nkept, nfreed;
+        const int kr = block_prefix(has && newm != 0, wave_tot, nkept);
+        const int fr = block_prefix(has && newm == 0, wave_tot, nfreed);
+        if (has) {
+            if (newm != 0) {
+                row[kept_base + kr] = ent;
+            } else {
+                freed[freed_base + fr] = ent;
+                atomicAdd(&pool_cnt[ent >> 30], 1);
+            }
+        }
+        kept_base += nkept;
+        freed_base += nfreed;
+        __syncthreads();
+    }
+    if (tid == 0) c.n_blocks[b] = kept_base;
+    if (tid < 4) ws.nfreed[b * 4 + tid] = tid < 3 ? pool_cnt[tid] : freed_base;
+}
+
+__global__ __launch_bounds__(256) void evict_push(kvq_cache c, EvictWs ws) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    __shared__ int base[3];
+    __shared__ int wave_cnt[4][3];
+    if (tid < 3) {
+        int s = ws.top[tid];
+        for (int bb = 0; bb < b; ++bb) s += ws.nfreed[bb * 4 + tid];
+        base[tid] = s;
+        if (b == 0) {
+            int tot = ws.top[tid];
+            for (int bb = 0; bb < c.B; ++bb) tot += ws.nfreed[bb * 4 + tid];
+            c.free_top[tid] = tot;
+        }
+    }
+    __syncthreads();
+    const int nf = ws.nfreed[b * 4 + 3];
+    const uint32_t *freed = ws.freed + (size_t)b * c.max_blocks;
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int c0 = 0; c0 < nf; c0 += 256) {
+        const int i = c0 + tid;
+        const uint32_t ent = i < nf ? freed[i] : 0xffffffffu;
+        const int pool = i < nf ? (int)(ent >> 30) : 3;
+        int rank = 0;
+        for (int p = 0; p < 3; ++p) {
+            const uint64_t bal = __ballot(pool == p);
+            if (lane == 0) wave_cnt[wv][p] = __popcll(bal);
+            if (pool == p) rank = __popcll(bal & ((1ull << lane) - 1));
+        }
+        __syncthreads();
+        if (pool < 3) {
+            int before = 0;
+            for (int w = 0; w < wv; ++w) before += wave_cnt[w][pool];
+            c.free_ids[pool][base[pool] + before + rank] = ent & 0x3fffffffu;
+        }
+        __syncthreads();
+        if (tid < 3) {
+            int tot = 0;
+            for (int w = 0; w < 4; ++w) tot += wave_cnt[w][tid];
+            base[tid] += tot;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *keep_k, int q_window,
+                  int recent_window, void *ws_ptr, hipStream_t s) {
+    EvictWs ws(ws_ptr, c);
+    hipLaunchKernelGGL(evict_select, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, keep_k,
+                       q_window, recent_window, ws);
+    hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);
+    return hipGetLastError() == hipSuccess;
+}
+
+}  // namespace kvq

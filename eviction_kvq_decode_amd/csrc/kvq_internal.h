@@ -1,0 +1,80 @@
+// kvq_internal.h -- host-side contract between the C ABI and the kernels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+// Decode split-K: a split covers this many table entries of one sequence
+// and kv head.
+constexpr int ENTRIES_PER_SPLIT = 64;
+
+inline int n_splits(const kvq_cache &c) {
+    return (c.max_blocks + ENTRIES_PER_SPLIT - 1) / ENTRIES_PER_SPLIT;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace carve-up.  Calls are stream-ordered, so they share one buffer.
+struct AppendWs {
+    int32_t *need;     // [B] -2 nothing, -1 reuse slot, p >= 0 pop pool p
+    int32_t *entry;    // [B] table index of the reused block
+    int32_t *slot;     // [B]
+    int32_t *top;      // [4] free_top before the call
+    static size_t bytes(const kvq_cache &c) { return align256(16 * 4) + 3 * align256(4L * c.B); }
+    AppendWs(void *ws, const kvq_cache &c) {
+        char *p = (char *)ws;
+        top = (int32_t *)p;   p += align256(16 * 4);
+        need = (int32_t *)p;  p += align256(4L * c.B);
+        entry = (int32_t *)p; p += align256(4L * c.B);
+        slot = (int32_t *)p;
+    }
+};
+
+struct DecodeWs {
+    float *ml;         // [B][Hq][S][2]  split max (base-2 units), split sum
+    float *o;          // [B][Hq][S][128] split output, unnormalised
+    float *score;      // [B][Hq][max_blocks*16] base-2 scaled scores
+    static size_t bytes(const kvq_cache &c) {
+        const size_t S = n_splits(c);
+        return align256(8L * c.B * c.Hq * S) + align256(512L * c.B * c.Hq * S) +
+               align256(4L * c.B * c.Hq * c.max_blocks * 16);
+    }
+    DecodeWs(void *ws, const kvq_cache &c) {
+        const size_t S = n_splits(c);
+        char *p = (char *)ws;
+        ml = (float *)p;    p += align256(8L * c.B * c.Hq * S);
+        o = (float *)p;     p += align256(512L * c.B * c.Hq * S);
+        score = (float *)p;
+    }
+};
+
+struct EvictWs {
+    uint64_t *cand;    // [B][max_blocks*16] selection keys
+    uint32_t *freed;   // [B][max_blocks] freed table entries, table order
+    int32_t *nfreed;   // [B][4] freed per pool
+    int32_t *top;      // [4] free_top before the call
+    static size_t bytes(const kvq_cache &c) {
+        return align256(8L * c.B * c.max_blocks * 16) + align256(4L * c.B * c.max_blocks) +
+               align256(16L * c.B) + align256(16);
+    }
+    EvictWs(void *ws, const kvq_cache &c) {
+        char *p = (char *)ws;
+        cand = (uint64_t *)p;  p += align256(8L * c.B * c.max_blocks * 16);
+        freed = (uint32_t *)p; p += align256(4L * c.B * c.max_blocks);
+        nfreed = (int32_t *)p; p += align256(16L * c.B);
+        top = (int32_t *)p;
+    }
+};
+
+// Launchers (one per kernel file); return false if a launch failed.
+bool launch_append(const kvq_cache &c, const void *k_new, const void *v_new, const uint8_t *tags,
+                   void *ws, hipStream_t s);
+bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, float *importance,
+                   float decay, float sm_scale, void *ws, hipStream_t s);
+bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *keep_k, int q_window,
+                  int recent_window, void *ws, hipStream_t s);
+
+}  // namespace kvq

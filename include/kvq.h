@@ -1,0 +1,165 @@
+/*
+ * kvq.h -- C ABI of libkvq: decode attention over a paged KV cache whose
+ * tokens are stored at 8, 4 or 2 bits according to their thought type, with
+ * evicted slots reused in place, on AMD Instinct MI355X (gfx950).
+ *
+ * The method (web pages, cited by title and section):
+ *  - "ThinKV: Thought-Adaptive KV Cache Compression for Efficient Reasoning
+ *    Models", Methodology, "Thought-Adaptive Quantization (TBQ)": each token's
+ *    K/V precision follows its thought type (Reasoning > Execution >
+ *    Transition), by group quantisation.
+ *  - same page, Methodology, "System Implementation: Continuous Thinking":
+ *    a PagedAttention-style block table that records thought type and an
+ *    eviction mask; new tokens of the same type overwrite evicted slots in
+ *    place; no gather compaction.
+ *  - "Dynamic Thinking-Token Selection ...", section 2.3: question window,
+ *    local window, and top-k by importance inside the selection window.
+ *  - "Thought-Aware KV Cache Compaction ... (TAM)", sections 1 and 2.B, and
+ *    "Back from the Future ...", Problem Statement: the attention mass a
+ *    token receives (H2O-style cumulative score) is the importance signal;
+ *    attention itself is scaled dot-product attention over the cache.
+ *
+ * Conventions for every call:
+ *  - All pointers are DEVICE pointers owned by the caller, except the
+ *    kvq_cache struct itself, which is read on the host during the call.
+ *    The library never allocates, frees or synchronises; all work is
+ *    enqueued on `stream` and returns immediately.
+ *  - A host-detectable problem (null pointer, unsupported shape, workspace
+ *    too small) returns an error and enqueues nothing.  A failed launch
+ *    returns KVQ_EHIP.  Data-dependent problems found on the device (a pool
+ *    or table full, a bad tag) store a negative kvq_status into *status and
+ *    leave the affected sequence unchanged; the library never clears
+ *    *status.
+ *  - Calls on one cache must be ordered on one stream; calls on disjoint
+ *    caches may run concurrently.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_EINVAL = -1,       /* bad argument                          */
+    KVQ_EUNSUPPORTED = -2, /* shape outside what the kernels handle */
+    KVQ_EHIP = -3,         /* a HIP launch failed                   */
+    KVQ_ENOSPC = -4        /* pool, table or position space full    */
+} kvq_status;
+
+enum { KVQ_HEAD_DIM = 128, KVQ_BLOCK = 16, KVQ_GROUP = 32, KVQ_MAX_GQA = 16 };
+
+/* Thought types; the pool index equals the tag.  R -> 8 bit, E -> 4 bit,
+ * T -> 2 bit ("ThinKV", TBQ: precision ordered R > E > T). */
+enum { KVQ_TAG_R = 0, KVQ_TAG_E = 1, KVQ_TAG_T = 2, KVQ_TAG_NONE = 255 };
+
+/*
+ * The cache.  One pool per bit width; a block holds 16 slots of one thought
+ * type.  For pool p (bits b = 8 >> p) and block id, kv head h, the region at
+ *     kv[p] + (id * Hkv + h) * kvq_region_bytes(p)
+ * holds, in order:
+ *     K codes  256*b bytes : token t's K row is 16*b contiguous bytes at t*16*b;
+ *                            channel d sits at code index kappa_b(d) of the row
+ *     V codes  256*b bytes : channel-major tiles (see DESIGN notes / the oracle)
+ *     K (scale, zero) 256 B: fp16 pair for token t, group g at (t*4 + g)*4
+ *     V (scale, zero) 256 B: same layout
+ * Codes are packed LSB first.  A dequantised value is code * scale + zero.
+ * Bytes of slots whose mask bit is clear are unspecified.
+ *
+ * table[b * max_blocks + e] = (pool << 30) | id, for e < n_blocks[b], in
+ * logical order.  pos[p][id * 16 + s] is the logical position held by slot
+ * s of block id (meaningful where mask bit s is set).  free_ids[p][0 ..
+ * free_top[p]) is pool p's stack of unused block ids; pops take the top.
+ */
+typedef struct kvq_cache {
+    int32_t B;            /* sequences                                   */
+    int32_t Hq;           /* query heads                                 */
+    int32_t Hkv;          /* kv heads; Hq % Hkv == 0, Hq/Hkv <= 16       */
+    int32_t head_dim;     /* must be 128                                 */
+    int32_t max_blocks;   /* table row capacity per sequence             */
+    int32_t n_cap;        /* row stride (positions) of mass / importance */
+    int32_t pool_blocks[3];
+    uint8_t *kv[3];       /* [pool_blocks][Hkv] regions                  */
+    uint16_t *mask[3];    /* [pool_blocks] valid-slot bitmask            */
+    int32_t *pos[3];      /* [pool_blocks][16]                           */
+    uint32_t *table;      /* [B][max_blocks]                             */
+    int32_t *n_blocks;    /* [B]                                         */
+    int32_t *seq_len;     /* [B] next logical position                   */
+    uint32_t *free_ids[3];/* [pool_blocks]                               */
+    int32_t *free_top;    /* [3]                                         */
+    int32_t *status;      /* [1] device error word                       */
+} kvq_cache;
+
+/* Bytes of one (block, kv head) region of pool p (0, 1, 2): 512*b + 512. */
+size_t kvq_region_bytes(int pool);
+
+/* Workspace bytes that every call below needs for this cache (device
+ * memory, 256-byte aligned, contents need not be initialised). */
+size_t kvq_workspace_bytes(const kvq_cache *cache);
+
+/*
+ * Append one token per sequence ("ThinKV", TBQ and Continuous Thinking).
+ *   k_new, v_new : fp16 [B][Hkv][128]
+ *   tags         : uint8 [B]; KVQ_TAG_R/E/T, or KVQ_TAG_NONE to skip b
+ * Per kv head and per 32-channel group, K and V are quantised to b bits:
+ * zero = group min, scale = least fp16 >= (max - min)/(2^b - 1) (fp32),
+ * code = clamp(rint((x - zero)/scale), 0, 2^b - 1) (fp32, ties to even).
+ * The token goes to the first free slot of a block of its own type, in table
+ * order then slot order; otherwise a block is popped from that pool's free
+ * stack (sequences served in batch order) and appended to the table.  It
+ * gets position seq_len[b], which then grows by one.  Sequences that cannot
+ * be served (pool empty, table full, seq_len == n_cap) set *status =
+ * KVQ_ENOSPC and are left unchanged; a tag > 2 sets KVQ_EINVAL.
+ */
+kvq_status kvq_append_quantize(const kvq_cache *cache, const void *k_new, const void *v_new,
+                               const uint8_t *tags, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Decode attention for one query token per sequence ("Back from the
+ * Future", Problem Statement: scaled dot-product attention over the cache),
+ * plus the per-position attention mass ("TAM", sections 1 and 2.B).
+ *   q          : fp16 [B][Hq][128]
+ *   out        : fp32 [B][Hq][128] = sum_t p_ht * v_t over valid slots of the
+ *                sequence, p = softmax(sm_scale * q_h . k_t); query head h
+ *                reads kv head h / (Hq / Hkv).  Zero if no slot is valid.
+ *   mass       : fp32 [B][n_cap]; for positions < seq_len[b]:
+ *                sum over all Hq heads of p_ht for the slot holding the
+ *                position, 0 if no valid slot holds it.  Other entries are
+ *                not written.
+ *   importance : fp32 [B][n_cap] or NULL; at valid positions
+ *                importance = decay * importance + mass (H2O-style
+ *                cumulative score); other entries are not touched.
+ */
+kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, float *out, float *mass,
+                                float *importance, float decay, float sm_scale, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Windowed top-k eviction ("Dynamic Thinking-Token Selection ...", 2.3) with
+ * metadata-only compaction ("ThinKV", Continuous Thinking).
+ *   importance : fp32 [B][n_cap], read at the positions of valid slots
+ *                (finite values; -0 counts as +0)
+ *   keep_k     : int32 [B]
+ * Per sequence, valid slots with position < q_window or >= seq_len -
+ * recent_window are kept; of the others, the keep_k with the largest
+ * importance (ties: lower position) are kept and the rest are evicted
+ * (mask bit cleared; the bytes stay in place).  Then every table entry whose
+ * mask is empty is removed from the table, order kept, and its id pushed on
+ * its pool's free stack, in table order, sequences in batch order.
+ */
+kvq_status kvq_evict_topk(const kvq_cache *cache, const float *importance, const int32_t *keep_k,
+                          int32_t q_window, int32_t recent_window, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

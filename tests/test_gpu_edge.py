@@ -1,0 +1,188 @@
+"""GPU edge cases against the oracle: empty and skipped sequences, pool
+exhaustion, bad tags, GQA group sizes 1 and 16, empty blocks left in the
+table, degenerate eviction budgets, and the closed forms of attention."""
+import math
+
+import numpy as np
+import pytest
+
+from eviction_kvq_decode_amd import workloads as wl
+from helpers import small_geometry
+from oracle import oracle as orc
+from pairs import assert_attention_close, assert_mass_close, assert_same_cache, log
+
+pytestmark = pytest.mark.gpu
+
+HD = 128
+SM = 1 / math.sqrt(HD)
+
+
+def _mk(g, identity=True, state=None):
+    from eviction_kvq_decode_amd import kvq
+
+    st = wl.empty_state(g, identity) if state is None else state
+    return orc.OracleCache(g, st), kvq.Cache(g, st)
+
+
+def _dev(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _append(oc, gc, k, v, tags):
+    oc.append(k, v, tags)
+    gc.append(_dev(k), _dev(v), _dev(np.asarray(tags, np.uint8)))
+
+
+def _decode(oc, gc, q, imp=None, decay=0.0):
+    import torch
+
+    g = oc.g
+    ref = oc.decode(q, SM, imp, decay)
+    out = torch.full((g.B, g.Hq, HD), float("nan"), device="cuda")
+    mass = torch.full((g.B, g.n_cap), -7.0, device="cuda")
+    imp_d = None if imp is None else _dev(imp.astype(np.float32))
+    gc.decode(_dev(q), out, mass, imp_d, decay)
+    torch.cuda.synchronize()
+    return ref, (out.cpu().numpy(), mass.cpu().numpy(), None if imp_d is None else imp_d.cpu().numpy())
+
+
+def _fill(oc, gc, rng, n, tags_fn=None, kscale=1.0):
+    g = oc.g
+    for i in range(n):
+        k = (rng.standard_normal((g.B, g.Hkv, HD)) * kscale).astype(np.float16)
+        v = rng.standard_normal((g.B, g.Hkv, HD)).astype(np.float16)
+        tags = rng.integers(0, 3, g.B).astype(np.uint8) if tags_fn is None else tags_fn(i)
+        _append(oc, gc, k, v, tags)
+
+
+def test_empty_and_skipped_sequences():
+    log("[edge] empty and skipped sequences")
+    g = small_geometry(3, 8, 2, 120)
+    oc, gc = _mk(g)
+    rng = np.random.default_rng(0)
+    _fill(oc, gc, rng, 100, lambda i: np.array([i % 3, 255, (i // 7) % 3], np.uint8))
+    assert_same_cache(oc, gc.state_numpy())
+    q = rng.standard_normal((3, 8, HD)).astype(np.float16)
+    ref, got = _decode(oc, gc, q)
+    assert np.all(got[0][1] == 0.0)
+    assert_attention_close(ref, got)
+    assert_mass_close(oc.st["seq_len"], ref, got)
+
+
+def test_pool_exhaustion_and_bad_tag():
+    log("[edge] ENOSPC / EINVAL")
+    g = wl.Geometry(3, 2, 1, 2, 64, (1, 1, 1))
+    oc, gc = _mk(g)
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((3, 1, HD)).astype(np.float16)
+    _append(oc, gc, k, k, np.array([0, 0, 2], np.uint8))
+    assert oc.status == gc.status == -4
+    assert_same_cache(oc, gc.state_numpy())
+    oc.st["status"][0] = 0
+    oc2, gc2 = _mk(g, state=oc.st)
+    _append(oc2, gc2, k, k, np.array([7, 255, 255], np.uint8))
+    assert oc2.status == gc2.status == -1
+    assert_same_cache(oc2, gc2.state_numpy())
+    # table full: max_blocks 2 and a third type
+    oc3, gc3 = _mk(wl.Geometry(1, 2, 1, 2, 64, (4, 4, 4)))
+    for tag in (0, 1, 2):
+        _append(oc3, gc3, k[:1], k[:1], np.array([tag], np.uint8))
+    assert oc3.status == gc3.status == -4
+    assert_same_cache(oc3, gc3.state_numpy())
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (16, 1), (24, 2)])
+def test_gqa_group_sizes(Hq, Hkv):
+    log(f"[edge] Hq={Hq} Hkv={Hkv}")
+    g = small_geometry(2, Hq, Hkv, 700)
+    oc, gc = _mk(g, identity=False)
+    rng = np.random.default_rng(Hq)
+    _fill(oc, gc, rng, 700)
+    q = rng.standard_normal((2, Hq, HD)).astype(np.float16)
+    imp = rng.exponential(0.1, (2, g.n_cap)).astype(np.float32)
+    ref, got = _decode(oc, gc, q, imp, 0.9)
+    assert_attention_close(ref, got)
+    assert_mass_close(oc.st["seq_len"], ref, got)
+
+
+def test_empty_blocks_left_in_table():
+    log("[edge] empty blocks in table")
+    g = small_geometry(2, 8, 2, 600)
+    oc, gc = _mk(g, identity=False)
+    rng = np.random.default_rng(3)
+    _fill(oc, gc, rng, 600)
+    st = gc.state_numpy()
+    for b in range(2):
+        for e in oc.table_row(b)[1::3]:
+            p, bid = int(e >> 30), int(e & 0x3FFFFFFF)
+            oc.st[f"mask{p}"][bid] = 0
+            st[f"mask{p}"][bid] = 0
+        for e in oc.table_row(b)[2::5]:
+            p, bid = int(e >> 30), int(e & 0x3FFFFFFF)
+            oc.st[f"mask{p}"][bid] &= 0x5A5A
+            st[f"mask{p}"][bid] &= 0x5A5A
+    _, gc2 = _mk(g, state=st)
+    q = rng.standard_normal((2, 8, HD)).astype(np.float16)
+    ref, got = _decode(oc, gc2, q)
+    assert_attention_close(ref, got)
+    assert_mass_close(oc.st["seq_len"], ref, got)
+
+
+@pytest.mark.parametrize("keep,qw,rw", [(0, 0, 0), (0, 10, 10), (10 ** 6, 0, 0), (5, 400, 400), (1, 0, 1)])
+def test_degenerate_eviction(keep, qw, rw):
+    log(f"[edge] evict keep={keep} qw={qw} rw={rw}")
+    g = small_geometry(3, 4, 1, 300)
+    oc, gc = _mk(g, identity=False)
+    rng = np.random.default_rng(4)
+    _fill(oc, gc, rng, 300)
+    imp = rng.random((3, g.n_cap)).astype(np.float32)
+    imp[1] = 0.5                                      # all ties
+    kk = np.full(3, keep, np.int32)
+    oc.evict(imp, kk, qw, rw)
+    gc.evict(_dev(imp), _dev(kk), qw, rw)
+    assert_same_cache(oc, gc.state_numpy())
+    q = rng.standard_normal((3, 4, HD)).astype(np.float16)
+    ref, got = _decode(oc, gc, q)
+    assert_attention_close(ref, got)
+    assert_mass_close(oc.st["seq_len"], ref, got)
+
+
+def test_identical_keys_closed_form():
+    log("[edge] identical keys")
+    g = small_geometry(1, 8, 2, 300)
+    oc, gc = _mk(g)
+    rng = np.random.default_rng(5)
+    kvec = rng.standard_normal((1, 2, HD)).astype(np.float16)
+    for i in range(300):
+        v = rng.standard_normal((1, 2, HD)).astype(np.float16)
+        _append(oc, gc, kvec, v, np.array([1], np.uint8))
+    q = rng.standard_normal((1, 8, HD)).astype(np.float16)
+    ref, got = _decode(oc, gc, q)
+    assert np.all(np.abs(got[1][0, :300] - 8 / 300) <= 1e-5)
+    vmean = np.stack([np.mean([oc.dequant_slot(p, b, kh, s)[1] for p, b, s, _ in oc.valid_slots(0)], axis=0)
+                      for kh in range(2)])
+    for h in range(8):
+        assert np.all(np.abs(got[0][0, h] - vmean[h // 4]) <= 1e-3 + 2e-3 * np.abs(vmean[h // 4]))
+
+
+def test_dominant_key_closed_form():
+    log("[edge] dominant key")
+    g = small_geometry(1, 4, 1, 200)
+    oc, gc = _mk(g)
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 4, HD)).astype(np.float16)
+    qm = q[0].astype(np.float32).mean(axis=0)
+    for i in range(200):
+        k = rng.standard_normal((1, 1, HD)).astype(np.float16)
+        tag = rng.integers(0, 3)
+        if i == 77:
+            k[0, 0] = (40.0 * qm / np.abs(qm).max()).astype(np.float16)
+            tag = 0
+        _append(oc, gc, k, rng.standard_normal((1, 1, HD)).astype(np.float16), np.array([tag], np.uint8))
+    ref, got = _decode(oc, gc, q)
+    assert abs(got[1][0, 77] - 4.0) <= 1e-5
+    vj = [oc.dequant_slot(p, b, 0, s)[1] for p, b, s, ps in oc.valid_slots(0) if ps == 77][0]
+    for h in range(4):
+        assert np.all(np.abs(got[0][0, h] - vj) <= 1e-3 + 2e-3 * np.abs(vj))
