@@ -1,0 +1,215 @@
+"""Benchmark: decode attention over the compressed, partly evicted KV cache.
+
+One step = append one new token per sequence (quantise into a free slot of
+its type) + decode attention for one query token per sequence (output,
+per-position mass), on the long-reasoning-trace workload:
+B=32, Hq=32, Hkv=8, D=128, 32768 logical positions per sequence, 60% of the
+slots evicted (whole thought runs, T-biased), tokens at 8/4/2 bits by type.
+
+Prints one JSON line.  `value` is decode tokens/s (B tokens per step);
+`roofline` rates the decode call against MI355X HBM bandwidth on the
+compressed-KV bytes it must read; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn tokens/s + effective compressed-KV GB/s (% of HBM peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+ROW_BYTES = (288, 160, 96)   # K+V codes + (scale, zero) per token per kv head, R/E/T
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kv_bytes(tags_valid: np.ndarray, Hkv: int) -> int:
+    return int(np.asarray(ROW_BYTES)[tags_valid.astype(np.int64)].sum()) * Hkv
+
+
+def build_gpu_cache(w, toks, g):
+    import torch
+
+    from eviction_kvq_decode_amd import kvq
+    from eviction_kvq_decode_amd import workloads as wl
+
+    cache = kvq.Cache(g, wl.empty_state(g, w.identity_ids, seed_key=(w.wid,)))
+    K = torch.from_numpy(toks.k).cuda()
+    V = torch.from_numpy(toks.v).cuda()
+    T = torch.from_numpy(toks.tags).cuda()
+    sk, sv, st = K[0].numel() * 2, V[0].numel() * 2, T[0].numel()
+    kp, vp, tp = K.data_ptr(), V.data_ptr(), T.data_ptr()
+    for i in range(toks.k.shape[0]):
+        cache.append(kp + i * sk, vp + i * sv, tp + i * st)
+    torch.cuda.synchronize()
+    del K, V, T
+    if w.holes > 0:
+        imp = torch.from_numpy(toks.keep.astype(np.float32)).cuda()
+        keep = torch.from_numpy(toks.keep.sum(axis=1).astype(np.int32)).cuda()
+        cache.evict(imp, keep, 0, 0)
+    torch.cuda.synchronize()
+    if cache.status != 0:
+        raise RuntimeError(f"cache build set status {cache.status}")
+    return cache
+
+
+def cpu_baseline(w, toks, n_seq: int, seconds: float):
+    """Time the CPU oracle on the first n_seq sequences of the workload."""
+    from eviction_kvq_decode_amd import workloads as wl
+    from oracle import oracle as orc
+
+    ws = wl.scaled(w, B=n_seq)
+    g = wl.geometry_for(ws, toks.seq_tags[:n_seq])
+    oc = orc.OracleCache(g, wl.empty_state(g, ws.identity_ids, seed_key=(w.wid,)))
+    t0 = time.time()
+    for i in range(toks.k.shape[0]):
+        oc.append(toks.k[i, :n_seq], toks.v[i, :n_seq], toks.tags[i, :n_seq])
+    if w.holes > 0:
+        keep = toks.keep[:n_seq]
+        oc.evict(keep.astype(np.float32), keep.sum(axis=1).astype(np.int32), 0, 0)
+    log(f"[cpu] oracle sample of {n_seq} sequences built in {time.time() - t0:.1f}s")
+    reps, t0 = 0, time.time()
+    step = 0
+    while time.time() - t0 < seconds or reps < 2:
+        k, v, tags = wl.step_tokens(w, 10_000 + step)
+        oc.append(k[:n_seq], v[:n_seq], tags[:n_seq])
+        oc.decode(wl.queries(w, step)[:n_seq], 1 / math.sqrt(128))
+        reps += 1
+        step += 1
+    dt = time.time() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": n_seq * reps / dt, "unit": "tokens/s", "cores": min(n_seq, threads),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {w.B} sequences at full length, {reps} append+decode steps "
+                      f"in {dt:.1f}s (fp64 C, OpenMP over sequences)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_evicted")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the path shards by sequence "
+                                   "with no exchange (see the design notes)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from eviction_kvq_decode_amd import kvq
+    from eviction_kvq_decode_amd import workloads as wl
+
+    kvq.lib()
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    if w.keep or w.keep_frac:
+        raise SystemExit("the timed step of this benchmark appends and decodes; "
+                         "eviction workloads are measured by the test suite")
+    total_steps = args.warmup + args.steps
+    w = wl.scaled(w, extra_steps=max(w.extra_steps, total_steps + 8))
+    t0 = time.time()
+    n = wl.seq_lengths(w)
+    n_cap = int(n.max()) + w.extra_steps + w.append_steps
+    toks = wl.lockstep_tokens(w, n_cap, threads=min(16, os.cpu_count() or 1))
+    g = wl.geometry_for(w, toks.seq_tags)
+    log(f"[gen] {w.name}: tokens generated in {time.time() - t0:.1f}s; geometry {g}")
+    t0 = time.time()
+    cache = build_gpu_cache(w, toks, g)
+    log(f"[gpu] cache built in {time.time() - t0:.1f}s")
+
+    # compressed-KV bytes the decode must read at each step
+    valid = toks.keep[:, : toks.tags.shape[0]].T & (toks.tags != wl.TAG_SKIP)
+    base_bytes = kv_bytes(toks.tags[valid], w.Hkv)
+    B = w.B
+    steps_k, steps_v, steps_t, steps_q, step_bytes = [], [], [], [], []
+    acc = base_bytes
+    for s in range(total_steps):
+        k, v, tags = wl.step_tokens(w, s)
+        steps_k.append(k), steps_v.append(v), steps_t.append(tags)
+        steps_q.append(wl.queries(w, s))
+        acc += kv_bytes(tags, w.Hkv)
+        step_bytes.append(acc)
+    K = torch.from_numpy(np.stack(steps_k)).cuda()
+    V = torch.from_numpy(np.stack(steps_v)).cuda()
+    T = torch.from_numpy(np.stack(steps_t)).cuda()
+    Q = torch.from_numpy(np.stack(steps_q)).cuda()
+    out = torch.empty((B, w.Hq, 128), device="cuda")
+    mass = torch.empty((B, g.n_cap), device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total_steps)]
+
+    def step(s):
+        cache.append(K[s], V[s], T[s])
+        ev[s][0].record()
+        cache.decode(Q[s], out, mass)
+        ev[s][1].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        step(s)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    if cache.status != 0:
+        raise RuntimeError(f"status {cache.status} after timed steps")
+    dec_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, total_steps)]
+    dec_bytes = step_bytes[args.warmup:]
+    achieved = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
+    ms_per_step = dt * 1e3 / args.steps
+    log(f"[gpu] step {ms_per_step * 1e3:.1f} us, decode call {np.mean(dec_ms) * 1e3:.1f} us "
+        f"(min {np.min(dec_ms) * 1e3:.1f}), {dec_bytes[-1] / 1e6:.1f} MB compressed KV, "
+        f"{achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": B * args.steps / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, "
+                               f"{int(n.max())} logical positions/seq, "
+                               f"{100 * (1 - toks.keep[:, : int(n.max())].mean()):.0f}% evicted, "
+                               f"R/E/T at 8/4/2 bits; step = append 1 token/seq + decode",
+                   "global_batch": B, "seq_len": int(n.max()),
+                   "compressed_kv_mb_per_step": round(dec_bytes[-1] / 1e6, 1)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvq_decode_attention (split + finalize)",
+                     "avg_us": float(np.mean(dec_ms) * 1e3)},
+        "cpu_baseline": None,
+    }
+    del K, V, Q
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, toks, min(args.cpu_seqs, B), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

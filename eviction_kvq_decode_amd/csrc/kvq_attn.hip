@@ -28,119 +28,377 @@ constexpr int THREADS = 256;
 constexpr int MAX_HQ = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 
-// Dequantised K code (t, d) and V code (t, d) of a region.
-__device__ inline uint32_t k_code(const uint8_t *reg, int bits, int t, int d) {
-    const int bit = (t * HD + k_row_index(bits, d)) * bits;
-    return (reg[bit >> 3] >> (bit & 7)) & ((1u << bits) - 1);
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVES = 4;
+
+// kv heads packed into one wave: the 16 MFMA columns hold PACK(G) * G query heads
+__host__ __device__ constexpr int PACK(int G) { return 16 / G < 4 ? 16 / G : 4; }
+constexpr uint32_t BIAS2 = 0x64006400u;   // two fp16 1024.0: (1024 + c) has c in its low bits
+constexpr float P_HEADROOM = 60000.0f;    // P' = p * v_scale * mult must stay below fp16 max
+
+// fp16 pair (1024 + lo, 1024 + hi) -> exact (lo, hi).
+__device__ inline uint32_t unbias(uint32_t x) {
+    half2v h = __builtin_bit_cast(half2v, x);
+    h = h - (half2v){(_Float16)1024.0f, (_Float16)1024.0f};
+    return __builtin_bit_cast(uint32_t, h);
 }
-__device__ inline uint32_t v_code(const uint8_t *reg, int bits, int t, int d) {
-    const uint8_t *dw = reg + 256 * bits + v_dword_byte(bits, t, d);
-    const int bit = v_code_slot(bits, t, d) * bits;
-    return (dw[bit >> 3] >> (bit & 7)) & ((1u << bits) - 1);
+// Bytes i and j of w as the exact fp16 pair (w.byte[i], w.byte[j]).
+__device__ inline uint32_t byte_pair(uint32_t w, int i, int j) {
+    const uint32_t sel = (uint32_t)(4 + i) | ((uint32_t)(4 + j) << 16);  // 0 selects a 0x64 byte
+    return unbias(__builtin_amdgcn_perm(w, 0x64646464u, sel));
+}
+// Fields at bit offsets sh and sh+16 of w (mask m per field) as an exact fp16 pair.
+__device__ inline uint32_t field_pair(uint32_t w, int sh, uint32_t m) {
+    return unbias(((w >> sh) & m) | BIAS2);
 }
 
-__global__ __launch_bounds__(THREADS) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
-                                                      DecodeWs ws, float scale2) {
-    const int split = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
-    const int S = gridDim.x, G = c.Hq / c.Hkv;
-    const int tid = threadIdx.x;
-
-    // Positions of this sequence start at mass 0; the finalize pass adds the
-    // valid ones.  All workgroups of the sequence share the fill.
-    {
-        const int w = split * c.Hkv + kh, W = S * c.Hkv, len = c.seq_len[b];
-        for (int p = w * THREADS + tid; p < len; p += W * THREADS) mass[(size_t)b * c.n_cap + p] = 0.f;
-    }
-
-    __shared__ float qs[KVQ_MAX_GQA][HD];
-    __shared__ float sc[BLK][KVQ_MAX_GQA];
-    __shared__ float pb[BLK][KVQ_MAX_GQA];
-    __shared__ float m_run[KVQ_MAX_GQA], l_run[KVQ_MAX_GQA], alpha[KVQ_MAX_GQA];
-    for (int i = tid; i < G * HD; i += THREADS)
-        qs[i / HD][i % HD] = h2f(q[((size_t)b * c.Hq + kh * G) * HD + i]);
-    if (tid < G) {
-        m_run[tid] = -INFINITY;
-        l_run[tid] = 0.f;
-    }
-    float acc[KVQ_MAX_GQA / 2];
+// QK A operand: the eight codes of group g held by this lane's K slice,
+// in channel order e0..e7 (see the K row layout).
+template <int BITS>
+__device__ inline half8 k_operand(const uint32_t *kw, int g) {
+    uint32_t r[4];
+    if constexpr (BITS == 8) {
+        r[0] = byte_pair(kw[2 * g], 0, 1);
+        r[1] = byte_pair(kw[2 * g], 2, 3);
+        r[2] = byte_pair(kw[2 * g + 1], 0, 1);
+        r[3] = byte_pair(kw[2 * g + 1], 2, 3);
+    } else if constexpr (BITS == 4) {
 #pragma unroll
-    for (int k = 0; k < KVQ_MAX_GQA / 2; ++k) acc[k] = 0.f;
+        for (int k = 0; k < 4; ++k) r[k] = field_pair(kw[g], 4 * k, 0x000F000Fu);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = field_pair(kw[g >> 1], 2 * (4 * (g & 1) + k), 0x00030003u);
+    }
+    return __builtin_bit_cast(half8, r);
+}
+
+// PV B operand: codes of tokens 4r..4r+3 at this lane's channel of tile n.
+template <int BITS>
+__device__ inline half4 v_operand(const uint32_t *vw, int n) {
+    uint32_t r[2];
+    if constexpr (BITS == 8) {
+        r[0] = byte_pair(vw[n], 0, 2);
+        r[1] = byte_pair(vw[n], 1, 3);
+    } else if constexpr (BITS == 4) {
+        const int m = n & 1;
+        r[0] = field_pair(vw[n >> 1], 8 * m, 0x000F000Fu);
+        r[1] = field_pair(vw[n >> 1], 8 * m + 4, 0x000F000Fu);
+    } else {
+        const int m = n & 3;
+        r[0] = field_pair(vw[n >> 2], 4 * m, 0x00030003u);
+        r[1] = field_pair(vw[n >> 2], 4 * m + 2, 0x00030003u);
+    }
+    return __builtin_bit_cast(half4, r);
+}
+
+__device__ inline float lo_h(uint32_t x) { return h2f((uint16_t)(x & 0xffff)); }
+__device__ inline float hi_h(uint32_t x) { return h2f((uint16_t)(x >> 16)); }
+
+// Per-wave running state for the G query heads of each kv head in the pack.
+// Lane (rho = lane % 16, r = lane / 16) owns head rho and, inside a block,
+// tokens 4r..4r+3; the PV accumulators O[n] hold heads 4r..4r+3 at
+// channel 16n + lane % 16.
+struct WaveState {
+    float m;         // running max of head rho (base-2 scaled scores)
+    float l;         // this lane's share of the running sum
+    float z[NGRP];   // this lane's share of sum p * v_zero per group
+    floatx4 o[8];    // sum p * v_scale * mult * code, per 16-channel tile
+    float mult;      // power-of-two headroom factor applied to P'
+};
+
+template <int G, int BITS>
+__device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base, uint32_t id, int kh0,
+                                    int np, uint32_t m16, int e, int b, const half8 *qop,
+                                    const float *qsum, float scale2, const DecodeWs &ws, WaveState &st) {
+    constexpr int P = PACK(G);
+    const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
+    const int a_rho = min(lo / G, np - 1);
+    const bool row_ok = lo < np * G;
+    const long RB = 512L * BITS + 512L;
+    const uint8_t *blk = pool_base + (long)id * c.Hkv * RB;
+
+    // -- loads: K and V code slices of every kv head in the pack, and the
+    //    (scale, zero) pairs of this lane's four tokens for its own kv head
+    constexpr int KW = BITS;          // dwords per K slice: 32 codes * BITS / 32
+    constexpr int VW = BITS;          // dwords per V slice: 32 codes * BITS / 32
+    uint32_t kw[P][KW], vw[P][VW];
+#pragma unroll
+    for (int a = 0; a < P; ++a) {
+        if (a >= np) continue;
+        const uint8_t *reg = blk + (long)(kh0 + a) * RB;
+        const uint8_t *kp = reg + lo * 16 * BITS + hi * 4 * BITS;
+        const uint8_t *vp = reg + 256 * BITS;
+        if constexpr (BITS == 8) {
+            const uint4 k0 = reinterpret_cast<const uint4 *>(kp)[0];
+            const uint4 k1 = reinterpret_cast<const uint4 *>(kp)[1];
+            const uint4 v0 = reinterpret_cast<const uint4 *>(vp)[lane];
+            const uint4 v1 = reinterpret_cast<const uint4 *>(vp + 1024)[lane];
+            kw[a][0] = k0.x; kw[a][1] = k0.y; kw[a][2] = k0.z; kw[a][3] = k0.w;
+            kw[a][4] = k1.x; kw[a][5] = k1.y; kw[a][6] = k1.z; kw[a][7] = k1.w;
+            vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
+            vw[a][4] = v1.x; vw[a][5] = v1.y; vw[a][6] = v1.z; vw[a][7] = v1.w;
+        } else if constexpr (BITS == 4) {
+            const uint4 k0 = *reinterpret_cast<const uint4 *>(kp);
+            const uint4 v0 = reinterpret_cast<const uint4 *>(vp)[lane];
+            kw[a][0] = k0.x; kw[a][1] = k0.y; kw[a][2] = k0.z; kw[a][3] = k0.w;
+            vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
+        } else {
+            const uint2 k0 = *reinterpret_cast<const uint2 *>(kp);
+            const uint2 v0 = reinterpret_cast<const uint2 *>(vp)[lane];
+            kw[a][0] = k0.x; kw[a][1] = k0.y;
+            vw[a][0] = v0.x; vw[a][1] = v0.y;
+        }
+    }
+    const uint8_t *own = blk + (long)(kh0 + a_rho) * RB + 512 * BITS + 64 * hi;
+    uint32_t ksz[16], vsz[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 kq = reinterpret_cast<const uint4 *>(own)[i];
+        const uint4 vq = reinterpret_cast<const uint4 *>(own + 256)[i];
+        ksz[4 * i + 0] = kq.x; ksz[4 * i + 1] = kq.y; ksz[4 * i + 2] = kq.z; ksz[4 * i + 3] = kq.w;
+        vsz[4 * i + 0] = vq.x; vsz[4 * i + 1] = vq.y; vsz[4 * i + 2] = vq.z; vsz[4 * i + 3] = vq.w;
+    }
+
+    // -- QK^T per group: rows = tokens, columns = the pack's 16 query heads;
+    //    a kv head's codes meet only its own heads (block-diagonal q)
+    floatx4 acc[NGRP];
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) acc[g] = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int a = 0; a < P; ++a) {
+        if (a >= np) continue;
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) {
+            const half8 qb = (a_rho == a && row_ok) ? qop[g] : (half8){};
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS>(kw[a], g), qb, acc[g], 0, 0, 0);
+        }
+    }
+
+    // -- scores of tokens 4hi..4hi+3 for head lo: fold the group scales and
+    //    zeros, base-2 scale, mask cleared slots
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = 0.f;
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) {
+            const uint32_t sz = ksz[4 * i + g];
+            v = fmaf(lo_h(sz), acc[g][i], v);
+            v = fmaf(hi_h(sz), qsum[g], v);
+        }
+        const bool valid = row_ok && ((m16 >> (4 * hi + i)) & 1u);
+        s[i] = valid ? v * scale2 : -INFINITY;
+    }
+    if (row_ok) {
+        float *sp = ws.score + ((size_t)b * c.Hq + (size_t)kh0 * G + lo) * ((size_t)c.max_blocks * BLK) +
+                    (size_t)e * BLK + 4 * hi;
+        *reinterpret_cast<float4 *>(sp) = make_float4(s[0], s[1], s[2], s[3]);
+    }
+
+    // -- online softmax; the max only moves when some score exceeds it
+    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__ballot(bm > st.m)) {
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(st.m, bm);
+        const float alpha = st.m == -INFINITY ? 0.f : exp2f(st.m - mn);
+        st.m = mn;
+        st.l *= alpha;
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) st.z[g] *= alpha;
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * hi + i);
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.o[n][i] *= al[i];
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[i] = s[i] == -INFINITY ? 0.f : exp2f(s[i] - st.m);
+        st.l += p[i];
+    }
+
+    // -- headroom for P' = p * v_scale * mult in fp16
+    {
+        float vmax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) vmax = fmaxf(vmax, lo_h(vsz[j]));
+        if (__ballot(vmax * st.mult > P_HEADROOM)) {
+            for (int off = 1; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+            float nm = st.mult;
+            while (vmax * nm > P_HEADROOM) nm *= 0.5f;
+            const float f = nm / st.mult;
+            st.mult = nm;
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st.o[n][i] *= f;
+        }
+    }
+
+    // -- P' per group in the PV A-operand layout (lane = head, 4 tokens), and
+    //    the zero-point term
+    half4 pop[NGRP];
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) {
+        half4 t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t sz = vsz[4 * i + g];
+            t[i] = (_Float16)(p[i] * lo_h(sz) * st.mult);
+            st.z[g] = fmaf(p[i], hi_h(sz), st.z[g]);
+        }
+        pop[g] = t;
+    }
+
+    // -- PV: block-diagonal over the pack's kv heads
+#pragma unroll
+    for (int a = 0; a < P; ++a) {
+        if (a >= np) continue;
+        const bool mine = a_rho == a && row_ok;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            const half4 pa = mine ? pop[n >> 1] : (half4){};
+            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v_operand<BITS>(vw[a], n), st.o[n], 0, 0, 0);
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(WAVES * 64) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
+                                                         DecodeWs ws, float scale2) {
+    constexpr int P = PACK(G);
+    const int split = blockIdx.x, pack = blockIdx.y, b = blockIdx.z;
+    const int S = gridDim.x, n_packs = gridDim.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lo = lane & 15, hi = lane >> 4;
+    const int kh0 = pack * P, np = min(P, c.Hkv - kh0);
+    const bool row_ok = lo < np * G;
+
+    {   // positions of this sequence start at mass 0 (finalize adds the valid ones)
+        const int w = split * n_packs + pack, W = S * n_packs, len = c.seq_len[b];
+        for (int p = w * WAVES * 64 + tid; p < len; p += W * WAVES * 64) mass[(size_t)b * c.n_cap + p] = 0.f;
+    }
+
+    // -- non-empty table entries of this split, compacted (wave 0)
+    __shared__ uint32_t s_ent[E];
+    __shared__ int s_idx[E];
+    __shared__ uint32_t s_msk[E];
+    __shared__ int s_n;
+    const int nb = c.n_blocks[b];
+    const int e0 = split * E;
+    if (wave == 0) {
+        const int e = e0 + lane;
+        uint32_t ent = 0, m = 0;
+        if (lane < E && e < nb) {
+            ent = c.table[(size_t)b * c.max_blocks + e];
+            m = c.mask[ent >> 30][ent & 0x3fffffffu];
+        }
+        const uint64_t bal = __ballot(m != 0);
+        const int at = __popcll(bal & ((1ull << lane) - 1));
+        if (m != 0) {
+            s_ent[at] = ent;
+            s_idx[at] = e;
+            s_msk[at] = m;
+        }
+        if (lane == 0) s_n = __popcll(bal);
+    }
+
+    // -- q operands (block-diagonal columns) and per-group q sums of head lo
+    half8 qop[NGRP];
+    float qsum[NGRP];
+    {
+        const int h = kh0 * G + lo;
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) {
+            uint4 raw = make_uint4(0, 0, 0, 0);
+            if (row_ok) raw = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + h) * HD + 32 * g + 8 * hi);
+            qop[g] = __builtin_bit_cast(half8, raw);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sum += (float)qop[g][i];
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            qsum[g] = sum;
+        }
+    }
     __syncthreads();
 
-    const int nb = c.n_blocks[b];
-    const int e0 = split * E, e1 = min(nb, e0 + E);
-    const size_t score_row = (size_t)c.max_blocks * BLK;
-    for (int e = e0; e < e1; ++e) {
-        const uint32_t ent = c.table[(size_t)b * c.max_blocks + e];
+    WaveState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+    st.mult = 4096.f;
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) st.z[g] = 0.f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+    const int n_ent = s_n;
+    for (int k = wave; k < n_ent; k += WAVES) {
+        const uint32_t ent = s_ent[k];
         const int pool = (int)(ent >> 30);
         const uint32_t id = ent & 0x3fffffffu;
-        const uint32_t m = c.mask[pool][id];
-        if (m == 0) continue;
-        const int bits = pool_bits(pool);
-        const uint8_t *reg = region_ptr(c.kv[pool], id, c.Hkv, kh, pool);
-        const uint32_t *ksz = reinterpret_cast<const uint32_t *>(reg + 512 * bits);
-        const uint32_t *vsz = reinterpret_cast<const uint32_t *>(reg + 512 * bits + 256);
-        {   // scores: 16 threads per token, 8 channels each
-            const int t = tid >> 4, sub = tid & 15, g = sub >> 2;
-            const uint32_t sz = ksz[t * NGRP + g];
-            const float s = h2f((uint16_t)(sz & 0xffff)), z = h2f((uint16_t)(sz >> 16));
-            float kv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) kv[i] = (float)k_code(reg, bits, t, 8 * sub + i) * s + z;
-            for (int hh = 0; hh < G; ++hh) {
-                float part = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) part += qs[hh][8 * sub + i] * kv[i];
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
-                if (sub == 0) sc[t][hh] = part * scale2;
-            }
-        }
-        __syncthreads();
-        if (tid < G) {
-            float mx = m_run[tid];
-            for (int t = 0; t < BLK; ++t)
-                if ((m >> t) & 1) mx = fmaxf(mx, sc[t][tid]);
-            const float a = exp2f(m_run[tid] - mx);
-            float lsum = 0.f;
-            for (int t = 0; t < BLK; ++t) {
-                const float p = ((m >> t) & 1) ? exp2f(sc[t][tid] - mx) : 0.f;
-                pb[t][tid] = p;
-                lsum += p;
-            }
-            l_run[tid] = l_run[tid] * a + lsum;
-            m_run[tid] = mx;
-            alpha[tid] = a;
-        }
-        for (int i = tid; i < BLK * G; i += THREADS) {
-            const int t = i / G, hh = i % G;
-            ws.score[((size_t)b * c.Hq + kh * G + hh) * score_row + (size_t)e * BLK + t] = sc[t][hh];
-        }
-        __syncthreads();
-        {   // PV: thread owns channel d for heads hh = (tid >> 7) + 2k
-            const int d = tid & (HD - 1), h0 = tid >> 7;
-            for (int k = 0; 2 * k + h0 < G; ++k) acc[k] *= alpha[2 * k + h0];
-            const int g = d / GS;
-            for (int t = 0; t < BLK; ++t) {
-                if (!((m >> t) & 1)) continue;
-                const uint32_t sz = vsz[t * NGRP + g];
-                const float v = (float)v_code(reg, bits, t, d) * h2f((uint16_t)(sz & 0xffff)) +
-                                h2f((uint16_t)(sz >> 16));
-                for (int k = 0; 2 * k + h0 < G; ++k) acc[k] += pb[t][2 * k + h0] * v;
-            }
-        }
-        __syncthreads();
+        if (pool == 0)
+            attend_block<G, 8>(c, c.kv[0], id, kh0, np, s_msk[k], s_idx[k], b, qop, qsum, scale2, ws, st);
+        else if (pool == 1)
+            attend_block<G, 4>(c, c.kv[1], id, kh0, np, s_msk[k], s_idx[k], b, qop, qsum, scale2, ws, st);
+        else
+            attend_block<G, 2>(c, c.kv[2], id, kh0, np, s_msk[k], s_idx[k], b, qop, qsum, scale2, ws, st);
     }
 
-    const size_t base = (size_t)b * c.Hq + kh * G;
-    if (tid < G) {
-        ws.ml[((base + tid) * S + split) * 2 + 0] = m_run[tid];
-        ws.ml[((base + tid) * S + split) * 2 + 1] = l_run[tid];
+    // -- merge the waves of this workgroup and write the split's partial
+    __shared__ float s_m[WAVES][16], s_l[WAVES][16], s_z[WAVES][16][NGRP];
+    __shared__ float s_o[WAVES][16][HD];
+    float lsum = st.l;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    float zs[NGRP];
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) {
+        zs[g] = st.z[g];
+        zs[g] += __shfl_xor(zs[g], 16);
+        zs[g] += __shfl_xor(zs[g], 32);
     }
-    {
-        const int d = tid & (HD - 1), h0 = tid >> 7;
-        for (int k = 0; 2 * k + h0 < G; ++k)
-            ws.o[((base + 2 * k + h0) * S + split) * HD + d] = acc[k];
+    if (hi == 0) {
+        s_m[wave][lo] = st.m;
+        s_l[wave][lo] = lsum;
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) s_z[wave][lo][g] = zs[g];
+    }
+    const float inv_mult = 1.0f / st.mult;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_o[wave][4 * hi + i][16 * n + lo] = st.o[n][i] * inv_mult;
+    __syncthreads();
+
+    const int rows = np * G;
+    for (int idx = tid; idx < rows * HD; idx += WAVES * 64) {
+        const int r = idx / HD, d = idx % HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][r]);
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float mw = s_m[w][r];
+            const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+            L = fmaf(s_l[w][r], f, L);
+            o = fmaf(s_o[w][r][d] + s_z[w][r][d / GS], f, o);
+        }
+        const size_t hrow = (size_t)b * c.Hq + (size_t)kh0 * G + r;
+        ws.o[(hrow * S + split) * HD + d] = o;
+        if (d == 0) {
+            ws.ml[(hrow * S + split) * 2 + 0] = M;
+            ws.ml[(hrow * S + split) * 2 + 1] = L;
+        }
     }
 }
 
@@ -198,8 +456,19 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
                    float decay, float sm_scale, void *ws_ptr, hipStream_t s) {
     DecodeWs ws(ws_ptr, c);
     const int S = n_splits(c);
-    hipLaunchKernelGGL(attn_split, dim3(S, c.Hkv, c.B), dim3(THREADS), 0, s, c,
-                       static_cast<const uint16_t *>(q), mass, ws, sm_scale * LOG2E);
+    const int G = c.Hq / c.Hkv;
+    const int P = PACK(G);
+    const dim3 grid(S, (c.Hkv + P - 1) / P, c.B);
+    const uint16_t *qq = static_cast<const uint16_t *>(q);
+    const float scale2 = sm_scale * LOG2E;
+    switch (G) {
+#define KVQ_G(g) \
+    case g: hipLaunchKernelGGL(attn_split<g>, grid, dim3(WAVES * 64), 0, s, c, qq, mass, ws, scale2); break;
+        KVQ_G(1) KVQ_G(2) KVQ_G(3) KVQ_G(4) KVQ_G(5) KVQ_G(6) KVQ_G(7) KVQ_G(8)
+        KVQ_G(9) KVQ_G(10) KVQ_G(11) KVQ_G(12) KVQ_G(13) KVQ_G(14) KVQ_G(15) KVQ_G(16)
+#undef KVQ_G
+        default: return false;
+    }
     hipLaunchKernelGGL(attn_finalize, dim3(S, c.B), dim3(THREADS), 0, s, c, out, mass, importance,
                        decay, ws, S);
     return hipGetLastError() == hipSuccess;

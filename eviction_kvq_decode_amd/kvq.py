@@ -70,7 +70,10 @@ def _check(rc: int, what: str):
 
 
 def _ptr(t):
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor (or an address passed as an int)."""
+    if t is None or isinstance(t, int):
+        return t
+    return t.data_ptr()
 
 
 class Cache:

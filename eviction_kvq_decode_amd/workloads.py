@@ -15,8 +15,9 @@ no dataset or model is used):
     tag drawn i.i.d. with the workload's R/E/T probabilities
     ("ThinKV", Methodology, thought decomposition into R/E/T segments).
   * Eviction holes (long-trace workload): whole runs are dropped with
-    probability 0.9 (T), 0.5 (E), 0.2 (R), then further passes over the
-    surviving runs until at least 60% of tokens are gone.
+    probability 0.9 (T), 0.5 (E), 0.2 (R); then surviving runs are visited
+    in random order and dropped with the same probabilities until at least
+    60% of the tokens are gone.
   * Prior importance ~ Exponential(mean Hq/N) in fp32.
 Every stream is a numpy PCG64 generator seeded by (workload id, sequence,
 purpose), so any one sequence can be regenerated on its own.
@@ -156,13 +157,17 @@ def keep_plan(w: Workload, b: int, tags: np.ndarray, run_id: np.ndarray) -> np.n
     run_tag = np.zeros(n_runs, dtype=np.int64)
     run_tag[run_id] = tags
     p_drop = np.array([0.2, 0.5, 0.9])[run_tag]
-    alive = np.ones(n_runs, dtype=bool)
     run_len = np.bincount(run_id, minlength=n_runs)
-    while True:
-        drop = (rng.random(n_runs) < p_drop) & alive
-        alive &= ~drop
-        if run_len[~alive].sum() >= w.holes * n:
-            break
+    alive = rng.random(n_runs) >= p_drop               # first pass over all runs
+    gone = int(run_len[~alive].sum())
+    target = w.holes * n
+    while gone < target:                               # later passes stop at the target
+        for r in rng.permutation(np.nonzero(alive)[0]):
+            if rng.random() < p_drop[r]:
+                alive[r] = False
+                gone += int(run_len[r])
+                if gone >= target:
+                    break
     return alive[run_id]
 
 
