@@ -37,10 +37,14 @@ constexpr int WAVES = 4;
 
 // kv heads packed into one wave: the 16 MFMA columns hold PACK(G) * G query heads
 __host__ __device__ constexpr int PACK(int G) { return 16 / G < 4 ? 16 / G : 4; }
-constexpr uint32_t BIAS2 = 0x64006400u;   // two fp16 1024.0: (1024 + c) has c in its low bits
 constexpr float P_HEADROOM = 60000.0f;    // P' = p * v_scale * mult must stay below fp16 max
+constexpr uint32_t BIAS2 = 0x64006400u;   // two fp16 1024.0: (1024 + c) has c in its low bits
 
-// fp16 pair (1024 + lo, 1024 + hi) -> exact (lo, hi).
+// Codes become exact integer-valued fp16 operands: the code bits are placed
+// under the exponent of 1024 (0x64 high byte), giving 1024 + c, and 1024 is
+// subtracted with one packed fp16 add.  (Operands with a zero exponent,
+// i.e. c * 2^-24 subnormals, would save the subtract but lose precision in
+// the MFMA products on this hardware.)
 __device__ inline uint32_t unbias(uint32_t x) {
     half2v h = __builtin_bit_cast(half2v, x);
     h = h - (half2v){(_Float16)1024.0f, (_Float16)1024.0f};
@@ -48,7 +52,7 @@ __device__ inline uint32_t unbias(uint32_t x) {
 }
 // Bytes i and j of w as the exact fp16 pair (w.byte[i], w.byte[j]).
 __device__ inline uint32_t byte_pair(uint32_t w, int i, int j) {
-    const uint32_t sel = (uint32_t)(4 + i) | ((uint32_t)(4 + j) << 16);  // 0 selects a 0x64 byte
+    const uint32_t sel = (uint32_t)(4 + i) | ((uint32_t)(4 + j) << 16);  // selector 0: a 0x64 byte
     return unbias(__builtin_amdgcn_perm(w, 0x64646464u, sel));
 }
 // Fields at bit offsets sh and sh+16 of w (mask m per field) as an exact fp16 pair.
@@ -112,7 +116,7 @@ struct WaveState {
 
 template <int G, int BITS>
 __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base, uint32_t id, int kh0,
-                                    int np, uint32_t m16, int e, int b, const half8 *qop,
+                                    int np, uint32_t m16, int e, int b, const uint4 (*qop)[NGRP][64],
                                     const float *qsum, float scale2, const DecodeWs &ws, WaveState &st) {
     constexpr int P = PACK(G);
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
@@ -125,42 +129,65 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
     //    (scale, zero) pairs of this lane's four tokens for its own kv head
     constexpr int KW = BITS;          // dwords per K slice: 32 codes * BITS / 32
     constexpr int VW = BITS;          // dwords per V slice: 32 codes * BITS / 32
+    // a lane skips the bytes of evicted slots: its K row if token lo is
+    // cleared, its V slice and (scale, zero) pairs if all four tokens
+    // 4hi..4hi+3 are cleared.  Skipped code registers keep stale values:
+    // they are finite subnormals whose products are masked (K) or meet
+    // P' = 0 (V); the (scale, zero) consumers select on g_live.
+    const bool k_live = (m16 >> lo) & 1u;
+    const bool g_live = (m16 >> (4 * hi)) & 15u;
+    const uint32_t k_off = lo * 16 * BITS + hi * 4 * BITS;          // K slice of token lo
+    const uint32_t v_off = 256 * BITS + lane * (BITS == 2 ? 8 : 16); // V slice of lane
+    const uint32_t sz_off = 512 * BITS + 64 * hi;                   // tokens 4hi..4hi+3
     uint32_t kw[P][KW], vw[P][VW];
 #pragma unroll
     for (int a = 0; a < P; ++a) {
-        if (a >= np) continue;
-        const uint8_t *reg = blk + (long)(kh0 + a) * RB;
-        const uint8_t *kp = reg + lo * 16 * BITS + hi * 4 * BITS;
-        const uint8_t *vp = reg + 256 * BITS;
+        // a partial pack re-reads its last kv head; the zero q / P' operands
+        // of the missing heads cancel those products
+        const uint8_t *reg = blk + (uint32_t)(kh0 + min(a, np - 1)) * (uint32_t)RB;
         if constexpr (BITS == 8) {
-            const uint4 k0 = reinterpret_cast<const uint4 *>(kp)[0];
-            const uint4 k1 = reinterpret_cast<const uint4 *>(kp)[1];
-            const uint4 v0 = reinterpret_cast<const uint4 *>(vp)[lane];
-            const uint4 v1 = reinterpret_cast<const uint4 *>(vp + 1024)[lane];
-            kw[a][0] = k0.x; kw[a][1] = k0.y; kw[a][2] = k0.z; kw[a][3] = k0.w;
-            kw[a][4] = k1.x; kw[a][5] = k1.y; kw[a][6] = k1.z; kw[a][7] = k1.w;
-            vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
-            vw[a][4] = v1.x; vw[a][5] = v1.y; vw[a][6] = v1.z; vw[a][7] = v1.w;
+            if (k_live) {
+                const uint4 k0 = *reinterpret_cast<const uint4 *>(reg + k_off);
+                const uint4 k1 = *reinterpret_cast<const uint4 *>(reg + k_off + 16);
+                kw[a][0] = k0.x; kw[a][1] = k0.y; kw[a][2] = k0.z; kw[a][3] = k0.w;
+                kw[a][4] = k1.x; kw[a][5] = k1.y; kw[a][6] = k1.z; kw[a][7] = k1.w;
+            }
+            if (g_live) {
+                const uint4 v0 = *reinterpret_cast<const uint4 *>(reg + v_off);
+                const uint4 v1 = *reinterpret_cast<const uint4 *>(reg + v_off + 1024);
+                vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
+                vw[a][4] = v1.x; vw[a][5] = v1.y; vw[a][6] = v1.z; vw[a][7] = v1.w;
+            }
         } else if constexpr (BITS == 4) {
-            const uint4 k0 = *reinterpret_cast<const uint4 *>(kp);
-            const uint4 v0 = reinterpret_cast<const uint4 *>(vp)[lane];
-            kw[a][0] = k0.x; kw[a][1] = k0.y; kw[a][2] = k0.z; kw[a][3] = k0.w;
-            vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
+            if (k_live) {
+                const uint4 k0 = *reinterpret_cast<const uint4 *>(reg + k_off);
+                kw[a][0] = k0.x; kw[a][1] = k0.y; kw[a][2] = k0.z; kw[a][3] = k0.w;
+            }
+            if (g_live) {
+                const uint4 v0 = *reinterpret_cast<const uint4 *>(reg + v_off);
+                vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
+            }
         } else {
-            const uint2 k0 = *reinterpret_cast<const uint2 *>(kp);
-            const uint2 v0 = reinterpret_cast<const uint2 *>(vp)[lane];
-            kw[a][0] = k0.x; kw[a][1] = k0.y;
-            vw[a][0] = v0.x; vw[a][1] = v0.y;
+            if (k_live) {
+                const uint2 k0 = *reinterpret_cast<const uint2 *>(reg + k_off);
+                kw[a][0] = k0.x; kw[a][1] = k0.y;
+            }
+            if (g_live) {
+                const uint2 v0 = *reinterpret_cast<const uint2 *>(reg + v_off);
+                vw[a][0] = v0.x; vw[a][1] = v0.y;
+            }
         }
     }
-    const uint8_t *own = blk + (long)(kh0 + a_rho) * RB + 512 * BITS + 64 * hi;
+    const uint8_t *own = blk + (uint32_t)(kh0 + a_rho) * (uint32_t)RB + sz_off;
     uint32_t ksz[16], vsz[16];
+    if (g_live) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 kq = reinterpret_cast<const uint4 *>(own)[i];
-        const uint4 vq = reinterpret_cast<const uint4 *>(own + 256)[i];
-        ksz[4 * i + 0] = kq.x; ksz[4 * i + 1] = kq.y; ksz[4 * i + 2] = kq.z; ksz[4 * i + 3] = kq.w;
-        vsz[4 * i + 0] = vq.x; vsz[4 * i + 1] = vq.y; vsz[4 * i + 2] = vq.z; vsz[4 * i + 3] = vq.w;
+        for (int i = 0; i < 4; ++i) {
+            const uint4 kq = reinterpret_cast<const uint4 *>(own)[i];
+            const uint4 vq = reinterpret_cast<const uint4 *>(own + 256)[i];
+            ksz[4 * i + 0] = kq.x; ksz[4 * i + 1] = kq.y; ksz[4 * i + 2] = kq.z; ksz[4 * i + 3] = kq.w;
+            vsz[4 * i + 0] = vq.x; vsz[4 * i + 1] = vq.y; vsz[4 * i + 2] = vq.z; vsz[4 * i + 3] = vq.w;
+        }
     }
 
     // -- QK^T per group: rows = tokens, columns = the pack's 16 query heads;
@@ -170,10 +197,9 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
     for (int g = 0; g < NGRP; ++g) acc[g] = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int a = 0; a < P; ++a) {
-        if (a >= np) continue;
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
-            const half8 qb = (a_rho == a && row_ok) ? qop[g] : (half8){};
+            const half8 qb = __builtin_bit_cast(half8, qop[a][g][lane]);
             acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS>(kw[a], g), qb, acc[g], 0, 0, 0);
         }
     }
@@ -183,6 +209,8 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
     float s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        // group by group, so each group's scale and zero terms (which largely
+        // cancel) meet before the next group is added
         float v = 0.f;
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
@@ -230,6 +258,7 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
         float vmax = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) vmax = fmaxf(vmax, lo_h(vsz[j]));
+        vmax = g_live ? vmax : 0.f;
         if (__ballot(vmax * st.mult > P_HEADROOM)) {
             for (int off = 1; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
             float nm = st.mult;
@@ -249,19 +278,20 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
 #pragma unroll
     for (int g = 0; g < NGRP; ++g) {
         half4 t;
+        float zg = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t sz = vsz[4 * i + g];
             t[i] = (_Float16)(p[i] * lo_h(sz) * st.mult);
-            st.z[g] = fmaf(p[i], hi_h(sz), st.z[g]);
+            zg = fmaf(p[i], hi_h(sz), zg);
         }
-        pop[g] = t;
+        st.z[g] += g_live ? zg : 0.f;
+        pop[g] = g_live ? t : (half4){};
     }
 
     // -- PV: block-diagonal over the pack's kv heads
 #pragma unroll
     for (int a = 0; a < P; ++a) {
-        if (a >= np) continue;
         const bool mine = a_rho == a && row_ok;
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
@@ -272,7 +302,7 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
 }
 
 template <int G>
-__global__ __launch_bounds__(WAVES * 64) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
+__global__ __launch_bounds__(WAVES * 64, 2) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
                                                          DecodeWs ws, float scale2) {
     constexpr int P = PACK(G);
     const int split = blockIdx.x, pack = blockIdx.y, b = blockIdx.z;
@@ -311,19 +341,26 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split(kvq_cache c, const uint
         if (lane == 0) s_n = __popcll(bal);
     }
 
-    // -- q operands (block-diagonal columns) and per-group q sums of head lo
-    half8 qop[NGRP];
+    // -- q operands (lane = head lo, channel slice hi) kept in LDS, and the
+    //    per-group q sums of head lo in registers
+    // s_q[a][g][lane]: q of head lo, channel slice hi of group g if head lo
+    // belongs to kv head a of the pack, else zero (block-diagonal columns)
+    __shared__ uint4 s_q[P][NGRP][64];
     float qsum[NGRP];
     {
         const int h = kh0 * G + lo;
+        const int a_lo = lo / G;
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
             uint4 raw = make_uint4(0, 0, 0, 0);
             if (row_ok) raw = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + h) * HD + 32 * g + 8 * hi);
-            qop[g] = __builtin_bit_cast(half8, raw);
+            if (wave == 0)
+#pragma unroll
+                for (int a = 0; a < P; ++a) s_q[a][g][lane] = a == a_lo ? raw : make_uint4(0, 0, 0, 0);
+            const half8 qv = __builtin_bit_cast(half8, raw);
             float sum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sum += (float)qop[g][i];
+            for (int i = 0; i < 8; ++i) sum += (float)qv[i];
             sum += __shfl_xor(sum, 16);
             sum += __shfl_xor(sum, 32);
             qsum[g] = sum;
@@ -342,15 +379,18 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split(kvq_cache c, const uint
 
     const int n_ent = s_n;
     for (int k = wave; k < n_ent; k += WAVES) {
-        const uint32_t ent = s_ent[k];
+        // block metadata is wave-uniform: keep it in scalar registers
+        const uint32_t ent = __builtin_amdgcn_readfirstlane(s_ent[k]);
+        const uint32_t msk = __builtin_amdgcn_readfirstlane(s_msk[k]);
+        const int eix = __builtin_amdgcn_readfirstlane(s_idx[k]);
         const int pool = (int)(ent >> 30);
         const uint32_t id = ent & 0x3fffffffu;
         if (pool == 0)
-            attend_block<G, 8>(c, c.kv[0], id, kh0, np, s_msk[k], s_idx[k], b, qop, qsum, scale2, ws, st);
+            attend_block<G, 8>(c, c.kv[0], id, kh0, np, msk, eix, b, s_q, qsum, scale2, ws, st);
         else if (pool == 1)
-            attend_block<G, 4>(c, c.kv[1], id, kh0, np, s_msk[k], s_idx[k], b, qop, qsum, scale2, ws, st);
+            attend_block<G, 4>(c, c.kv[1], id, kh0, np, msk, eix, b, s_q, qsum, scale2, ws, st);
         else
-            attend_block<G, 2>(c, c.kv[2], id, kh0, np, s_msk[k], s_idx[k], b, qop, qsum, scale2, ws, st);
+            attend_block<G, 2>(c, c.kv[2], id, kh0, np, msk, eix, b, s_q, qsum, scale2, ws, st);
     }
 
     // -- merge the waves of this workgroup and write the split's partial
@@ -409,39 +449,83 @@ __global__ __launch_bounds__(THREADS) void attn_finalize(kvq_cache c, float *out
     const int tid = threadIdx.x;
     const int nb = c.n_blocks[b];
     const int s_act = (nb + E - 1) / E;
+    const int Hq = c.Hq;
     __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
-    for (int h = tid; h < c.Hq; h += THREADS) {
-        const float *ml = ws.ml + ((size_t)b * c.Hq + h) * S * 2;
-        float M = -INFINITY;
-        for (int s = 0; s < s_act; ++s) M = fmaxf(M, ml[2 * s]);
-        float L = 0.f;
-        for (int s = 0; s < s_act; ++s)
-            if (ml[2 * s] != -INFINITY) L += ml[2 * s + 1] * exp2f(ml[2 * s] - M);
-        Mh[h] = M;
-        Rh[h] = L > 0.f ? 1.0f / L : 0.f;
+    __shared__ float pm[THREADS], pl[THREADS];
+    __shared__ uint32_t s_ent[E], s_msk[E];
+
+    // stage this chunk's table entries and masks
+    const int e0 = chunk * E;
+    if (tid < E) {
+        uint32_t ent = 0, m = 0;
+        if (e0 + tid < nb) {
+            ent = c.table[(size_t)b * c.max_blocks + e0 + tid];
+            m = c.mask[ent >> 30][ent & 0x3fffffffu];
+        }
+        s_ent[tid] = ent;
+        s_msk[tid] = m;
     }
-    __syncthreads();
-    for (int h = chunk; h < c.Hq; h += C) {
+    // global max / sum per head: TPH threads per head, each over a stride of splits
+    int tph = 1;
+    while (tph * 2 * Hq <= THREADS) tph *= 2;
+    for (int h0 = 0; h0 < Hq; h0 += THREADS / tph) {
+        const int h = h0 + tid / tph, j = tid % tph;
+        float M = -INFINITY, L = 0.f;
+        if (h < Hq) {
+            const float *ml = ws.ml + ((size_t)b * Hq + h) * S * 2;
+            for (int s = j; s < s_act; s += tph) {
+                const float m = ml[2 * s], l = ml[2 * s + 1];
+                if (m == -INFINITY) continue;
+                if (m > M) {
+                    L = L * exp2f(M - m) + l;
+                    M = m;
+                } else {
+                    L += l * exp2f(m - M);
+                }
+            }
+        }
+        pm[tid] = M;
+        pl[tid] = L;
+        __syncthreads();
+        if (j == 0 && h < Hq) {
+            float MM = -INFINITY;
+            for (int k = 0; k < tph; ++k) MM = fmaxf(MM, pm[tid + k]);
+            float LL = 0.f;
+            for (int k = 0; k < tph; ++k)
+                if (pm[tid + k] != -INFINITY) LL += pl[tid + k] * exp2f(pm[tid + k] - MM);
+            Mh[h] = MM;
+            Rh[h] = LL > 0.f ? 1.0f / LL : 0.f;
+        }
+        __syncthreads();
+    }
+
+    // output rows of the heads this chunk owns
+    for (int h = chunk; h < Hq; h += C) {
         if (tid >= HD) break;
-        const float *ml = ws.ml + ((size_t)b * c.Hq + h) * S * 2;
-        const float *o = ws.o + ((size_t)b * c.Hq + h) * S * HD;
+        const float *ml = ws.ml + ((size_t)b * Hq + h) * S * 2;
+        const float *o = ws.o + ((size_t)b * Hq + h) * S * HD;
         float acc = 0.f;
-        for (int s = 0; s < s_act; ++s)
-            if (ml[2 * s] != -INFINITY) acc += o[(size_t)s * HD + tid] * exp2f(ml[2 * s] - Mh[h]);
-        out[((size_t)b * c.Hq + h) * HD + tid] = acc * Rh[h];
+        for (int s = 0; s < s_act; ++s) {
+            const float m = ml[2 * s];
+            if (m != -INFINITY) acc = fmaf(o[(size_t)s * HD + tid], exp2f(m - Mh[h]), acc);
+        }
+        out[((size_t)b * Hq + h) * HD + tid] = acc * Rh[h];
     }
+
+    // mass (and importance) of the valid slots of this chunk's entries
     const size_t score_row = (size_t)c.max_blocks * BLK;
+    const float *sbase = ws.score + (size_t)b * Hq * score_row;
+#pragma unroll 1
     for (int i = tid; i < E * BLK; i += THREADS) {
-        const int e = chunk * E + i / BLK, t = i % BLK;
-        if (e >= nb) break;
-        const uint32_t ent = c.table[(size_t)b * c.max_blocks + e];
-        const int pool = (int)(ent >> 30);
-        const uint32_t id = ent & 0x3fffffffu;
-        if (!((c.mask[pool][id] >> t) & 1)) continue;
-        const int p = c.pos[pool][(size_t)id * BLK + t];
-        const float *sp = ws.score + (size_t)b * c.Hq * score_row + (size_t)e * BLK + t;
+        const int k = i / BLK, t = i % BLK;
+        const uint32_t m = s_msk[k];
+        if (!((m >> t) & 1)) continue;
+        const uint32_t ent = s_ent[k];
+        const int p = c.pos[ent >> 30][(size_t)(ent & 0x3fffffffu) * BLK + t];
+        const float *sp = sbase + (size_t)(e0 + k) * BLK + t;
         float sum = 0.f;
-        for (int h = 0; h < c.Hq; ++h) sum += exp2f(sp[h * score_row] - Mh[h]) * Rh[h];
+#pragma unroll 8
+        for (int h = 0; h < Hq; ++h) sum += exp2f(sp[h * score_row] - Mh[h]) * Rh[h];
         mass[(size_t)b * c.n_cap + p] = sum;
         if (importance) {
             float *ip = importance + (size_t)b * c.n_cap + p;
