@@ -26,6 +26,7 @@ namespace {
 constexpr int E = ENTRIES_PER_SPLIT;
 constexpr int THREADS = 256;
 constexpr int MAX_HQ = 256;
+constexpr int MAX_B = 1024;       // sequences per call handled by the split kernel's item prefix
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -33,7 +34,13 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int WAVES = 4;
+#ifndef KVQ_WAVES
+#define KVQ_WAVES 4          // waves per split workgroup
+#endif
+#ifndef KVQ_MIN_WAVES_PER_SIMD
+#define KVQ_MIN_WAVES_PER_SIMD 2
+#endif
+constexpr int WAVES = KVQ_WAVES;
 
 // kv heads packed into one wave: the 16 MFMA columns hold PACK(G) * G query heads
 __host__ __device__ constexpr int PACK(int G) { return 16 / G < 4 ? 16 / G : 4; }
@@ -301,51 +308,66 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
     }
 }
 
+// Workgroup LDS of the split kernel.
+template <int P>
+struct SplitLds {
+    uint32_t ent[E];
+    int idx[E];
+    uint32_t msk[E];
+    int n;
+    uint4 q[P][NGRP][64];
+    float m[WAVES][16], l[WAVES][16], z[WAVES][16][NGRP];
+    float o[WAVES][16][HD];
+};
+
+// One work item (sequence, kv-head pack, run of E entries).
 template <int G>
-__global__ __launch_bounds__(WAVES * 64, 2) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
-                                                         DecodeWs ws, float scale2) {
+__device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const DecodeWs &ws,
+                                        float scale2, int S, int item, const int *s_first,
+                                        SplitLds<PACK(G)> &sh) {
     constexpr int P = PACK(G);
-    const int split = blockIdx.x, pack = blockIdx.y, b = blockIdx.z;
-    const int S = gridDim.x, n_packs = gridDim.y;
+    const int n_packs = (c.Hkv + P - 1) / P;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lo = lane & 15, hi = lane >> 4;
+    // decode the item: sequence by binary search over the item prefix
+    int lo_b = 0, hi_b = c.B - 1;
+    while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if (s_first[mid] <= item) lo_b = mid; else hi_b = mid - 1;
+    }
+    const int b = lo_b;
+    const int r = item - s_first[b];
+    const int pack = r % n_packs, split = r / n_packs;
     const int kh0 = pack * P, np = min(P, c.Hkv - kh0);
     const bool row_ok = lo < np * G;
 
-    {   // positions of this sequence start at mass 0 (finalize adds the valid ones)
-        const int w = split * n_packs + pack, W = S * n_packs, len = c.seq_len[b];
-        for (int p = w * WAVES * 64 + tid; p < len; p += W * WAVES * 64) mass[(size_t)b * c.n_cap + p] = 0.f;
-    }
-
-    // -- non-empty table entries of this split, compacted (wave 0)
-    __shared__ uint32_t s_ent[E];
-    __shared__ int s_idx[E];
-    __shared__ uint32_t s_msk[E];
-    __shared__ int s_n;
+    // -- non-empty table entries of this run, compacted (wave 0)
     const int nb = c.n_blocks[b];
     const int e0 = split * E;
     if (wave == 0) {
-        const int e = e0 + lane;
-        uint32_t ent = 0, m = 0;
-        if (lane < E && e < nb) {
-            ent = c.table[(size_t)b * c.max_blocks + e];
-            m = c.mask[ent >> 30][ent & 0x3fffffffu];
+        int n = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int e = e0 + base + lane;
+            uint32_t ent = 0, m = 0;
+            if (base + lane < E && e < nb) {
+                ent = c.table[(size_t)b * c.max_blocks + e];
+                m = c.mask[ent >> 30][ent & 0x3fffffffu];
+            }
+            const uint64_t bal = __ballot(m != 0);
+            const int at = n + __popcll(bal & ((1ull << lane) - 1));
+            if (m != 0) {
+                sh.ent[at] = ent;
+                sh.idx[at] = e;
+                sh.msk[at] = m;
+            }
+            n += __popcll(bal);
         }
-        const uint64_t bal = __ballot(m != 0);
-        const int at = __popcll(bal & ((1ull << lane) - 1));
-        if (m != 0) {
-            s_ent[at] = ent;
-            s_idx[at] = e;
-            s_msk[at] = m;
-        }
-        if (lane == 0) s_n = __popcll(bal);
+        if (lane == 0) sh.n = n;
     }
 
-    // -- q operands (lane = head lo, channel slice hi) kept in LDS, and the
-    //    per-group q sums of head lo in registers
-    // s_q[a][g][lane]: q of head lo, channel slice hi of group g if head lo
-    // belongs to kv head a of the pack, else zero (block-diagonal columns)
-    __shared__ uint4 s_q[P][NGRP][64];
+    // -- q operands: sh.q[a][g][lane] is q of head lo, channel slice hi of
+    //    group g if head lo belongs to kv head a of the pack, else zero
+    //    (block-diagonal columns); per-group q sums of head lo in registers
     float qsum[NGRP];
     {
         const int h = kh0 * G + lo;
@@ -356,7 +378,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_split(kvq_cache c, const u
             if (row_ok) raw = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + h) * HD + 32 * g + 8 * hi);
             if (wave == 0)
 #pragma unroll
-                for (int a = 0; a < P; ++a) s_q[a][g][lane] = a == a_lo ? raw : make_uint4(0, 0, 0, 0);
+                for (int a = 0; a < P; ++a) sh.q[a][g][lane] = a == a_lo ? raw : make_uint4(0, 0, 0, 0);
             const half8 qv = __builtin_bit_cast(half8, raw);
             float sum = 0.f;
 #pragma unroll
@@ -377,25 +399,23 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_split(kvq_cache c, const u
 #pragma unroll
     for (int n = 0; n < 8; ++n) st.o[n] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    const int n_ent = s_n;
+    const int n_ent = sh.n;
     for (int k = wave; k < n_ent; k += WAVES) {
         // block metadata is wave-uniform: keep it in scalar registers
-        const uint32_t ent = __builtin_amdgcn_readfirstlane(s_ent[k]);
-        const uint32_t msk = __builtin_amdgcn_readfirstlane(s_msk[k]);
-        const int eix = __builtin_amdgcn_readfirstlane(s_idx[k]);
+        const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
+        const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
+        const int eix = __builtin_amdgcn_readfirstlane(sh.idx[k]);
         const int pool = (int)(ent >> 30);
         const uint32_t id = ent & 0x3fffffffu;
         if (pool == 0)
-            attend_block<G, 8>(c, c.kv[0], id, kh0, np, msk, eix, b, s_q, qsum, scale2, ws, st);
+            attend_block<G, 8>(c, c.kv[0], id, kh0, np, msk, eix, b, sh.q, qsum, scale2, ws, st);
         else if (pool == 1)
-            attend_block<G, 4>(c, c.kv[1], id, kh0, np, msk, eix, b, s_q, qsum, scale2, ws, st);
+            attend_block<G, 4>(c, c.kv[1], id, kh0, np, msk, eix, b, sh.q, qsum, scale2, ws, st);
         else
-            attend_block<G, 2>(c, c.kv[2], id, kh0, np, msk, eix, b, s_q, qsum, scale2, ws, st);
+            attend_block<G, 2>(c, c.kv[2], id, kh0, np, msk, eix, b, sh.q, qsum, scale2, ws, st);
     }
 
-    // -- merge the waves of this workgroup and write the split's partial
-    __shared__ float s_m[WAVES][16], s_l[WAVES][16], s_z[WAVES][16][NGRP];
-    __shared__ float s_o[WAVES][16][HD];
+    // -- merge the waves of this workgroup and write the run's partial
     float lsum = st.l;
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
@@ -407,39 +427,94 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_split(kvq_cache c, const u
         zs[g] += __shfl_xor(zs[g], 32);
     }
     if (hi == 0) {
-        s_m[wave][lo] = st.m;
-        s_l[wave][lo] = lsum;
+        sh.m[wave][lo] = st.m;
+        sh.l[wave][lo] = lsum;
 #pragma unroll
-        for (int g = 0; g < NGRP; ++g) s_z[wave][lo][g] = zs[g];
+        for (int g = 0; g < NGRP; ++g) sh.z[wave][lo][g] = zs[g];
     }
     const float inv_mult = 1.0f / st.mult;
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_o[wave][4 * hi + i][16 * n + lo] = st.o[n][i] * inv_mult;
+        for (int i = 0; i < 4; ++i) sh.o[wave][4 * hi + i][16 * n + lo] = st.o[n][i] * inv_mult;
     __syncthreads();
 
     const int rows = np * G;
     for (int idx = tid; idx < rows * HD; idx += WAVES * 64) {
-        const int r = idx / HD, d = idx % HD;
+        const int rr = idx / HD, d = idx % HD;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][r]);
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.m[w][rr]);
         float L = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            const float mw = s_m[w][r];
+            const float mw = sh.m[w][rr];
             const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-            L = fmaf(s_l[w][r], f, L);
-            o = fmaf(s_o[w][r][d] + s_z[w][r][d / GS], f, o);
+            L = fmaf(sh.l[w][rr], f, L);
+            o = fmaf(sh.o[w][rr][d] + sh.z[w][rr][d / GS], f, o);
         }
-        const size_t hrow = (size_t)b * c.Hq + (size_t)kh0 * G + r;
+        const size_t hrow = (size_t)b * c.Hq + (size_t)kh0 * G + rr;
         ws.o[(hrow * S + split) * HD + d] = o;
         if (d == 0) {
             ws.ml[(hrow * S + split) * 2 + 0] = M;
             ws.ml[(hrow * S + split) * 2 + 1] = L;
         }
     }
+    __syncthreads();   // LDS is reused by the next item
+}
+
+// Work items are (sequence, kv-head pack, run of E table entries), ordered
+// by sequence, pack, run, for the runs that hold entries.  The kernel is
+// persistent: gridDim.x workgroups (what fits on the GPU at once) take the
+// items round-robin, so the dispatcher never has to refill slots and no
+// workgroup is launched for a run past a sequence's end.
+template <int G>
+__global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
+                                                         DecodeWs ws, float scale2, int S) {
+    constexpr int P = PACK(G);
+    const int n_packs = (c.Hkv + P - 1) / P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lo = lane & 15, hi = lane >> 4;
+    constexpr int NT = WAVES * 64;
+
+    // -- item prefix: s_first[b] = first item of sequence b (items per
+    //    sequence = active runs * packs)
+    __shared__ int s_first[MAX_B + 1];
+    __shared__ int s_carry;
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int b0 = 0; b0 < c.B; b0 += NT) {
+        const int bb = b0 + tid;
+        const int cnt = bb < c.B ? ((c.n_blocks[bb] + E - 1) / E) * n_packs : 0;
+        // inclusive scan of cnt over the workgroup (Hillis-Steele in LDS)
+        __shared__ int s_scan[NT];
+        s_scan[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < NT; off <<= 1) {
+            const int v = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += v;
+            __syncthreads();
+        }
+        if (bb < c.B) s_first[bb] = s_carry + s_scan[tid] - cnt;
+        __syncthreads();
+        if (tid == NT - 1) s_carry += s_scan[NT - 1];
+        __syncthreads();
+    }
+    if (tid == 0) s_first[c.B] = s_carry;
+    __syncthreads();
+    const int n_items = s_first[c.B];
+
+    // -- every position below seq_len starts at mass 0; the finalize pass
+    //    writes the valid ones.  Grid-stride over (sequence, position).
+    for (int bb = 0; bb < c.B; ++bb) {
+        const int len = c.seq_len[bb];
+        for (int p = blockIdx.x * NT + tid; p < len; p += gridDim.x * NT) mass[(size_t)bb * c.n_cap + p] = 0.f;
+    }
+
+    __shared__ SplitLds<P> lds;
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x)
+        split_item<G>(c, q, ws, scale2, S, item, s_first, lds);
 }
 
 __global__ __launch_bounds__(THREADS) void attn_finalize(kvq_cache c, float *out, float *mass,
@@ -456,14 +531,14 @@ __global__ __launch_bounds__(THREADS) void attn_finalize(kvq_cache c, float *out
 
     // stage this chunk's table entries and masks
     const int e0 = chunk * E;
-    if (tid < E) {
+    for (int k = tid; k < E; k += THREADS) {
         uint32_t ent = 0, m = 0;
-        if (e0 + tid < nb) {
-            ent = c.table[(size_t)b * c.max_blocks + e0 + tid];
+        if (e0 + k < nb) {
+            ent = c.table[(size_t)b * c.max_blocks + e0 + k];
             m = c.mask[ent >> 30][ent & 0x3fffffffu];
         }
-        s_ent[tid] = ent;
-        s_msk[tid] = m;
+        s_ent[k] = ent;
+        s_msk[k] = m;
     }
     // global max / sum per head: TPH threads per head, each over a stride of splits
     int tph = 1;
@@ -536,18 +611,36 @@ __global__ __launch_bounds__(THREADS) void attn_finalize(kvq_cache c, float *out
 
 }  // namespace
 
+// Workgroups of attn_split<G> that fit on the device at once (cached).
+int persistent_grid(int G, const void *kernel) {
+    static int cache[64][KVQ_MAX_GQA + 1];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int &v = cache[dev][G];
+    if (v == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WAVES * 64, 0) != hipSuccess) return 0;
+        v = cus * (per_cu > 0 ? per_cu : 1);
+    }
+    return v;
+}
+
 bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, float *importance,
                    float decay, float sm_scale, void *ws_ptr, hipStream_t s) {
     DecodeWs ws(ws_ptr, c);
     const int S = n_splits(c);
     const int G = c.Hq / c.Hkv;
-    const int P = PACK(G);
-    const dim3 grid(S, (c.Hkv + P - 1) / P, c.B);
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     const float scale2 = sm_scale * LOG2E;
     switch (G) {
-#define KVQ_G(g) \
-    case g: hipLaunchKernelGGL(attn_split<g>, grid, dim3(WAVES * 64), 0, s, c, qq, mass, ws, scale2); break;
+#define KVQ_G(g)                                                                                   \
+    case g: {                                                                                      \
+        const int grid = persistent_grid(g, reinterpret_cast<const void *>(attn_split<g>));         \
+        if (grid <= 0) return false;                                                               \
+        hipLaunchKernelGGL(attn_split<g>, dim3(grid), dim3(WAVES * 64), 0, s, c, qq, mass, ws, scale2, S); \
+        break;                                                                                     \
+    }
         KVQ_G(1) KVQ_G(2) KVQ_G(3) KVQ_G(4) KVQ_G(5) KVQ_G(6) KVQ_G(7) KVQ_G(8)
         KVQ_G(9) KVQ_G(10) KVQ_G(11) KVQ_G(12) KVQ_G(13) KVQ_G(14) KVQ_G(15) KVQ_G(16)
 #undef KVQ_G

@@ -3,13 +3,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 
 namespace kvq {
 
 // Decode split-K: a split covers this many table entries of one sequence
-// and kv head.
-constexpr int ENTRIES_PER_SPLIT = 64;
+// and kv-head pack.
+#ifndef KVQ_ENTRIES_PER_SPLIT
+#define KVQ_ENTRIES_PER_SPLIT 64
+#endif
+constexpr int ENTRIES_PER_SPLIT = KVQ_ENTRIES_PER_SPLIT;
 
 inline int n_splits(const kvq_cache &c) {
     return (c.max_blocks + ENTRIES_PER_SPLIT - 1) / ENTRIES_PER_SPLIT;
