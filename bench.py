@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run 3 device-to-device copies of this many MiB before the steps "
+                         "(a kernel of known traffic, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the path shards by sequence "
@@ -162,6 +165,14 @@ def main():
         cache.decode(Q[s], out, mass)
         ev[s][1].record()
 
+    if args.copy_probe_mb > 0:
+        src = torch.ones(args.copy_probe_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[gpu] copy probe: 3 x {args.copy_probe_mb} MB read + written")
+        del src, dst
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()

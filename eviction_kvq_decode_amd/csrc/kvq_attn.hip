@@ -24,7 +24,6 @@ namespace kvq {
 namespace {
 
 constexpr int E = ENTRIES_PER_SPLIT;
-constexpr int THREADS = 256;
 constexpr int MAX_HQ = 256;
 constexpr int MAX_B = 1024;       // sequences per call handled by the split kernel's item prefix
 constexpr float LOG2E = 1.4426950408889634f;
@@ -121,10 +120,16 @@ struct WaveState {
     float mult;      // power-of-two headroom factor applied to P'
 };
 
+// The block's slot positions, read by the first kv-head pack only.
+__device__ inline const int *pos_blk(const kvq_cache &c, int pool, uint32_t id, int pack) {
+    return pack == 0 ? c.pos[pool] + (size_t)id * BLK : nullptr;
+}
+
 template <int G, int BITS>
 __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base, uint32_t id, int kh0,
-                                    int np, uint32_t m16, int e, int b, const uint4 (*qop)[NGRP][64],
-                                    const float *qsum, float scale2, const DecodeWs &ws, WaveState &st) {
+                                    int np, uint32_t m16, float *srow, int *prow, const int *pos_blk,
+                                    const uint4 (*qop)[NGRP][64], const float *qsum, float scale2,
+                                    const DecodeWs &ws, WaveState &st) {
     constexpr int P = PACK(G);
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
     const int a_rho = min(lo / G, np - 1);
@@ -185,6 +190,10 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
             }
         }
     }
+    // positions of tokens 4hi..4hi+3 (one lane per token group, first pack
+    // of the sequence only): copied next to the score rows
+    int4 pos4 = make_int4(0, 0, 0, 0);
+    if (pos_blk != nullptr && lo == 0 && g_live) pos4 = reinterpret_cast<const int4 *>(pos_blk)[hi];
     const uint8_t *own = blk + (uint32_t)(kh0 + a_rho) * (uint32_t)RB + sz_off;
     uint32_t ksz[16], vsz[16];
     if (g_live) {
@@ -228,10 +237,24 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
         const bool valid = row_ok && ((m16 >> (4 * hi + i)) & 1u);
         s[i] = valid ? v * scale2 : -INFINITY;
     }
-    if (row_ok) {
-        float *sp = ws.score + ((size_t)b * c.Hq + (size_t)kh0 * G + lo) * ((size_t)c.max_blocks * BLK) +
-                    (size_t)e * BLK + 4 * hi;
-        *reinterpret_cast<float4 *>(sp) = make_float4(s[0], s[1], s[2], s[3]);
+    {
+        // score rows: valid slots only, in slot order from srow; the Hq
+        // scores of a slot are contiguous
+        const uint32_t below = m16 & ((1u << (4 * hi)) - 1u);
+        float *sp = srow + (size_t)__popc(below) * c.Hq + (size_t)kh0 * G + lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (s[i] != -INFINITY) {
+                *sp = s[i];
+                sp += c.Hq;
+            }
+        if (pos_blk != nullptr && lo == 0) {
+            int *pp = prow + __popc(below);
+            const int pv[4] = {pos4.x, pos4.y, pos4.z, pos4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if ((m16 >> (4 * hi + i)) & 1u) *pp++ = pv[i];
+        }
     }
 
     // -- online softmax; the max only moves when some score exceeds it
@@ -312,8 +335,8 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
 template <int P>
 struct SplitLds {
     uint32_t ent[E];
-    int idx[E];
     uint32_t msk[E];
+    int rb[E];         // first score row of the entry within the run
     int n;
     uint4 q[P][NGRP][64];
     float m[WAVES][16], l[WAVES][16], z[WAVES][16][NGRP];
@@ -345,7 +368,7 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     const int nb = c.n_blocks[b];
     const int e0 = split * E;
     if (wave == 0) {
-        int n = 0;
+        int n = 0, rows = 0;
         for (int base = 0; base < E; base += 64) {
             const int e = e0 + base + lane;
             uint32_t ent = 0, m = 0;
@@ -355,14 +378,25 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
             }
             const uint64_t bal = __ballot(m != 0);
             const int at = n + __popcll(bal & ((1ull << lane) - 1));
+            // exclusive prefix of valid-slot counts: the entry's first row
+            int cnt = __popc(m), incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(incl, d);
+                if (lane >= d) incl += v;
+            }
             if (m != 0) {
                 sh.ent[at] = ent;
-                sh.idx[at] = e;
                 sh.msk[at] = m;
+                sh.rb[at] = rows + incl - cnt;
             }
             n += __popcll(bal);
+            rows += __shfl(incl, 63);
         }
-        if (lane == 0) sh.n = n;
+        if (lane == 0) {
+            sh.n = n;
+            if (pack == 0) ws.rows[(size_t)b * S + split] = rows;
+        }
     }
 
     // -- q operands: sh.q[a][g][lane] is q of head lo, channel slice hi of
@@ -404,15 +438,17 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         // block metadata is wave-uniform: keep it in scalar registers
         const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
         const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
-        const int eix = __builtin_amdgcn_readfirstlane(sh.idx[k]);
+        const size_t row0 = (size_t)(b * S + split) * (E * BLK) + (size_t)__builtin_amdgcn_readfirstlane(sh.rb[k]);
+        float *srow = ws.score + row0 * c.Hq;
+        int *prow = ws.spos + row0;
         const int pool = (int)(ent >> 30);
         const uint32_t id = ent & 0x3fffffffu;
         if (pool == 0)
-            attend_block<G, 8>(c, c.kv[0], id, kh0, np, msk, eix, b, sh.q, qsum, scale2, ws, st);
+            attend_block<G, 8>(c, c.kv[0], id, kh0, np, msk, srow, prow, pos_blk(c, 0, id, pack), sh.q, qsum, scale2, ws, st);
         else if (pool == 1)
-            attend_block<G, 4>(c, c.kv[1], id, kh0, np, msk, eix, b, sh.q, qsum, scale2, ws, st);
+            attend_block<G, 4>(c, c.kv[1], id, kh0, np, msk, srow, prow, pos_blk(c, 1, id, pack), sh.q, qsum, scale2, ws, st);
         else
-            attend_block<G, 2>(c, c.kv[2], id, kh0, np, msk, eix, b, sh.q, qsum, scale2, ws, st);
+            attend_block<G, 2>(c, c.kv[2], id, kh0, np, msk, srow, prow, pos_blk(c, 2, id, pack), sh.q, qsum, scale2, ws, st);
     }
 
     // -- merge the waves of this workgroup and write the run's partial
@@ -517,95 +553,200 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
         split_item<G>(c, q, ws, scale2, S, item, s_first, lds);
 }
 
-__global__ __launch_bounds__(THREADS) void attn_finalize(kvq_cache c, float *out, float *mass,
-                                                         float *importance, float decay, DecodeWs ws,
-                                                         int S) {
-    const int chunk = blockIdx.x, b = blockIdx.y, C = gridDim.x;
-    const int tid = threadIdx.x;
+// Finalize: one workgroup per (run of E entries, sequence).  The run's
+// valid slots are rows of Hq scores with their positions; RPL lanes share a
+// row, each reading four heads.  Two dependent rounds of loads: the row
+// count and split partials, then the rows.
+constexpr int FT = 256;
+
+template <int RPL>
+__global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass,
+                                                    float *importance, float decay, DecodeWs ws, int S) {
+    constexpr int ROWS = FT / RPL;             // rows one pass of the workgroup covers
+    constexpr int BATCH = 16;                  // passes whose loads are issued together
+    static_assert(2 * RPL >= BATCH, "row positions: two passes per lane");
+    const int split = blockIdx.x, b = blockIdx.y, X = gridDim.x;
+    const int tid = threadIdx.x, j = tid % RPL;
     const int nb = c.n_blocks[b];
     const int s_act = (nb + E - 1) / E;
     const int Hq = c.Hq;
+    if (split >= s_act && split >= Hq) return;   // no rows and no output head
     __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
-    __shared__ float pm[THREADS], pl[THREADS];
-    __shared__ uint32_t s_ent[E], s_msk[E];
+    __shared__ float4 red[FT];
 
-    // stage this chunk's table entries and masks
-    const int e0 = chunk * E;
-    for (int k = tid; k < E; k += THREADS) {
-        uint32_t ent = 0, m = 0;
-        if (e0 + k < nb) {
-            ent = c.table[(size_t)b * c.max_blocks + e0 + k];
-            m = c.mask[ent >> 30][ent & 0x3fffffffu];
-        }
-        s_ent[k] = ent;
-        s_msk[k] = m;
-    }
-    // global max / sum per head: TPH threads per head, each over a stride of splits
-    int tph = 1;
-    while (tph * 2 * Hq <= THREADS) tph *= 2;
-    for (int h0 = 0; h0 < Hq; h0 += THREADS / tph) {
-        const int h = h0 + tid / tph, j = tid % tph;
-        float M = -INFINITY, L = 0.f;
+    // (1) row count, split (m, l) pairs of every head, and the partial
+    //     outputs of the head this workgroup writes
+    const int n_rows = split < s_act ? ws.rows[(size_t)b * S + split] : 0;
+    int tpg = 64;
+    while (tpg > 1 && tpg * Hq > FT) tpg >>= 1;
+    float M = -INFINITY, L = 0.f;
+    {
+        // one pass of tpg lanes per head covers Hq <= FT / tpg heads; more
+        // heads take more passes below
+        const int h = tid / tpg, jj = tid % tpg;
         if (h < Hq) {
-            const float *ml = ws.ml + ((size_t)b * Hq + h) * S * 2;
-            for (int s = j; s < s_act; s += tph) {
-                const float m = ml[2 * s], l = ml[2 * s + 1];
-                if (m == -INFINITY) continue;
-                if (m > M) {
-                    L = L * exp2f(M - m) + l;
-                    M = m;
-                } else {
-                    L += l * exp2f(m - M);
+            const float2 *ml = reinterpret_cast<const float2 *>(ws.ml + ((size_t)b * Hq + h) * S * 2);
+            for (int s0 = jj; s0 < s_act; s0 += 8 * tpg) {
+                float2 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int s = s0 + u * tpg;
+                    v[u] = s < s_act ? ml[s] : make_float2(-INFINITY, 0.f);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (v[u].x == -INFINITY) continue;
+                    if (v[u].x > M) {
+                        L = L * exp2f(M - v[u].x) + v[u].y;
+                        M = v[u].x;
+                    } else {
+                        L += v[u].y * exp2f(v[u].x - M);
+                    }
                 }
             }
         }
-        pm[tid] = M;
-        pl[tid] = L;
-        __syncthreads();
-        if (j == 0 && h < Hq) {
-            float MM = -INFINITY;
-            for (int k = 0; k < tph; ++k) MM = fmaxf(MM, pm[tid + k]);
-            float LL = 0.f;
-            for (int k = 0; k < tph; ++k)
-                if (pm[tid + k] != -INFINITY) LL += pl[tid + k] * exp2f(pm[tid + k] - MM);
-            Mh[h] = MM;
-            Rh[h] = LL > 0.f ? 1.0f / LL : 0.f;
-        }
-        __syncthreads();
     }
 
-    // output rows of the heads this chunk owns
-    for (int h = chunk; h < Hq; h += C) {
-        if (tid >= HD) break;
+    // (2) score rows and positions of the first batch
+    const bool vec = (Hq & 3) == 0 && Hq <= 4 * RPL;
+    const size_t row0 = (size_t)(b * S + split) * (E * BLK);
+    float4 sv[BATCH];
+    int pv[2];          // positions of passes 2j and 2j + 1 of this lane's row group
+    auto load_batch = [&](int r0) {
+#pragma unroll
+        for (int ps = 0; ps < BATCH; ++ps) {
+            const int r = r0 + ps * ROWS + tid / RPL;
+            sv[ps] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < n_rows && vec && 4 * j < Hq)
+                sv[ps] = *reinterpret_cast<const float4 *>(ws.score + (row0 + r) * Hq + 4 * j);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ps = 2 * j + u;
+            const int r = r0 + ps * ROWS + tid / RPL;
+            pv[u] = ps < BATCH && r < n_rows ? ws.spos[row0 + r] : 0;
+        }
+    };
+    load_batch(0);
+
+    // (3) global max / sum per head (butterfly over the tpg lanes)
+    for (int w = 1; w < tpg; w <<= 1) {
+        const float Mo = __shfl_xor(M, w), Lo = __shfl_xor(L, w);
+        const float MM = fmaxf(M, Mo);
+        L = (M == -INFINITY ? 0.f : L * exp2f(M - MM)) + (Mo == -INFINITY ? 0.f : Lo * exp2f(Mo - MM));
+        M = MM;
+    }
+    if (tid % tpg == 0 && tid / tpg < Hq) {
+        Mh[tid / tpg] = M;
+        Rh[tid / tpg] = L > 0.f ? 1.0f / L : 0.f;
+    }
+    for (int h0 = FT / tpg; h0 < Hq; h0 += FT / tpg) {   // heads beyond one pass
+        const int h = h0 + tid / tpg, jj = tid % tpg;
+        float Mx = -INFINITY, Lx = 0.f;
+        if (h < Hq) {
+            const float2 *ml = reinterpret_cast<const float2 *>(ws.ml + ((size_t)b * Hq + h) * S * 2);
+            for (int s = jj; s < s_act; s += tpg) {
+                const float2 v = ml[s];
+                if (v.x == -INFINITY) continue;
+                if (v.x > Mx) {
+                    Lx = Lx * exp2f(Mx - v.x) + v.y;
+                    Mx = v.x;
+                } else {
+                    Lx += v.y * exp2f(v.x - Mx);
+                }
+            }
+        }
+        for (int w = 1; w < tpg; w <<= 1) {
+            const float Mo = __shfl_xor(Mx, w), Lo = __shfl_xor(Lx, w);
+            const float MM = fmaxf(Mx, Mo);
+            Lx = (Mx == -INFINITY ? 0.f : Lx * exp2f(Mx - MM)) + (Mo == -INFINITY ? 0.f : Lo * exp2f(Mo - MM));
+            Mx = MM;
+        }
+        if (jj == 0 && h < Hq) {
+            Mh[h] = Mx;
+            Rh[h] = Lx > 0.f ? 1.0f / Lx : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // (5) mass (and importance) of each row: partial sums over the lane's
+    //     heads, then a fixed-order butterfly
+    float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f), r4 = m4;
+    if (vec && 4 * j < Hq) {
+        m4 = *reinterpret_cast<const float4 *>(&Mh[4 * j]);
+        r4 = *reinterpret_cast<const float4 *>(&Rh[4 * j]);
+    }
+    for (int r0 = 0; r0 < n_rows; r0 += BATCH * ROWS) {
+        if (r0 > 0) load_batch(r0);
+#pragma unroll
+        for (int ps = 0; ps < BATCH; ++ps) {
+            const int r = r0 + ps * ROWS + tid / RPL;
+            const bool valid = r < n_rows;
+            float sum = 0.f;
+            if (valid) {
+                if (vec) {
+                    sum = exp2f(sv[ps].x - m4.x) * r4.x;
+                    sum += exp2f(sv[ps].y - m4.y) * r4.y;
+                    sum += exp2f(sv[ps].z - m4.z) * r4.z;
+                    sum += exp2f(sv[ps].w - m4.w) * r4.w;
+                } else {
+                    const float *sp = ws.score + (row0 + r) * Hq;
+                    for (int h = j; h < Hq; h += RPL) sum += exp2f(sp[h] - Mh[h]) * Rh[h];
+                }
+            }
+#pragma unroll
+            for (int w = 1; w < RPL; w <<= 1) sum += __shfl_xor(sum, w);
+            const int p = __shfl(pv[ps & 1], (tid & 63) - j + ps / 2);
+            if (valid && j == 0) {
+                mass[(size_t)b * c.n_cap + p] = sum;
+                if (importance) {
+                    float *ip = importance + (size_t)b * c.n_cap + p;
+                    *ip = fmaf(decay, *ip, sum);
+                }
+            }
+        }
+    }
+    // (4) output rows of the heads this workgroup owns: 32 channel quads x
+    //     8 split groups, merged in a fixed order
+    for (int h = split; h < Hq; h += X) {
+        const int c4 = tid & 31, sg = tid >> 5;
         const float *ml = ws.ml + ((size_t)b * Hq + h) * S * 2;
-        const float *o = ws.o + ((size_t)b * Hq + h) * S * HD;
-        float acc = 0.f;
-        for (int s = 0; s < s_act; ++s) {
-            const float m = ml[2 * s];
-            if (m != -INFINITY) acc = fmaf(o[(size_t)s * HD + tid], exp2f(m - Mh[h]), acc);
+        const float4 *o = reinterpret_cast<const float4 *>(ws.o + ((size_t)b * Hq + h) * S * HD);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float Mx = Mh[h];
+        for (int s0 = sg; s0 < s_act; s0 += 4 * 8) {
+            float mv[4];
+            float4 ov[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int s = s0 + 8 * u;
+                mv[u] = s < s_act ? ml[2 * s] : -INFINITY;
+                ov[u] = s < s_act ? o[(size_t)s * (HD / 4) + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (mv[u] == -INFINITY) continue;
+                const float f = exp2f(mv[u] - Mx);
+                acc.x = fmaf(ov[u].x, f, acc.x);
+                acc.y = fmaf(ov[u].y, f, acc.y);
+                acc.z = fmaf(ov[u].z, f, acc.z);
+                acc.w = fmaf(ov[u].w, f, acc.w);
+            }
         }
-        out[((size_t)b * Hq + h) * HD + tid] = acc * Rh[h];
-    }
-
-    // mass (and importance) of the valid slots of this chunk's entries
-    const size_t score_row = (size_t)c.max_blocks * BLK;
-    const float *sbase = ws.score + (size_t)b * Hq * score_row;
-#pragma unroll 1
-    for (int i = tid; i < E * BLK; i += THREADS) {
-        const int k = i / BLK, t = i % BLK;
-        const uint32_t m = s_msk[k];
-        if (!((m >> t) & 1)) continue;
-        const uint32_t ent = s_ent[k];
-        const int p = c.pos[ent >> 30][(size_t)(ent & 0x3fffffffu) * BLK + t];
-        const float *sp = sbase + (size_t)(e0 + k) * BLK + t;
-        float sum = 0.f;
-#pragma unroll 8
-        for (int h = 0; h < Hq; ++h) sum += exp2f(sp[h * score_row] - Mh[h]) * Rh[h];
-        mass[(size_t)b * c.n_cap + p] = sum;
-        if (importance) {
-            float *ip = importance + (size_t)b * c.n_cap + p;
-            *ip = fmaf(decay, *ip, sum);
+        red[tid] = acc;
+        __syncthreads();
+        if (tid < 32) {
+            float4 sum = red[tid];
+#pragma unroll
+            for (int k = 1; k < 8; ++k) {
+                const float4 r = red[k * 32 + tid];
+                sum.x += r.x; sum.y += r.y; sum.z += r.z; sum.w += r.w;
+            }
+            const float R = Rh[h];
+            reinterpret_cast<float4 *>(out + ((size_t)b * Hq + h) * HD)[tid] =
+                make_float4(sum.x * R, sum.y * R, sum.z * R, sum.w * R);
         }
+        __syncthreads();
     }
 }
 
@@ -646,8 +787,23 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
 #undef KVQ_G
         default: return false;
     }
-    hipLaunchKernelGGL(attn_finalize, dim3(S, c.B), dim3(THREADS), 0, s, c, out, mass, importance,
-                       decay, ws, S);
+    // lanes per score row: enough float4s to cover Hq heads (8 when Hq is
+    // not a multiple of four: that case reads rows head by head)
+    int rpl = 8;
+    if ((c.Hq & 3) == 0)
+        while (rpl < 64 && 4 * rpl < c.Hq) rpl *= 2;
+    switch (rpl) {
+#define KVQ_FIN(r)                                                                                 \
+    case r:                                                                                        \
+        hipLaunchKernelGGL(attn_finalize<r>, dim3(S > c.Hq ? S : c.Hq, c.B), dim3(FT), 0, s, \
+                           c, out, mass, importance, decay, ws, S);                                \
+        break;
+        KVQ_FIN(8)
+        KVQ_FIN(16)
+        KVQ_FIN(32)
+        KVQ_FIN(64)
+#undef KVQ_FIN
+    }
     return hipGetLastError() == hipSuccess;
 }
 

@@ -39,17 +39,23 @@ struct AppendWs {
 struct DecodeWs {
     float *ml;         // [B][Hq][S][2]  split max (base-2 units), split sum
     float *o;          // [B][Hq][S][128] split output, unnormalised
-    float *score;      // [B][Hq][max_blocks*16] base-2 scaled scores
+    int32_t *rows;     // [B][S] valid slots of the split's entries
+    int32_t *spos;     // [B][S][E*16] position of each score row
+    float *score;      // [B][S][E*16][Hq] base-2 scaled scores of the split's
+                       // valid slots, in table then slot order
     static size_t bytes(const kvq_cache &c) {
         const size_t S = n_splits(c);
-        return align256(8L * c.B * c.Hq * S) + align256(512L * c.B * c.Hq * S) +
-               align256(4L * c.B * c.Hq * c.max_blocks * 16);
+        return align256(8L * c.B * c.Hq * S) + align256(512L * c.B * c.Hq * S) + align256(4L * c.B * S) +
+               align256(4L * c.B * S * ENTRIES_PER_SPLIT * 16) +
+               align256(4L * c.B * S * ENTRIES_PER_SPLIT * 16 * c.Hq);
     }
     DecodeWs(void *ws, const kvq_cache &c) {
         const size_t S = n_splits(c);
         char *p = (char *)ws;
         ml = (float *)p;    p += align256(8L * c.B * c.Hq * S);
         o = (float *)p;     p += align256(512L * c.B * c.Hq * S);
+        rows = (int32_t *)p; p += align256(4L * c.B * S);
+        spos = (int32_t *)p; p += align256(4L * c.B * S * ENTRIES_PER_SPLIT * 16);
         score = (float *)p;
     }
 };

@@ -65,8 +65,15 @@ enum { KVQ_TAG_R = 0, KVQ_TAG_E = 1, KVQ_TAG_T = 2, KVQ_TAG_NONE = 255 };
  *     kv[p] + (id * Hkv + h) * kvq_region_bytes(p)
  * holds, in order:
  *     K codes  256*b bytes : token t's K row is 16*b contiguous bytes at t*16*b;
- *                            channel d sits at code index kappa_b(d) of the row
- *     V codes  256*b bytes : channel-major tiles (see DESIGN notes / the oracle)
+ *                            channel d = 32g + 8k + e sits at code index
+ *                            (b=8) 32k + 8g + e, (b=4) 32k + 8g + 4(e&1) + (e>>1),
+ *                            (b=2) 32k + 16(g>>1) + 8(e&1) + 4(g&1) + (e>>1)
+ *     V codes  256*b bytes : tiles for a 16x16x16 MFMA; for token t = 4r + u
+ *                            and channel d = 16n + j, lane L = 16r + j owns
+ *                            dword w = n*b/8 of a slice at byte
+ *                            (b=8) (w>>2)*1024 + 16L + 4(w&3), (b=4) 16L + 4w,
+ *                            (b=2) 8L + 4w; inside it the code sits at slot
+ *                            (u&1)*(16/b) + 2*(n mod 8/b) + (u>>1)
  *     K (scale, zero) 256 B: fp16 pair for token t, group g at (t*4 + g)*4
  *     V (scale, zero) 256 B: same layout
  * Codes are packed LSB first.  A dequantised value is code * scale + zero.
