@@ -105,6 +105,10 @@ __device__ inline half4 v_operand(const uint32_t *vw, int n) {
     return __builtin_bit_cast(half4, r);
 }
 
+// 2^x by the hardware instruction (results below the normal range flush to
+// zero, which no probability here needs)
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline float lo_h(uint32_t x) { return h2f((uint16_t)(x & 0xffff)); }
 __device__ inline float hi_h(uint32_t x) { return h2f((uint16_t)(x >> 16)); }
 
@@ -120,83 +124,137 @@ struct WaveState {
     float mult;      // power-of-two headroom factor applied to P'
 };
 
-// The block's slot positions, read by the first kv-head pack only.
-__device__ inline const int *pos_blk(const kvq_cache &c, int pool, uint32_t id, int pack) {
-    return pack == 0 ? c.pos[pool] + (size_t)id * BLK : nullptr;
+// ---------------------------------------------------------------------------
+// Block staging.  Each wave owns an LDS stage that holds one block-pack: the
+// (scale, zero) areas of its kv heads at a * 512, the block's 16 slot
+// positions at P * 512 (first pack of a sequence only), and the code areas
+// at code0(P) + a * CB (CB = 512 * BITS).  Loads go straight from HBM to
+// LDS, 1 KB per instruction (lane i's 16 bytes land at base + 16 i), and
+// skip the 16-byte chunks that belong only to evicted slots; those bytes
+// keep stale contents.  The (scale, zero) areas sit at the same place for
+// every bit width, so their stale bytes are always zeros or pairs of valid
+// slots: finite fp16, which a cleared slot (p = 0) turns into exact zeros.
+constexpr int STAGE_REGION = 4096 + 512;                        // 8-bit region
+__host__ __device__ constexpr int stage_bytes(int P) { return P * STAGE_REGION + 64; }
+__host__ __device__ constexpr int code0(int P) { return P * 512 + 64; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// lane i: 16 bytes from gptr (its own address) + OFF to lds_base + OFF + 16 i
+template <int OFF = 0>
+__device__ inline void lds_load16(const void *gptr, uint8_t *lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (lds_void *)lds_base, 16, OFF, 0);
+}
+// s_waitcnt encodings (gfx9): vmcnt(0), and lgkmcnt(0) alone
+__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Issue the loads of one block-pack into `stage`.  blk = the pack's first
+// region (kv head kh0) in HBM; np kv heads are real; posb = the block's
+// positions or null.
+template <int BITS, int P>
+__device__ inline void issue_block(uint8_t *stage, const uint8_t *blk, int np, uint32_t m16, const int *posb) {
+    constexpr uint32_t CB = 512u * BITS, RB = CB + 512u;
+    const int lane = threadIdx.x & 63;
+    const uint32_t live4 = ((m16 & 0x000fu) ? 1u : 0u) | ((m16 & 0x00f0u) ? 2u : 0u) |
+                           ((m16 & 0x0f00u) ? 4u : 0u) | ((m16 & 0xf000u) ? 8u : 0u);
+    // addresses: a wave-uniform base plus a 32-bit lane offset; loads that
+    // share a lane predicate are issued under one exec mask
+    const uint32_t loff = (uint32_t)lane * 16u;
+    if constexpr (BITS == 8) {
+        // K: token (1024 j + 16 lane) / 128 = 8 j + lane / 8; V: two 1 KB halves
+        if ((m16 >> (lane >> 3)) & 1u) {
+#pragma unroll
+            for (int a = 0; a < P; ++a)
+                if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+        }
+        if ((m16 >> (8 + (lane >> 3))) & 1u) {
+#pragma unroll
+            for (int a = 0; a < P; ++a)
+                if (a < np) lds_load16<1024>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+        }
+        if ((live4 >> (lane >> 4)) & 1u) {
+#pragma unroll
+            for (int a = 0; a < P; ++a)
+                if (a < np) {
+                    lds_load16<2048>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+                    lds_load16<3072>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+                }
+        }
+    } else if constexpr (BITS == 4) {
+        if ((m16 >> (lane >> 2)) & 1u) {                              // K: token lane / 4
+#pragma unroll
+            for (int a = 0; a < P; ++a)
+                if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+        }
+        if ((live4 >> (lane >> 4)) & 1u) {
+#pragma unroll
+            for (int a = 0; a < P; ++a)
+                if (a < np) lds_load16<1024>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+        }
+    } else {
+        // K in lanes 0-31 (token lane / 2), V in lanes 32-63 (group (lane-32) / 8)
+        const bool pr = lane < 32 ? ((m16 >> (lane >> 1)) & 1u) : ((live4 >> ((lane - 32) >> 3)) & 1u);
+        if (pr) {
+#pragma unroll
+            for (int a = 0; a < P; ++a)
+                if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+        }
+    }
+    // (scale, zero) areas, two kv heads per instruction: lane i < 32 takes
+    // chunk i of head 2 a2, lane i >= 32 chunk i - 32 of head 2 a2 + 1;
+    // chunk c < 16 holds token c's K pairs, c >= 16 token c - 16's V pairs
+    if ((m16 >> (lane & 15)) & 1u) {
+        const uint32_t soff = (uint32_t)(lane >> 5) * RB + CB + ((uint32_t)lane & 31u) * 16u;
+#pragma unroll
+        for (int a2 = 0; a2 < (P + 1) / 2; ++a2)
+            if (2 * a2 + (lane >> 5) < np) lds_load16(blk + (2u * a2 * RB + soff), stage + a2 * 1024);
+    }
+    if (posb != nullptr && lane < 4 && ((m16 >> (4 * lane)) & 15u))
+        lds_load16(reinterpret_cast<const uint8_t *>(posb) + loff, stage + P * 512);
 }
 
-template <int G, int BITS>
-__device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base, uint32_t id, int kh0,
-                                    int np, uint32_t m16, float *srow, int *prow, const int *pos_blk,
-                                    const uint4 (*qop)[NGRP][64], const float *qsum, float scale2,
-                                    const DecodeWs &ws, WaveState &st) {
+// The next block-pack's loads, issued by attend_block once it holds the
+// current one in registers.
+struct NoNext {
+    __device__ void operator()() const {}
+};
+
+template <int G, int BITS, class Next>
+__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, float *tile, int *ptile,
+                                    bool has_pos, const uint4 *const *qa, const float *qsum, float scale2,
+                                    WaveState &st, const Next &next) {
     constexpr int P = PACK(G);
+    constexpr uint32_t CB = 512u * BITS;
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
     const int a_rho = min(lo / G, np - 1);
     const bool row_ok = lo < np * G;
-    const long RB = 512L * BITS + 512L;
-    const uint8_t *blk = pool_base + (long)id * c.Hkv * RB;
 
-    // -- loads: K and V code slices of every kv head in the pack, and the
-    //    (scale, zero) pairs of this lane's four tokens for its own kv head
-    constexpr int KW = BITS;          // dwords per K slice: 32 codes * BITS / 32
-    constexpr int VW = BITS;          // dwords per V slice: 32 codes * BITS / 32
-    // a lane skips the bytes of evicted slots: its K row if token lo is
-    // cleared, its V slice and (scale, zero) pairs if all four tokens
-    // 4hi..4hi+3 are cleared.  Skipped code registers keep stale values:
-    // they are finite subnormals whose products are masked (K) or meet
-    // P' = 0 (V); the (scale, zero) consumers select on g_live.
-    const bool k_live = (m16 >> lo) & 1u;
-    const bool g_live = (m16 >> (4 * hi)) & 15u;
-    const uint32_t k_off = lo * 16 * BITS + hi * 4 * BITS;          // K slice of token lo
-    const uint32_t v_off = 256 * BITS + lane * (BITS == 2 ? 8 : 16); // V slice of lane
-    const uint32_t sz_off = 512 * BITS + 64 * hi;                   // tokens 4hi..4hi+3
-    uint32_t kw[P][KW], vw[P][VW];
+    // -- the block-pack from the stage: K slice of token lo (channel slice
+    //    hi), V slice of this lane, and the (scale, zero) pairs of tokens
+    //    4hi..4hi+3 of this lane's kv head; a partial pack re-reads its last
+    //    kv head, whose products meet zero q / P' operands
+    constexpr int KW = BITS, VW = BITS;
+    uint32_t vw[P][VW];
 #pragma unroll
     for (int a = 0; a < P; ++a) {
-        // a partial pack re-reads its last kv head; the zero q / P' operands
-        // of the missing heads cancel those products
-        const uint8_t *reg = blk + (uint32_t)(kh0 + min(a, np - 1)) * (uint32_t)RB;
+        const uint8_t *lr = stage + code0(P) + (uint32_t)min(a, np - 1) * CB;
         if constexpr (BITS == 8) {
-            if (k_live) {
-                const uint4 k0 = *reinterpret_cast<const uint4 *>(reg + k_off);
-                const uint4 k1 = *reinterpret_cast<const uint4 *>(reg + k_off + 16);
-                kw[a][0] = k0.x; kw[a][1] = k0.y; kw[a][2] = k0.z; kw[a][3] = k0.w;
-                kw[a][4] = k1.x; kw[a][5] = k1.y; kw[a][6] = k1.z; kw[a][7] = k1.w;
-            }
-            if (g_live) {
-                const uint4 v0 = *reinterpret_cast<const uint4 *>(reg + v_off);
-                const uint4 v1 = *reinterpret_cast<const uint4 *>(reg + v_off + 1024);
-                vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
-                vw[a][4] = v1.x; vw[a][5] = v1.y; vw[a][6] = v1.z; vw[a][7] = v1.w;
-            }
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(lr + 2048 + lane * 16);
+            const uint4 v1 = *reinterpret_cast<const uint4 *>(lr + 3072 + lane * 16);
+            vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
+            vw[a][4] = v1.x; vw[a][5] = v1.y; vw[a][6] = v1.z; vw[a][7] = v1.w;
         } else if constexpr (BITS == 4) {
-            if (k_live) {
-                const uint4 k0 = *reinterpret_cast<const uint4 *>(reg + k_off);
-                kw[a][0] = k0.x; kw[a][1] = k0.y; kw[a][2] = k0.z; kw[a][3] = k0.w;
-            }
-            if (g_live) {
-                const uint4 v0 = *reinterpret_cast<const uint4 *>(reg + v_off);
-                vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
-            }
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(lr + 1024 + lane * 16);
+            vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
         } else {
-            if (k_live) {
-                const uint2 k0 = *reinterpret_cast<const uint2 *>(reg + k_off);
-                kw[a][0] = k0.x; kw[a][1] = k0.y;
-            }
-            if (g_live) {
-                const uint2 v0 = *reinterpret_cast<const uint2 *>(reg + v_off);
-                vw[a][0] = v0.x; vw[a][1] = v0.y;
-            }
+            const uint2 v0 = *reinterpret_cast<const uint2 *>(lr + 512 + lane * 8);
+            vw[a][0] = v0.x; vw[a][1] = v0.y;
         }
     }
-    // positions of tokens 4hi..4hi+3 (one lane per token group, first pack
-    // of the sequence only): copied next to the score rows
-    int4 pos4 = make_int4(0, 0, 0, 0);
-    if (pos_blk != nullptr && lo == 0 && g_live) pos4 = reinterpret_cast<const int4 *>(pos_blk)[hi];
-    const uint8_t *own = blk + (uint32_t)(kh0 + a_rho) * (uint32_t)RB + sz_off;
     uint32_t ksz[16], vsz[16];
-    if (g_live) {
+    {
+        const uint8_t *own = stage + a_rho * 512 + 64 * hi;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint4 kq = reinterpret_cast<const uint4 *>(own)[i];
@@ -205,65 +263,76 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
             vsz[4 * i + 0] = vq.x; vsz[4 * i + 1] = vq.y; vsz[4 * i + 2] = vq.z; vsz[4 * i + 3] = vq.w;
         }
     }
+    int4 pos4 = make_int4(0, 0, 0, 0);
+    if (has_pos && lo == 0) pos4 = reinterpret_cast<const int4 *>(stage + P * 512)[hi];
 
     // -- QK^T per group: rows = tokens, columns = the pack's 16 query heads;
-    //    a kv head's codes meet only its own heads (block-diagonal q)
+    //    a kv head's codes meet only its own heads (block-diagonal q: a
+    //    column outside kv head a reads a zero operand).  Each kv head's K
+    //    slice (token lo, channel slice hi) is read just before its MFMAs.
     floatx4 acc[NGRP];
 #pragma unroll
     for (int g = 0; g < NGRP; ++g) acc[g] = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int a = 0; a < P; ++a) {
+        const uint8_t *lr = stage + code0(P) + (uint32_t)min(a, np - 1) * CB;
+        uint32_t kw[KW];
+        if constexpr (BITS == 8) {
+            const uint4 k0 = *reinterpret_cast<const uint4 *>(lr + lo * 128 + hi * 32);
+            const uint4 k1 = *reinterpret_cast<const uint4 *>(lr + lo * 128 + hi * 32 + 16);
+            kw[0] = k0.x; kw[1] = k0.y; kw[2] = k0.z; kw[3] = k0.w;
+            kw[4] = k1.x; kw[5] = k1.y; kw[6] = k1.z; kw[7] = k1.w;
+        } else if constexpr (BITS == 4) {
+            const uint4 k0 = *reinterpret_cast<const uint4 *>(lr + lo * 64 + hi * 16);
+            kw[0] = k0.x; kw[1] = k0.y; kw[2] = k0.z; kw[3] = k0.w;
+        } else {
+            const uint2 k0 = *reinterpret_cast<const uint2 *>(lr + lo * 32 + hi * 8);
+            kw[0] = k0.x; kw[1] = k0.y;
+        }
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
-            const half8 qb = __builtin_bit_cast(half8, qop[a][g][lane]);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS>(kw[a], g), qb, acc[g], 0, 0, 0);
+            const half8 qb = __builtin_bit_cast(half8, qa[a][65 * g]);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS>(kw, g), qb, acc[g], 0, 0, 0);
         }
     }
+
+    // -- the stage reads have landed: start the next block-pack.  No
+    //    LDS read follows in this block (an LDS read after the loads would
+    //    have to wait for them).
+    wait_lgkm0();
+    next();
 
     // -- scores of tokens 4hi..4hi+3 for head lo: fold the group scales and
-    //    zeros, base-2 scale, mask cleared slots
+    //    zeros, base-2 scale, mask cleared slots (a cleared slot's stage
+    //    bytes are stale: its score is replaced, never used)
     float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // group by group, so each group's scale and zero terms (which largely
-        // cancel) meet before the next group is added
-        float v = 0.f;
-#pragma unroll
-        for (int g = 0; g < NGRP; ++g) {
-            const uint32_t sz = ksz[4 * i + g];
-            v = fmaf(lo_h(sz), acc[g][i], v);
-            v = fmaf(hi_h(sz), qsum[g], v);
-        }
-        const bool valid = row_ok && ((m16 >> (4 * hi + i)) & 1u);
-        s[i] = valid ? v * scale2 : -INFINITY;
-    }
+    bool tv[4];
     {
-        // score rows: valid slots only, in slot order from srow; the Hq
-        // scores of a slot are contiguous
-        const uint32_t below = m16 & ((1u << (4 * hi)) - 1u);
-        float *sp = srow + (size_t)__popc(below) * c.Hq + (size_t)kh0 * G + lo;
+        // group by group, so each group's scale and zero terms (which largely
+        // cancel) meet before the next group is added; the four tokens'
+        // chains are independent and interleave
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (s[i] != -INFINITY) {
-                *sp = s[i];
-                sp += c.Hq;
+        for (int g = 0; g < NGRP; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t sz = ksz[4 * i + g];
+                v[i] = fmaf(lo_h(sz), acc[g][i], v[i]);
+                v[i] = fmaf(hi_h(sz), qsum[g], v[i]);
             }
-        if (pos_blk != nullptr && lo == 0) {
-            int *pp = prow + __popc(below);
-            const int pv[4] = {pos4.x, pos4.y, pos4.z, pos4.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if ((m16 >> (4 * hi + i)) & 1u) *pp++ = pv[i];
+        for (int i = 0; i < 4; ++i) {
+            tv[i] = (m16 >> (4 * hi + i)) & 1u;
+            s[i] = row_ok && tv[i] ? v[i] * scale2 : -INFINITY;
         }
     }
-
     // -- online softmax; the max only moves when some score exceeds it
     float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     if (__ballot(bm > st.m)) {
         bm = fmaxf(bm, __shfl_xor(bm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
         const float mn = fmaxf(st.m, bm);
-        const float alpha = st.m == -INFINITY ? 0.f : exp2f(st.m - mn);
+        const float alpha = st.m == -INFINITY ? 0.f : exp2_fast(st.m - mn);
         st.m = mn;
         st.l *= alpha;
 #pragma unroll
@@ -279,31 +348,34 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        p[i] = s[i] == -INFINITY ? 0.f : exp2f(s[i] - st.m);
+        p[i] = s[i] == -INFINITY ? 0.f : exp2_fast(s[i] - st.m);
         st.l += p[i];
     }
 
-    // -- headroom for P' = p * v_scale * mult in fp16
-    {
-        float vmax = 0.f;
+    // -- P' = p * v_scale * mult per group in the PV A-operand layout (lane =
+    //    head, 4 tokens), and the zero-point term.  A cleared token has p = 0
+    //    and finite stale pairs, so it contributes exact zeros.
+    float x[NGRP][4];
+    float vmax = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) vmax = fmaxf(vmax, lo_h(vsz[j]));
-        vmax = g_live ? vmax : 0.f;
-        if (__ballot(vmax * st.mult > P_HEADROOM)) {
-            for (int off = 1; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-            float nm = st.mult;
-            while (vmax * nm > P_HEADROOM) nm *= 0.5f;
-            const float f = nm / st.mult;
-            st.mult = nm;
+    for (int g = 0; g < NGRP; ++g)
 #pragma unroll
-            for (int n = 0; n < 8; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) st.o[n][i] *= f;
+        for (int i = 0; i < 4; ++i) {
+            x[g][i] = p[i] * lo_h(vsz[4 * i + g]);
+            vmax = fmaxf(vmax, x[g][i]);
         }
+    // headroom: P' must stay below the fp16 maximum
+    if (__ballot(vmax * st.mult > P_HEADROOM)) {
+        for (int off = 1; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+        float nm = st.mult;
+        while (vmax * nm > P_HEADROOM) nm *= 0.5f;
+        const float f = nm / st.mult;
+        st.mult = nm;
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.o[n][i] *= f;
     }
-
-    // -- P' per group in the PV A-operand layout (lane = head, 4 tokens), and
-    //    the zero-point term
     half4 pop[NGRP];
 #pragma unroll
     for (int g = 0; g < NGRP; ++g) {
@@ -311,12 +383,11 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
         float zg = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t sz = vsz[4 * i + g];
-            t[i] = (_Float16)(p[i] * lo_h(sz) * st.mult);
-            zg = fmaf(p[i], hi_h(sz), zg);
+            t[i] = (_Float16)(x[g][i] * st.mult);
+            zg = fmaf(p[i], hi_h(vsz[4 * i + g]), zg);
         }
-        st.z[g] += g_live ? zg : 0.f;
-        pop[g] = g_live ? t : (half4){};
+        st.z[g] += zg;
+        pop[g] = t;
     }
 
     // -- PV: block-diagonal over the pack's kv heads
@@ -329,25 +400,42 @@ __device__ inline void attend_block(const kvq_cache &c, const uint8_t *pool_base
             st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v_operand<BITS>(vw[a], n), st.o[n], 0, 0, 0);
         }
     }
+
+    // -- the block-pack's scores as one contiguous 1 KB tile [head][slot]
+    //    (lane: head lo, slots 4hi..4hi+3; cleared slots and columns past
+    //    the pack hold -inf), and, from the first pack, the slot positions
+    //    (-1 where cleared)
+    reinterpret_cast<float4 *>(tile)[lo * 4 + hi] = make_float4(s[0], s[1], s[2], s[3]);
+    if (has_pos && lo == 0)
+        reinterpret_cast<int4 *>(ptile)[hi] = make_int4(tv[0] ? pos4.x : -1, tv[1] ? pos4.y : -1,
+                                                        tv[2] ? pos4.z : -1, tv[3] ? pos4.w : -1);
 }
 
-// Workgroup LDS of the split kernel.
+// Workgroup LDS of the split kernel.  The stages and the wave-merge buffers
+// share one area (the merge runs after every wave has left its loop); the
+// prologue's scan buffer uses it too.
 template <int P>
 struct SplitLds {
     uint32_t ent[E];
     uint32_t msk[E];
-    int rb[E];         // first score row of the entry within the run
     int n;
-    uint4 q[P][NGRP][64];
-    float m[WAVES][16], l[WAVES][16], z[WAVES][16][NGRP];
-    float o[WAVES][16][HD];
+    uint4 qb[NGRP][65];      // [g][lane]: q of column head lane % 16, channel
+                             // slice lane / 16 of group g; [g][64] is zero
+    union alignas(16) {
+        uint8_t stage[WAVES][stage_bytes(P)];
+        struct {
+            float o[WAVES][16][HD];
+            float m[WAVES][16], l[WAVES][16], z[WAVES][16][NGRP];
+        } mg;
+        int scan[WAVES * 64];
+    } u;
 };
 
 // One work item (sequence, kv-head pack, run of E entries).
 template <int G>
 __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const DecodeWs &ws,
-                                        float scale2, int S, int item, const int *s_first,
-                                        SplitLds<PACK(G)> &sh) {
+                                  float scale2, int S, int item, const int *s_first,
+                                  SplitLds<PACK(G)> &sh) {
     constexpr int P = PACK(G);
     const int n_packs = (c.Hkv + P - 1) / P;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -358,8 +446,9 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         const int mid = (lo_b + hi_b + 1) >> 1;
         if (s_first[mid] <= item) lo_b = mid; else hi_b = mid - 1;
     }
-    const int b = lo_b;
-    const int r = item - s_first[b];
+    // (item values read from LDS are uniform: keep them in scalar registers)
+    const int b = __builtin_amdgcn_readfirstlane(lo_b);
+    const int r = __builtin_amdgcn_readfirstlane(item - s_first[b]);
     const int pack = r % n_packs, split = r / n_packs;
     const int kh0 = pack * P, np = min(P, c.Hkv - kh0);
     const bool row_ok = lo < np * G;
@@ -368,7 +457,7 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     const int nb = c.n_blocks[b];
     const int e0 = split * E;
     if (wave == 0) {
-        int n = 0, rows = 0;
+        int n = 0;
         for (int base = 0; base < E; base += 64) {
             const int e = e0 + base + lane;
             uint32_t ent = 0, m = 0;
@@ -378,41 +467,31 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
             }
             const uint64_t bal = __ballot(m != 0);
             const int at = n + __popcll(bal & ((1ull << lane) - 1));
-            // exclusive prefix of valid-slot counts: the entry's first row
-            int cnt = __popc(m), incl = cnt;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int v = __shfl_up(incl, d);
-                if (lane >= d) incl += v;
-            }
             if (m != 0) {
                 sh.ent[at] = ent;
                 sh.msk[at] = m;
-                sh.rb[at] = rows + incl - cnt;
             }
             n += __popcll(bal);
-            rows += __shfl(incl, 63);
         }
         if (lane == 0) {
             sh.n = n;
-            if (pack == 0) ws.rows[(size_t)b * S + split] = rows;
+            if (pack == 0) ws.ents[(size_t)b * S + split] = n;
         }
     }
 
-    // -- q operands: sh.q[a][g][lane] is q of head lo, channel slice hi of
-    //    group g if head lo belongs to kv head a of the pack, else zero
-    //    (block-diagonal columns); per-group q sums of head lo in registers
+    // -- q of the pack's heads into LDS (zero past the pack), and the
+    //    per-group q sums of head lo in registers
     float qsum[NGRP];
     {
         const int h = kh0 * G + lo;
-        const int a_lo = lo / G;
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
             uint4 raw = make_uint4(0, 0, 0, 0);
             if (row_ok) raw = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + h) * HD + 32 * g + 8 * hi);
-            if (wave == 0)
-#pragma unroll
-                for (int a = 0; a < P; ++a) sh.q[a][g][lane] = a == a_lo ? raw : make_uint4(0, 0, 0, 0);
+            if (wave == 0) {
+                sh.qb[g][lane] = raw;
+                if (lane == 0) sh.qb[g][64] = make_uint4(0, 0, 0, 0);
+            }
             const half8 qv = __builtin_bit_cast(half8, raw);
             float sum = 0.f;
 #pragma unroll
@@ -422,6 +501,10 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
             qsum[g] = sum;
         }
     }
+    // B operand rows: column lo reads its q for its own kv head, zeros else
+    const uint4 *qa[P];
+#pragma unroll
+    for (int a = 0; a < P; ++a) qa[a] = row_ok && lo / G == a ? &sh.qb[0][lane] : &sh.qb[0][64];
     __syncthreads();
 
     WaveState st;
@@ -433,23 +516,46 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
 #pragma unroll
     for (int n = 0; n < 8; ++n) st.o[n] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    const int n_ent = sh.n;
-    for (int k = wave; k < n_ent; k += WAVES) {
+    // -- this wave's entries k = wave, wave + WAVES, ...: the loads of entry
+    //    k + WAVES run while entry k is computed
+    const int n_ent = __builtin_amdgcn_readfirstlane(sh.n);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint8_t *stg = sh.u.stage[wv];
+    auto issue = [&](int k) {
         // block metadata is wave-uniform: keep it in scalar registers
         const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
         const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
-        const size_t row0 = (size_t)(b * S + split) * (E * BLK) + (size_t)__builtin_amdgcn_readfirstlane(sh.rb[k]);
-        float *srow = ws.score + row0 * c.Hq;
-        int *prow = ws.spos + row0;
         const int pool = (int)(ent >> 30);
         const uint32_t id = ent & 0x3fffffffu;
+        const int *pb = pack == 0 ? c.pos[pool] + (size_t)id * BLK : nullptr;
         if (pool == 0)
-            attend_block<G, 8>(c, c.kv[0], id, kh0, np, msk, srow, prow, pos_blk(c, 0, id, pack), sh.q, qsum, scale2, ws, st);
+            issue_block<8, P>(stg, c.kv[0] + ((size_t)id * c.Hkv + kh0) * (512u * 8 + 512u), np, msk, pb);
         else if (pool == 1)
-            attend_block<G, 4>(c, c.kv[1], id, kh0, np, msk, srow, prow, pos_blk(c, 1, id, pack), sh.q, qsum, scale2, ws, st);
+            issue_block<4, P>(stg, c.kv[1] + ((size_t)id * c.Hkv + kh0) * (512u * 4 + 512u), np, msk, pb);
         else
-            attend_block<G, 2>(c, c.kv[2], id, kh0, np, msk, srow, prow, pos_blk(c, 2, id, pack), sh.q, qsum, scale2, ws, st);
+            issue_block<2, P>(stg, c.kv[2] + ((size_t)id * c.Hkv + kh0) * (512u * 2 + 512u), np, msk, pb);
+    };
+    if (wv < n_ent) issue(wv);
+    for (int k = wv; k < n_ent; k += WAVES) {
+        wait_vm0();                     // entry k is in the stage
+        const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
+        const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
+        const size_t ek = (size_t)(b * S + split) * E + k;         // entry slot of the run
+        float *tile = ws.score + (ek * n_packs + pack) * 256;
+        int *ptile = ws.spos + ek * 16;
+        const int pool = (int)(ent >> 30);
+        const int kn = k + WAVES;
+        auto next = [&]() {
+            if (kn < n_ent) issue(kn);
+        };
+        if (pool == 0)
+            attend_block<G, 8>(stg, np, msk, tile, ptile, pack == 0, qa, qsum, scale2, st, next);
+        else if (pool == 1)
+            attend_block<G, 4>(stg, np, msk, tile, ptile, pack == 0, qa, qsum, scale2, st, next);
+        else
+            attend_block<G, 2>(stg, np, msk, tile, ptile, pack == 0, qa, qsum, scale2, st, next);
     }
+    __syncthreads();   // every wave is done with its stage: the merge reuses it
 
     // -- merge the waves of this workgroup and write the run's partial
     float lsum = st.l;
@@ -463,16 +569,16 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         zs[g] += __shfl_xor(zs[g], 32);
     }
     if (hi == 0) {
-        sh.m[wave][lo] = st.m;
-        sh.l[wave][lo] = lsum;
+        sh.u.mg.m[wave][lo] = st.m;
+        sh.u.mg.l[wave][lo] = lsum;
 #pragma unroll
-        for (int g = 0; g < NGRP; ++g) sh.z[wave][lo][g] = zs[g];
+        for (int g = 0; g < NGRP; ++g) sh.u.mg.z[wave][lo][g] = zs[g];
     }
     const float inv_mult = 1.0f / st.mult;
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sh.o[wave][4 * hi + i][16 * n + lo] = st.o[n][i] * inv_mult;
+        for (int i = 0; i < 4; ++i) sh.u.mg.o[wave][4 * hi + i][16 * n + lo] = st.o[n][i] * inv_mult;
     __syncthreads();
 
     const int rows = np * G;
@@ -480,14 +586,14 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         const int rr = idx / HD, d = idx % HD;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.m[w][rr]);
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.u.mg.m[w][rr]);
         float L = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            const float mw = sh.m[w][rr];
+            const float mw = sh.u.mg.m[w][rr];
             const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-            L = fmaf(sh.l[w][rr], f, L);
-            o = fmaf(sh.o[w][rr][d] + sh.z[w][rr][d / GS], f, o);
+            L = fmaf(sh.u.mg.l[w][rr], f, L);
+            o = fmaf(sh.u.mg.o[w][rr][d] + sh.u.mg.z[w][rr][d / GS], f, o);
         }
         const size_t hrow = (size_t)b * c.Hq + (size_t)kh0 * G + rr;
         ws.o[(hrow * S + split) * HD + d] = o;
@@ -496,34 +602,39 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
             ws.ml[(hrow * S + split) * 2 + 1] = L;
         }
     }
-    __syncthreads();   // LDS is reused by the next item
+    __syncthreads();   // the merge area has been read
+    // zero it: a later stage may keep any of its bytes as stale (scale,
+    // zero) pairs, which must be finite fp16 (the merge floats need not be)
+    for (int i = tid; i < (int)(sizeof(sh.u.mg) / 16); i += WAVES * 64)
+        reinterpret_cast<uint4 *>(&sh.u.mg)[i] = make_uint4(0, 0, 0, 0);
 }
 
 // Work items are (sequence, kv-head pack, run of E table entries), ordered
 // by sequence, pack, run, for the runs that hold entries.  The kernel is
 // persistent: gridDim.x workgroups (what fits on the GPU at once) take the
 // items round-robin, so the dispatcher never has to refill slots and no
-// workgroup is launched for a run past a sequence's end.
+// workgroup is launched for a run past a sequence's end.  The item prefix
+// (B + 1 ints) lives in dynamic LDS.
 template <int G>
 __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
                                                          DecodeWs ws, float scale2, int S) {
     constexpr int P = PACK(G);
     const int n_packs = (c.Hkv + P - 1) / P;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lo = lane & 15, hi = lane >> 4;
+    const int tid = threadIdx.x;
     constexpr int NT = WAVES * 64;
+    extern __shared__ int s_first[];
+    __shared__ SplitLds<P> lds;
+    __shared__ int s_carry;
 
     // -- item prefix: s_first[b] = first item of sequence b (items per
     //    sequence = active runs * packs)
-    __shared__ int s_first[MAX_B + 1];
-    __shared__ int s_carry;
     if (tid == 0) s_carry = 0;
     __syncthreads();
+    int *s_scan = lds.u.scan;
     for (int b0 = 0; b0 < c.B; b0 += NT) {
         const int bb = b0 + tid;
         const int cnt = bb < c.B ? ((c.n_blocks[bb] + E - 1) / E) * n_packs : 0;
         // inclusive scan of cnt over the workgroup (Hillis-Steele in LDS)
-        __shared__ int s_scan[NT];
         s_scan[tid] = cnt;
         __syncthreads();
         for (int off = 1; off < NT; off <<= 1) {
@@ -541,49 +652,51 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     __syncthreads();
     const int n_items = s_first[c.B];
 
+    // -- stage bytes start finite: zero the shared area once (the scan used it)
+    for (int i = tid; i < (int)(sizeof(lds.u) / 16); i += NT)
+        reinterpret_cast<uint4 *>(&lds.u)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
     // -- every position below seq_len starts at mass 0; the finalize pass
     //    writes the valid ones.  Grid-stride over (sequence, position).
     for (int bb = 0; bb < c.B; ++bb) {
-        const int len = c.seq_len[bb];
+        const int len = min(c.seq_len[bb], c.n_cap);
         for (int p = blockIdx.x * NT + tid; p < len; p += gridDim.x * NT) mass[(size_t)bb * c.n_cap + p] = 0.f;
     }
 
-    __shared__ SplitLds<P> lds;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x)
         split_item<G>(c, q, ws, scale2, S, item, s_first, lds);
 }
 
-// Finalize: one workgroup per (run of E entries, sequence).  The run's
-// valid slots are rows of Hq scores with their positions; RPL lanes share a
-// row, each reading four heads.  Two dependent rounds of loads: the row
-// count and split partials, then the rows.
+// Finalize: one workgroup per (run of E entries, sequence); workgroup x
+// also writes the output rows of heads x, x + gridDim.x, ...  Each wave
+// takes whole entries: an entry's score tiles (one per kv-head pack,
+// [head][slot]) are read with 1 KB loads, each lane summing
+// exp2(s - M_h) / L_h over its head of every pack for 4 slots, and a fixed
+// 16-lane butterfly totals the heads of each slot.
 constexpr int FT = 256;
+constexpr int FB = 4;                         // entries a wave takes per round
 
-template <int RPL>
-__global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass,
-                                                    float *importance, float decay, DecodeWs ws, int S) {
-    constexpr int ROWS = FT / RPL;             // rows one pass of the workgroup covers
-    constexpr int BATCH = 16;                  // passes whose loads are issued together
-    static_assert(2 * RPL >= BATCH, "row positions: two passes per lane");
+__global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
+                                                    float decay, DecodeWs ws, int S, int G, int P, int n_packs) {
     const int split = blockIdx.x, b = blockIdx.y, X = gridDim.x;
-    const int tid = threadIdx.x, j = tid % RPL;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lo = lane & 15, hi = lane >> 4;
     const int nb = c.n_blocks[b];
     const int s_act = (nb + E - 1) / E;
     const int Hq = c.Hq;
-    if (split >= s_act && split >= Hq) return;   // no rows and no output head
+    if (split >= s_act && split >= Hq) return;   // no entries and no output head
     __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
     __shared__ float4 red[FT];
+    const int n_ent = split < s_act ? ws.ents[(size_t)b * S + split] : 0;
 
-    // (1) row count, split (m, l) pairs of every head, and the partial
-    //     outputs of the head this workgroup writes
-    const int n_rows = split < s_act ? ws.rows[(size_t)b * S + split] : 0;
+    // -- global max / sum per head: tpg lanes of one wave per head, each over
+    //    a stride of splits with its loads issued together, then a butterfly
     int tpg = 64;
     while (tpg > 1 && tpg * Hq > FT) tpg >>= 1;
-    float M = -INFINITY, L = 0.f;
-    {
-        // one pass of tpg lanes per head covers Hq <= FT / tpg heads; more
-        // heads take more passes below
-        const int h = tid / tpg, jj = tid % tpg;
+    for (int h0 = 0; h0 < Hq; h0 += FT / tpg) {
+        const int h = h0 + tid / tpg, jj = tid % tpg;
+        float M = -INFINITY, L = 0.f;
         if (h < Hq) {
             const float2 *ml = reinterpret_cast<const float2 *>(ws.ml + ((size_t)b * Hq + h) * S * 2);
             for (int s0 = jj; s0 < s_act; s0 += 8 * tpg) {
@@ -605,109 +718,86 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
                 }
             }
         }
-    }
-
-    // (2) score rows and positions of the first batch
-    const bool vec = (Hq & 3) == 0 && Hq <= 4 * RPL;
-    const size_t row0 = (size_t)(b * S + split) * (E * BLK);
-    float4 sv[BATCH];
-    int pv[2];          // positions of passes 2j and 2j + 1 of this lane's row group
-    auto load_batch = [&](int r0) {
-#pragma unroll
-        for (int ps = 0; ps < BATCH; ++ps) {
-            const int r = r0 + ps * ROWS + tid / RPL;
-            sv[ps] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r < n_rows && vec && 4 * j < Hq)
-                sv[ps] = *reinterpret_cast<const float4 *>(ws.score + (row0 + r) * Hq + 4 * j);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ps = 2 * j + u;
-            const int r = r0 + ps * ROWS + tid / RPL;
-            pv[u] = ps < BATCH && r < n_rows ? ws.spos[row0 + r] : 0;
-        }
-    };
-    load_batch(0);
-
-    // (3) global max / sum per head (butterfly over the tpg lanes)
-    for (int w = 1; w < tpg; w <<= 1) {
-        const float Mo = __shfl_xor(M, w), Lo = __shfl_xor(L, w);
-        const float MM = fmaxf(M, Mo);
-        L = (M == -INFINITY ? 0.f : L * exp2f(M - MM)) + (Mo == -INFINITY ? 0.f : Lo * exp2f(Mo - MM));
-        M = MM;
-    }
-    if (tid % tpg == 0 && tid / tpg < Hq) {
-        Mh[tid / tpg] = M;
-        Rh[tid / tpg] = L > 0.f ? 1.0f / L : 0.f;
-    }
-    for (int h0 = FT / tpg; h0 < Hq; h0 += FT / tpg) {   // heads beyond one pass
-        const int h = h0 + tid / tpg, jj = tid % tpg;
-        float Mx = -INFINITY, Lx = 0.f;
-        if (h < Hq) {
-            const float2 *ml = reinterpret_cast<const float2 *>(ws.ml + ((size_t)b * Hq + h) * S * 2);
-            for (int s = jj; s < s_act; s += tpg) {
-                const float2 v = ml[s];
-                if (v.x == -INFINITY) continue;
-                if (v.x > Mx) {
-                    Lx = Lx * exp2f(Mx - v.x) + v.y;
-                    Mx = v.x;
-                } else {
-                    Lx += v.y * exp2f(v.x - Mx);
-                }
-            }
-        }
         for (int w = 1; w < tpg; w <<= 1) {
-            const float Mo = __shfl_xor(Mx, w), Lo = __shfl_xor(Lx, w);
-            const float MM = fmaxf(Mx, Mo);
-            Lx = (Mx == -INFINITY ? 0.f : Lx * exp2f(Mx - MM)) + (Mo == -INFINITY ? 0.f : Lo * exp2f(Mo - MM));
-            Mx = MM;
+            const float Mo = __shfl_xor(M, w), Lo = __shfl_xor(L, w);
+            const float MM = fmaxf(M, Mo);
+            L = (M == -INFINITY ? 0.f : L * exp2f(M - MM)) + (Mo == -INFINITY ? 0.f : Lo * exp2f(Mo - MM));
+            M = MM;
         }
         if (jj == 0 && h < Hq) {
-            Mh[h] = Mx;
-            Rh[h] = Lx > 0.f ? 1.0f / Lx : 0.f;
+            Mh[h] = M;
+            Rh[h] = L > 0.f ? 1.0f / L : 0.f;
         }
     }
     __syncthreads();
 
-    // (5) mass (and importance) of each row: partial sums over the lane's
-    //     heads, then a fixed-order butterfly
-    float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f), r4 = m4;
-    if (vec && 4 * j < Hq) {
-        m4 = *reinterpret_cast<const float4 *>(&Mh[4 * j]);
-        r4 = *reinterpret_cast<const float4 *>(&Rh[4 * j]);
-    }
-    for (int r0 = 0; r0 < n_rows; r0 += BATCH * ROWS) {
-        if (r0 > 0) load_batch(r0);
+    // -- mass (and importance) of the valid slots of this run's entries
+    const size_t ek0 = (size_t)(b * S + split) * E;
+    for (int k0 = wave * FB; k0 < n_ent; k0 += (FT / 64) * FB) {
+        int4 pos[FB];
+        float acc[FB][4];
 #pragma unroll
-        for (int ps = 0; ps < BATCH; ++ps) {
-            const int r = r0 + ps * ROWS + tid / RPL;
-            const bool valid = r < n_rows;
-            float sum = 0.f;
-            if (valid) {
-                if (vec) {
-                    sum = exp2f(sv[ps].x - m4.x) * r4.x;
-                    sum += exp2f(sv[ps].y - m4.y) * r4.y;
-                    sum += exp2f(sv[ps].z - m4.z) * r4.z;
-                    sum += exp2f(sv[ps].w - m4.w) * r4.w;
-                } else {
-                    const float *sp = ws.score + (row0 + r) * Hq;
-                    for (int h = j; h < Hq; h += RPL) sum += exp2f(sp[h] - Mh[h]) * Rh[h];
+        for (int e = 0; e < FB; ++e) {
+            const int k = k0 + e;
+            pos[e] = k < n_ent ? reinterpret_cast<const int4 *>(ws.spos + (ek0 + k) * 16)[hi]
+                               : make_int4(-1, -1, -1, -1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
+        }
+        for (int p0 = 0; p0 < n_packs; p0 += 2) {
+            // two packs' tiles of the round's entries, loads issued together
+            float4 t[FB][2];
+#pragma unroll
+            for (int e = 0; e < FB; ++e)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int k = k0 + e, p = p0 + q;
+                    t[e][q] = k < n_ent && p < n_packs
+                                  ? reinterpret_cast<const float4 *>(ws.score + ((ek0 + k) * n_packs + p) * 256)[lo * 4 + hi]
+                                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int p = p0 + q;
+                const int col = p * P * G + lo;
+                const bool cv = p < n_packs && lo < min(P, c.Hkv - p * P) * G && Mh[min(col, Hq - 1)] != -INFINITY;
+                if (!cv) continue;
+                const float Mx = Mh[col], Rx = Rh[col];
+#pragma unroll
+                for (int e = 0; e < FB; ++e) {
+                    acc[e][0] = fmaf(exp2f(t[e][q].x - Mx), Rx, acc[e][0]);
+                    acc[e][1] = fmaf(exp2f(t[e][q].y - Mx), Rx, acc[e][1]);
+                    acc[e][2] = fmaf(exp2f(t[e][q].z - Mx), Rx, acc[e][2]);
+                    acc[e][3] = fmaf(exp2f(t[e][q].w - Mx), Rx, acc[e][3]);
                 }
             }
+        }
 #pragma unroll
-            for (int w = 1; w < RPL; w <<= 1) sum += __shfl_xor(sum, w);
-            const int p = __shfl(pv[ps & 1], (tid & 63) - j + ps / 2);
-            if (valid && j == 0) {
-                mass[(size_t)b * c.n_cap + p] = sum;
-                if (importance) {
-                    float *ip = importance + (size_t)b * c.n_cap + p;
-                    *ip = fmaf(decay, *ip, sum);
+        for (int e = 0; e < FB; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int w = 1; w < 16; w <<= 1) acc[e][i] += __shfl_xor(acc[e][i], w);
+        if (lo == 0) {
+#pragma unroll
+            for (int e = 0; e < FB; ++e) {
+                const int pp[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // a position outside the row stride (a corrupt cache) is skipped
+                    if (pp[i] < 0 || pp[i] >= c.n_cap) continue;
+                    mass[(size_t)b * c.n_cap + pp[i]] = acc[e][i];
+                    if (importance) {
+                        float *ip = importance + (size_t)b * c.n_cap + pp[i];
+                        *ip = fmaf(decay, *ip, acc[e][i]);
+                    }
                 }
             }
         }
     }
-    // (4) output rows of the heads this workgroup owns: 32 channel quads x
-    //     8 split groups, merged in a fixed order
+
+    // -- output rows of the heads this workgroup owns: 32 channel quads x
+    //    8 split groups, merged in a fixed order
     for (int h = split; h < Hq; h += X) {
         const int c4 = tid & 31, sg = tid >> 5;
         const float *ml = ws.ml + ((size_t)b * Hq + h) * S * 2;
@@ -752,17 +842,21 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
 
 }  // namespace
 
-// Workgroups of attn_split<G> that fit on the device at once (cached).
-int persistent_grid(int G, const void *kernel) {
+// Workgroups of attn_split<G> that fit on the device at once, for a given
+// dynamic LDS size (cached per device and G).
+int persistent_grid(int G, const void *kernel, size_t dyn_lds) {
     static int cache[64][KVQ_MAX_GQA + 1];
+    static size_t cache_lds[64][KVQ_MAX_GQA + 1];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     int &v = cache[dev][G];
-    if (v == 0) {
+    if (v == 0 || cache_lds[dev][G] != dyn_lds) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WAVES * 64, 0) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WAVES * 64, dyn_lds) != hipSuccess)
+            return 0;
         v = cus * (per_cu > 0 ? per_cu : 1);
+        cache_lds[dev][G] = dyn_lds;
     }
     return v;
 }
@@ -774,12 +868,13 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
     const int G = c.Hq / c.Hkv;
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     const float scale2 = sm_scale * LOG2E;
+    const size_t dyn = sizeof(int) * ((size_t)c.B + 1);   // item prefix of the split kernel
     switch (G) {
 #define KVQ_G(g)                                                                                   \
     case g: {                                                                                      \
-        const int grid = persistent_grid(g, reinterpret_cast<const void *>(attn_split<g>));         \
+        const int grid = persistent_grid(g, reinterpret_cast<const void *>(attn_split<g>), dyn);    \
         if (grid <= 0) return false;                                                               \
-        hipLaunchKernelGGL(attn_split<g>, dim3(grid), dim3(WAVES * 64), 0, s, c, qq, mass, ws, scale2, S); \
+        hipLaunchKernelGGL(attn_split<g>, dim3(grid), dim3(WAVES * 64), dyn, s, c, qq, mass, ws, scale2, S); \
         break;                                                                                     \
     }
         KVQ_G(1) KVQ_G(2) KVQ_G(3) KVQ_G(4) KVQ_G(5) KVQ_G(6) KVQ_G(7) KVQ_G(8)
@@ -787,22 +882,10 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
 #undef KVQ_G
         default: return false;
     }
-    // lanes per score row: enough float4s to cover Hq heads (8 when Hq is
-    // not a multiple of four: that case reads rows head by head)
-    int rpl = 8;
-    if ((c.Hq & 3) == 0)
-        while (rpl < 64 && 4 * rpl < c.Hq) rpl *= 2;
-    switch (rpl) {
-#define KVQ_FIN(r)                                                                                 \
-    case r:                                                                                        \
-        hipLaunchKernelGGL(attn_finalize<r>, dim3(S > c.Hq ? S : c.Hq, c.B), dim3(FT), 0, s, \
-                           c, out, mass, importance, decay, ws, S);                                \
-        break;
-        KVQ_FIN(8)
-        KVQ_FIN(16)
-        KVQ_FIN(32)
-        KVQ_FIN(64)
-#undef KVQ_FIN
+    {
+        const int P = decode_pack(G);
+        hipLaunchKernelGGL(attn_finalize, dim3(S > c.Hq ? S : c.Hq, c.B), dim3(FT), 0, s, c, out, mass, importance,
+                           decay, ws, S, G, P, decode_n_packs(c));
     }
     return hipGetLastError() == hipSuccess;
 }

@@ -36,26 +36,31 @@ struct AppendWs {
     }
 };
 
+// kv heads whose query heads share one 16-column MFMA tile in decode
+inline int decode_pack(int G) { return 16 / G < 4 ? 16 / G : 4; }
+inline int decode_n_packs(const kvq_cache &c) {
+    const int P = decode_pack(c.Hq / c.Hkv);
+    return (c.Hkv + P - 1) / P;
+}
+
 struct DecodeWs {
     float *ml;         // [B][Hq][S][2]  split max (base-2 units), split sum
     float *o;          // [B][Hq][S][128] split output, unnormalised
-    int32_t *rows;     // [B][S] valid slots of the split's entries
-    int32_t *spos;     // [B][S][E*16] position of each score row
-    float *score;      // [B][S][E*16][Hq] base-2 scaled scores of the split's
-                       // valid slots, in table then slot order
+    int32_t *ents;     // [B][S] non-empty table entries of the split
+    int32_t *spos;     // [B][S][E][16] slot positions of those entries, -1 if cleared
+    float *score;      // [B][S][E][n_packs][16 heads][16 slots] base-2 scaled scores
     static size_t bytes(const kvq_cache &c) {
-        const size_t S = n_splits(c);
+        const size_t S = n_splits(c), E = ENTRIES_PER_SPLIT;
         return align256(8L * c.B * c.Hq * S) + align256(512L * c.B * c.Hq * S) + align256(4L * c.B * S) +
-               align256(4L * c.B * S * ENTRIES_PER_SPLIT * 16) +
-               align256(4L * c.B * S * ENTRIES_PER_SPLIT * 16 * c.Hq);
+               align256(64L * c.B * S * E) + align256(1024L * c.B * S * E * decode_n_packs(c));
     }
     DecodeWs(void *ws, const kvq_cache &c) {
-        const size_t S = n_splits(c);
+        const size_t S = n_splits(c), E = ENTRIES_PER_SPLIT;
         char *p = (char *)ws;
         ml = (float *)p;    p += align256(8L * c.B * c.Hq * S);
         o = (float *)p;     p += align256(512L * c.B * c.Hq * S);
-        rows = (int32_t *)p; p += align256(4L * c.B * S);
-        spos = (int32_t *)p; p += align256(4L * c.B * S * ENTRIES_PER_SPLIT * 16);
+        ents = (int32_t *)p; p += align256(4L * c.B * S);
+        spos = (int32_t *)p; p += align256(64L * c.B * S * E);
         score = (float *)p;
     }
 };
