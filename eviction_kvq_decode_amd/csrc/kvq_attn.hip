@@ -31,6 +31,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 #ifndef KVQ_WAVES
@@ -87,12 +88,17 @@ __device__ inline half8 k_operand(const uint32_t *kw, int g) {
 }
 
 // PV B operand: codes of tokens 4r..4r+3 at this lane's channel of tile n.
+// 8-bit codes keep the 1024 bias (1024 + c): the bias's contribution,
+// 1024 * sum P', is taken out through the zero-point sum instead (8-bit
+// codes are large enough next to 1024 for the fp32 accumulation to keep
+// them; 4- and 2-bit codes are not, and are unbiased exactly).
 template <int BITS>
 __device__ inline half4 v_operand(const uint32_t *vw, int n) {
     uint32_t r[2];
     if constexpr (BITS == 8) {
-        r[0] = byte_pair(vw[n], 0, 2);
-        r[1] = byte_pair(vw[n], 1, 3);
+        const uint32_t w = vw[n];
+        r[0] = __builtin_amdgcn_perm(w, 0x64646464u, 4u | (6u << 16));
+        r[1] = __builtin_amdgcn_perm(w, 0x64646464u, 5u | (7u << 16));
     } else if constexpr (BITS == 4) {
         const int m = n & 1;
         r[0] = field_pair(vw[n >> 1], 8 * m, 0x000F000Fu);
@@ -352,42 +358,53 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
         st.l += p[i];
     }
 
-    // -- P' = p * v_scale * mult per group in the PV A-operand layout (lane =
-    //    head, 4 tokens), and the zero-point term.  A cleared token has p = 0
-    //    and finite stale pairs, so it contributes exact zeros.
-    float x[NGRP][4];
-    float vmax = 0.f;
+    // -- headroom: P' = p * v_scale * mult must stay inside fp16, and p <= 1,
+    //    so the largest v_scale in the stage bounds it.  Scales are
+    //    non-negative fp16, whose bit patterns order like their values: a
+    //    packed unsigned max over the (scale, zero) words finds it in the low
+    //    halves.  (Stale pairs of cleared tokens only make the bound safer.)
+    {
+        ushort2v vm = __builtin_bit_cast(ushort2v, vsz[0]);
+#pragma unroll
+        for (int j = 1; j < 16; ++j) vm = __builtin_elementwise_max(vm, __builtin_bit_cast(ushort2v, vsz[j]));
+        float vmax = h2f(vm[0]);
+        if (__ballot(vmax * st.mult > P_HEADROOM)) {
+            for (int off = 1; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+            float nm = st.mult;
+            while (vmax * nm > P_HEADROOM) nm *= 0.5f;
+            const float f = nm / st.mult;
+            st.mult = nm;
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st.o[n][i] *= f;
+        }
+    }
+    // -- P' per group in the PV A-operand layout (lane = head, 4 tokens), one
+    //    rounding to fp16.  A cleared token has p = 0 and finite stale pairs,
+    //    so it contributes exact zeros.
+    float pm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pm[i] = p[i] * st.mult;
+    half4 pop[NGRP];
 #pragma unroll
     for (int g = 0; g < NGRP; ++g)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[g][i] = p[i] * lo_h(vsz[4 * i + g]);
-            vmax = fmaxf(vmax, x[g][i]);
+        for (int i = 0; i < 4; ++i) pop[g][i] = (_Float16)(pm[i] * lo_h(vsz[4 * i + g]));
+    // zero-point term sum p * v_zero, less the 8-bit V operands' bias share
+    // 1024 * P' / mult
+    {
+        const float kb = BITS == 8 ? -1024.0f / st.mult : 0.f;
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) {
+            float zg = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                zg = fmaf(p[i], hi_h(vsz[4 * i + g]), zg);
+                if constexpr (BITS == 8) zg = fmaf(kb, (float)pop[g][i], zg);
+            }
+            st.z[g] += zg;
         }
-    // headroom: P' must stay below the fp16 maximum
-    if (__ballot(vmax * st.mult > P_HEADROOM)) {
-        for (int off = 1; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-        float nm = st.mult;
-        while (vmax * nm > P_HEADROOM) nm *= 0.5f;
-        const float f = nm / st.mult;
-        st.mult = nm;
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st.o[n][i] *= f;
-    }
-    half4 pop[NGRP];
-#pragma unroll
-    for (int g = 0; g < NGRP; ++g) {
-        half4 t;
-        float zg = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            t[i] = (_Float16)(x[g][i] * st.mult);
-            zg = fmaf(p[i], hi_h(vsz[4 * i + g]), zg);
-        }
-        st.z[g] += zg;
-        pop[g] = t;
     }
 
     // -- PV: block-diagonal over the pack's kv heads
