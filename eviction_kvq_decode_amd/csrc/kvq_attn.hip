@@ -62,15 +62,23 @@ __device__ inline uint32_t byte_pair(uint32_t w, int i, int j) {
     const uint32_t sel = (uint32_t)(4 + i) | ((uint32_t)(4 + j) << 16);  // selector 0: a 0x64 byte
     return unbias(__builtin_amdgcn_perm(w, 0x64646464u, sel));
 }
-// Fields at bit offsets sh and sh+16 of w (mask m per field) as an exact fp16 pair.
-__device__ inline uint32_t field_pair(uint32_t w, int sh, uint32_t m) {
-    return unbias(((w >> sh) & m) | BIAS2);
+// Fields at bit offsets sh and sh+16 of w (mask m per field) as an exact fp16
+// pair.  vb holds BIAS2 in a vector register the compiler cannot see through,
+// so mask-and-bias is one v_and_or_b32 (a VOP3 instruction takes neither a
+// literal nor two scalar operands here).
+__device__ inline uint32_t field_pair(uint32_t w, int sh, uint32_t m, uint32_t vb) {
+    return unbias(((w >> sh) & m) | vb);
+}
+__device__ inline uint32_t opaque_bias() {
+    uint32_t vb = BIAS2;
+    asm volatile("" : "+v"(vb));
+    return vb;
 }
 
 // QK A operand: the eight codes of group g held by this lane's K slice,
 // in channel order e0..e7 (see the K row layout).
 template <int BITS>
-__device__ inline half8 k_operand(const uint32_t *kw, int g) {
+__device__ inline half8 k_operand(const uint32_t *kw, int g, uint32_t vb) {
     uint32_t r[4];
     if constexpr (BITS == 8) {
         r[0] = byte_pair(kw[2 * g], 0, 1);
@@ -79,10 +87,10 @@ __device__ inline half8 k_operand(const uint32_t *kw, int g) {
         r[3] = byte_pair(kw[2 * g + 1], 2, 3);
     } else if constexpr (BITS == 4) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) r[k] = field_pair(kw[g], 4 * k, 0x000F000Fu);
+        for (int k = 0; k < 4; ++k) r[k] = field_pair(kw[g], 4 * k, 0x000F000Fu, vb);
     } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) r[k] = field_pair(kw[g >> 1], 2 * (4 * (g & 1) + k), 0x00030003u);
+        for (int k = 0; k < 4; ++k) r[k] = field_pair(kw[g >> 1], 2 * (4 * (g & 1) + k), 0x00030003u, vb);
     }
     return __builtin_bit_cast(half8, r);
 }
@@ -93,7 +101,7 @@ __device__ inline half8 k_operand(const uint32_t *kw, int g) {
 // codes are large enough next to 1024 for the fp32 accumulation to keep
 // them; 4- and 2-bit codes are not, and are unbiased exactly).
 template <int BITS>
-__device__ inline half4 v_operand(const uint32_t *vw, int n) {
+__device__ inline half4 v_operand(const uint32_t *vw, int n, uint32_t vb) {
     uint32_t r[2];
     if constexpr (BITS == 8) {
         const uint32_t w = vw[n];
@@ -101,12 +109,12 @@ __device__ inline half4 v_operand(const uint32_t *vw, int n) {
         r[1] = __builtin_amdgcn_perm(w, 0x64646464u, 5u | (7u << 16));
     } else if constexpr (BITS == 4) {
         const int m = n & 1;
-        r[0] = field_pair(vw[n >> 1], 8 * m, 0x000F000Fu);
-        r[1] = field_pair(vw[n >> 1], 8 * m + 4, 0x000F000Fu);
+        r[0] = field_pair(vw[n >> 1], 8 * m, 0x000F000Fu, vb);
+        r[1] = field_pair(vw[n >> 1], 8 * m + 4, 0x000F000Fu, vb);
     } else {
         const int m = n & 3;
-        r[0] = field_pair(vw[n >> 2], 4 * m, 0x00030003u);
-        r[1] = field_pair(vw[n >> 2], 4 * m + 2, 0x00030003u);
+        r[0] = field_pair(vw[n >> 2], 4 * m, 0x00030003u, vb);
+        r[1] = field_pair(vw[n >> 2], 4 * m + 2, 0x00030003u, vb);
     }
     return __builtin_bit_cast(half4, r);
 }
@@ -235,6 +243,7 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
     const int a_rho = min(lo / G, np - 1);
     const bool row_ok = lo < np * G;
+    const uint32_t vb = opaque_bias();
 
     // -- the block-pack from the stage: K slice of token lo (channel slice
     //    hi), V slice of this lane, and the (scale, zero) pairs of tokens
@@ -298,7 +307,7 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
             const half8 qb = __builtin_bit_cast(half8, qa[a][65 * g]);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS>(kw, g), qb, acc[g], 0, 0, 0);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS>(kw, g, vb), qb, acc[g], 0, 0, 0);
         }
     }
 
@@ -414,7 +423,7 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
             const half4 pa = mine ? pop[n >> 1] : (half4){};
-            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v_operand<BITS>(vw[a], n), st.o[n], 0, 0, 0);
+            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v_operand<BITS>(vw[a], n, vb), st.o[n], 0, 0, 0);
         }
     }
 
