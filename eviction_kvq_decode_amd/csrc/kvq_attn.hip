@@ -154,13 +154,23 @@ __host__ __device__ constexpr int code0(int P) { return P * 512 + 64; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// lane i: 16 bytes from gptr (its own address) + OFF to lds_base + OFF + 16 i
+// lane i: 16 bytes from gptr (its own address) + OFF to lds_base + OFF + 16 i.
+// Written as an instruction the compiler does not track: its waits would
+// otherwise drain every store behind these loads before any later LDS read
+// (it cannot tell the stage from other LDS data).  The kernel waits for the
+// loads itself.  The instruction has no register result; m0 carries the LDS
+// base and needs one wait state before the load.
 template <int OFF = 0>
 __device__ inline void lds_load16(const void *gptr, uint8_t *lds_base) {
-    __builtin_amdgcn_global_load_lds(gptr, (lds_void *)lds_base, 16, OFF, 0);
+    const uint32_t lds = (uint32_t)(size_t)(lds_void *)lds_base + OFF;
+    const uint8_t *g = static_cast<const uint8_t *>(gptr) + OFF;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds)
+                 : "memory", "m0");
 }
-// s_waitcnt encodings (gfx9): vmcnt(0), and lgkmcnt(0) alone
+// s_waitcnt encodings (gfx9): vmcnt(0..2), and lgkmcnt(0) alone
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ inline void wait_vm1() { __builtin_amdgcn_s_waitcnt(0x0F71); }
+__device__ inline void wait_vm2() { __builtin_amdgcn_s_waitcnt(0x0F72); }
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Issue the loads of one block-pack into `stage`.  blk = the pack's first
@@ -563,7 +573,13 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     };
     if (wv < n_ent) issue(wv);
     for (int k = wv; k < n_ent; k += WAVES) {
-        wait_vm0();                     // entry k is in the stage
+        // entry k is in the stage once its loads are done.  The vector memory
+        // counter also counts stores, and returns in issue order: after the
+        // first entry, the previous entry's score tile (and position) stores
+        // were issued after these loads and may stay in flight.
+        if (k == wv) wait_vm0();
+        else if (pack == 0) wait_vm2();
+        else wait_vm1();
         const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
         const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
         const size_t ek = (size_t)(b * S + split) * E + k;         // entry slot of the run
