@@ -16,6 +16,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -66,6 +67,22 @@ def build_gpu_cache(w, toks, g):
     return cache
 
 
+def committed_traffic(workload: str):
+    """HBM bytes per decode call from the committed FETCH_SIZE / WRITE_SIZE
+    measurement (profiles/decode_long_evicted_traffic.json), or None when it
+    does not cover this workload or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "decode_long_evicted_traffic.json")
+    if workload != "long_evicted" or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    h = hashlib.sha256()
+    for src in d["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return d["hbm_bytes_per_call"] if h.hexdigest() == d["sources_sha256"] else None
+
+
 def cpu_baseline(w, toks, n_seq: int, seconds: float):
     """Time the CPU oracle on the first n_seq sequences of the workload."""
     from eviction_kvq_decode_amd import workloads as wl
@@ -104,7 +121,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_evicted")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run 3 device-to-device copies of this many MiB before the steps "
@@ -202,7 +219,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, "
                                f"{int(n.max())} logical positions/seq, "
@@ -211,7 +228,7 @@ def main():
                    "global_batch": B, "seq_len": int(n.max()),
                    "compressed_kv_mb_per_step": round(dec_bytes[-1] / 1e6, 1)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": committed_traffic(args.workload),
                      "kernel": "kvq_decode_attention (split + finalize)",
                      "avg_us": float(np.mean(dec_ms) * 1e3)},
         "cpu_baseline": None,

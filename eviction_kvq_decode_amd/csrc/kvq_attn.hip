@@ -807,10 +807,10 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
                 const float Mx = Mh[col], Rx = Rh[col];
 #pragma unroll
                 for (int e = 0; e < FB; ++e) {
-                    acc[e][0] = fmaf(exp2f(t[e][q].x - Mx), Rx, acc[e][0]);
-                    acc[e][1] = fmaf(exp2f(t[e][q].y - Mx), Rx, acc[e][1]);
-                    acc[e][2] = fmaf(exp2f(t[e][q].z - Mx), Rx, acc[e][2]);
-                    acc[e][3] = fmaf(exp2f(t[e][q].w - Mx), Rx, acc[e][3]);
+                    acc[e][0] = fmaf(exp2_fast(t[e][q].x - Mx), Rx, acc[e][0]);
+                    acc[e][1] = fmaf(exp2_fast(t[e][q].y - Mx), Rx, acc[e][1]);
+                    acc[e][2] = fmaf(exp2_fast(t[e][q].z - Mx), Rx, acc[e][2]);
+                    acc[e][3] = fmaf(exp2_fast(t[e][q].w - Mx), Rx, acc[e][3]);
                 }
             }
         }
