@@ -457,14 +457,19 @@ struct SplitLds {
     int n;
     uint4 qb[NGRP][65];      // [g][lane]: q of column head lane % 16, channel
                              // slice lane / 16 of group g; [g][64] is zero
+    // wave merge: row maxima, scaled row sums and zero-point sums per wave
+    float mm[WAVES][16], lw[WAVES][16], zz[WAVES][16][NGRP];
+    // the stages; a wave's merged output rows go to its own stage's code
+    // area (whose stale bytes are harmless), or after the stages when a
+    // one-kv-head stage is too small for 16 rows
     union alignas(16) {
-        uint8_t stage[WAVES][stage_bytes(P)];
-        struct {
-            float o[WAVES][16][HD];
-            float m[WAVES][16], l[WAVES][16], z[WAVES][16][NGRP];
-        } mg;
+        uint8_t stage[WAVES * stage_bytes(P) + (P == 1 ? WAVES * 16 * HD * 4 : 0)];
         int scan[WAVES * 64];
     } u;
+    __device__ float *merge_rows(int w) {
+        return reinterpret_cast<float *>(u.stage + (P == 1 ? WAVES * stage_bytes(P) + w * 16 * HD * 4
+                                                           : w * stage_bytes(P) + code0(P)));
+    }
 };
 
 // One work item (sequence, kv-head pack, run of E entries).
@@ -556,7 +561,7 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     //    k + WAVES run while entry k is computed
     const int n_ent = __builtin_amdgcn_readfirstlane(sh.n);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    uint8_t *stg = sh.u.stage[wv];
+    uint8_t *stg = sh.u.stage + wv * stage_bytes(P);
     auto issue = [&](int k) {
         // block metadata is wave-uniform: keep it in scalar registers
         const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
@@ -597,9 +602,10 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         else
             attend_block<G, 2>(stg, np, msk, tile, ptile, pack == 0, qa, qsum, scale2, st, next);
     }
-    __syncthreads();   // every wave is done with its stage: the merge reuses it
-
-    // -- merge the waves of this workgroup and write the run's partial
+    // -- merge the waves of this workgroup and write the run's partial.  Each
+    //    wave publishes its row maxima, then writes its output rows already
+    //    rescaled to the workgroup maximum (zero-point term included) into its
+    //    own stage; the rows are then summed over the waves in a fixed order.
     float lsum = st.l;
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
@@ -611,44 +617,59 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         zs[g] += __shfl_xor(zs[g], 32);
     }
     if (hi == 0) {
-        sh.u.mg.m[wave][lo] = st.m;
-        sh.u.mg.l[wave][lo] = lsum;
+        sh.mm[wave][lo] = st.m;
 #pragma unroll
-        for (int g = 0; g < NGRP; ++g) sh.u.mg.z[wave][lo][g] = zs[g];
+        for (int g = 0; g < NGRP; ++g) sh.zz[wave][lo][g] = zs[g];
     }
-    const float inv_mult = 1.0f / st.mult;
+    __syncthreads();   // maxima and zero-point sums of every wave
+    {
+        // this lane's output rows are 4hi..4hi+3
+        const float inv_mult = 1.0f / st.mult;
+        float f[4];
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * hi + i;
+            float M = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sh.u.mg.o[wave][4 * hi + i][16 * n + lo] = st.o[n][i] * inv_mult;
+            for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.mm[w][r]);
+            const float mw = sh.mm[wave][r];
+            f[i] = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
+        }
+        if (hi == 0) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.mm[w][lo]);
+            sh.lw[wave][lo] = st.m == -INFINITY ? 0.f : lsum * exp2_fast(st.m - M);
+        }
+        float *rows_out = sh.merge_rows(wave);
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * hi + i;
+                rows_out[r * HD + 16 * n + lo] = f[i] * fmaf(st.o[n][i], inv_mult, sh.zz[wave][r][n >> 1]);
+            }
+    }
     __syncthreads();
 
     const int rows = np * G;
     for (int idx = tid; idx < rows * HD; idx += WAVES * 64) {
         const int rr = idx / HD, d = idx % HD;
-        float M = -INFINITY;
+        float o = 0.f;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.u.mg.m[w][rr]);
-        float L = 0.f, o = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const float mw = sh.u.mg.m[w][rr];
-            const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-            L = fmaf(sh.u.mg.l[w][rr], f, L);
-            o = fmaf(sh.u.mg.o[w][rr][d] + sh.u.mg.z[w][rr][d / GS], f, o);
-        }
+        for (int w = 0; w < WAVES; ++w) o += sh.merge_rows(w)[rr * HD + d];
         const size_t hrow = (size_t)b * c.Hq + (size_t)kh0 * G + rr;
         ws.o[(hrow * S + split) * HD + d] = o;
         if (d == 0) {
+            float M = -INFINITY, L = 0.f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.mm[w][rr]);
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) L += sh.lw[w][rr];
             ws.ml[(hrow * S + split) * 2 + 0] = M;
             ws.ml[(hrow * S + split) * 2 + 1] = L;
         }
     }
-    __syncthreads();   // the merge area has been read
-    // zero it: a later stage may keep any of its bytes as stale (scale,
-    // zero) pairs, which must be finite fp16 (the merge floats need not be)
-    for (int i = tid; i < (int)(sizeof(sh.u.mg) / 16); i += WAVES * 64)
-        reinterpret_cast<uint4 *>(&sh.u.mg)[i] = make_uint4(0, 0, 0, 0);
 }
 
 // Work items are (sequence, kv-head pack, run of E table entries), ordered
@@ -694,7 +715,8 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     __syncthreads();
     const int n_items = s_first[c.B];
 
-    // -- stage bytes start finite: zero the shared area once (the scan used it)
+    // -- stage bytes start finite: zero the shared area once (the scan used it;
+    //    later only loaded pairs and merged rows in the code areas land there)
     for (int i = tid; i < (int)(sizeof(lds.u) / 16); i += NT)
         reinterpret_cast<uint4 *>(&lds.u)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
