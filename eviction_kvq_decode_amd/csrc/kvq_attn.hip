@@ -141,29 +141,34 @@ struct WaveState {
 // ---------------------------------------------------------------------------
 // Block staging.  Each wave owns an LDS stage that holds one block-pack: the
 // (scale, zero) areas of its kv heads at a * 512, the block's 16 slot
-// positions at P * 512 (first pack of a sequence only), and the code areas
-// at code0(P) + a * CB (CB = 512 * BITS).  Loads go straight from HBM to
-// LDS, 1 KB per instruction (lane i's 16 bytes land at base + 16 i), and
-// skip the 16-byte chunks that belong only to evicted slots; those bytes
-// keep stale contents.  The (scale, zero) areas sit at the same place for
-// every bit width, so their stale bytes are always zeros or pairs of valid
-// slots: finite fp16, which a cleared slot (p = 0) turns into exact zeros.
+// positions at P * 512 (first pack of a sequence only), kv head a's K codes
+// at kcode0(P) + 2048 a and its V codes at vcode0(P) + 2048 a, whatever the
+// bit width (an 8-bit block fills them; 4- and 2-bit blocks use the first
+// half or quarter).  The areas of one part sit at the same place for every
+// bit width, so the next block's V part can land while this block's K codes
+// are read.  Loads go straight from HBM to LDS, 1 KB per instruction (lane
+// i's 16 bytes land at base + 16 i), and skip the 16-byte chunks that belong
+// only to evicted slots; those bytes keep stale contents.  The (scale, zero)
+// areas only ever hold zeros or pairs of valid slots: finite fp16, which a
+// cleared slot (p = 0) turns into exact zeros.
 constexpr int STAGE_REGION = 4096 + 512;                        // 8-bit region
+constexpr int CODE_AREA = 2048;                                 // per part and kv head
 __host__ __device__ constexpr int stage_bytes(int P) { return P * STAGE_REGION + 64; }
-__host__ __device__ constexpr int code0(int P) { return P * 512 + 64; }
+__host__ __device__ constexpr int kcode0(int P) { return P * 512 + 64; }
+__host__ __device__ constexpr int vcode0(int P) { return kcode0(P) + P * CODE_AREA; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// lane i: 16 bytes from gptr (its own address) + OFF to lds_base + OFF + 16 i.
+// lane i: 16 bytes from gptr (its own address) + GOFF to lds_dst + 16 i.
 // Written as an instruction the compiler does not track: its waits would
 // otherwise drain every store behind these loads before any later LDS read
 // (it cannot tell the stage from other LDS data).  The kernel waits for the
 // loads itself.  The instruction has no register result; m0 carries the LDS
 // base and needs one wait state before the load.
-template <int OFF = 0>
-__device__ inline void lds_load16(const void *gptr, uint8_t *lds_base) {
-    const uint32_t lds = (uint32_t)(size_t)(lds_void *)lds_base + OFF;
-    const uint8_t *g = static_cast<const uint8_t *>(gptr) + OFF;
+template <int GOFF = 0>
+__device__ inline void lds_load16(const void *gptr, uint8_t *lds_dst) {
+    const uint32_t lds = (uint32_t)(size_t)(lds_void *)lds_dst;
+    const uint8_t *g = static_cast<const uint8_t *>(gptr) + GOFF;
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds)
                  : "memory", "m0");
 }
@@ -173,10 +178,12 @@ __device__ inline void wait_vm1() { __builtin_amdgcn_s_waitcnt(0x0F71); }
 __device__ inline void wait_vm2() { __builtin_amdgcn_s_waitcnt(0x0F72); }
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Issue the loads of one block-pack into `stage`.  blk = the pack's first
-// region (kv head kh0) in HBM; np kv heads are real; posb = the block's
-// positions or null.
-template <int BITS, int P>
+// Issue the loads of one block-pack into `stage`, in two parts: PART_V
+// (V codes, both (scale, zero) areas and the positions) and PART_K (K
+// codes).  blk = the pack's first region (kv head kh0) in HBM; np kv heads
+// are real; posb = the block's positions or null.
+constexpr int PART_V = 1, PART_K = 2;
+template <int BITS, int P, int PART>
 __device__ inline void issue_block(uint8_t *stage, const uint8_t *blk, int np, uint32_t m16, const int *posb) {
     constexpr uint32_t CB = 512u * BITS, RB = CB + 512u;
     const int lane = threadIdx.x & 63;
@@ -185,63 +192,78 @@ __device__ inline void issue_block(uint8_t *stage, const uint8_t *blk, int np, u
     // addresses: a wave-uniform base plus a 32-bit lane offset; loads that
     // share a lane predicate are issued under one exec mask
     const uint32_t loff = (uint32_t)lane * 16u;
-    if constexpr (BITS == 8) {
-        // K: token (1024 j + 16 lane) / 128 = 8 j + lane / 8; V: two 1 KB halves
-        if ((m16 >> (lane >> 3)) & 1u) {
+    if constexpr (PART == PART_K) {
+        if constexpr (BITS == 8) {
+            // token (1024 j + 16 lane) / 128 = 8 j + lane / 8
+            if ((m16 >> (lane >> 3)) & 1u) {
 #pragma unroll
-            for (int a = 0; a < P; ++a)
-                if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + code0(P) + a * CB);
-        }
-        if ((m16 >> (8 + (lane >> 3))) & 1u) {
+                for (int a = 0; a < P; ++a)
+                    if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + kcode0(P) + a * CODE_AREA);
+            }
+            if ((m16 >> (8 + (lane >> 3))) & 1u) {
 #pragma unroll
-            for (int a = 0; a < P; ++a)
-                if (a < np) lds_load16<1024>(blk + (a * RB + loff), stage + code0(P) + a * CB);
-        }
-        if ((live4 >> (lane >> 4)) & 1u) {
+                for (int a = 0; a < P; ++a)
+                    if (a < np) lds_load16<1024>(blk + (a * RB + loff), stage + kcode0(P) + a * CODE_AREA + 1024);
+            }
+        } else if constexpr (BITS == 4) {
+            if ((m16 >> (lane >> 2)) & 1u) {                          // token lane / 4
 #pragma unroll
-            for (int a = 0; a < P; ++a)
-                if (a < np) {
-                    lds_load16<2048>(blk + (a * RB + loff), stage + code0(P) + a * CB);
-                    lds_load16<3072>(blk + (a * RB + loff), stage + code0(P) + a * CB);
-                }
-        }
-    } else if constexpr (BITS == 4) {
-        if ((m16 >> (lane >> 2)) & 1u) {                              // K: token lane / 4
+                for (int a = 0; a < P; ++a)
+                    if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + kcode0(P) + a * CODE_AREA);
+            }
+        } else {
+            if (lane < 32 && ((m16 >> (lane >> 1)) & 1u)) {           // token lane / 2
 #pragma unroll
-            for (int a = 0; a < P; ++a)
-                if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + code0(P) + a * CB);
-        }
-        if ((live4 >> (lane >> 4)) & 1u) {
-#pragma unroll
-            for (int a = 0; a < P; ++a)
-                if (a < np) lds_load16<1024>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+                for (int a = 0; a < P; ++a)
+                    if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + kcode0(P) + a * CODE_AREA);
+            }
         }
     } else {
-        // K in lanes 0-31 (token lane / 2), V in lanes 32-63 (group (lane-32) / 8)
-        const bool pr = lane < 32 ? ((m16 >> (lane >> 1)) & 1u) : ((live4 >> ((lane - 32) >> 3)) & 1u);
-        if (pr) {
+        if constexpr (BITS == 8) {
+            // two 1 KB halves; a 16-byte chunk holds 4 consecutive tokens
+            if ((live4 >> (lane >> 4)) & 1u) {
 #pragma unroll
-            for (int a = 0; a < P; ++a)
-                if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + code0(P) + a * CB);
+                for (int a = 0; a < P; ++a)
+                    if (a < np) {
+                        lds_load16<2048>(blk + (a * RB + loff), stage + vcode0(P) + a * CODE_AREA);
+                        lds_load16<3072>(blk + (a * RB + loff), stage + vcode0(P) + a * CODE_AREA + 1024);
+                    }
+            }
+        } else if constexpr (BITS == 4) {
+            if ((live4 >> (lane >> 4)) & 1u) {
+#pragma unroll
+                for (int a = 0; a < P; ++a)
+                    if (a < np) lds_load16<1024>(blk + (a * RB + loff), stage + vcode0(P) + a * CODE_AREA);
+            }
+        } else {
+            // the V codes follow the 512 K bytes: lanes 32-63 of the region's
+            // first 1 KB (group (lane - 32) / 8 of 4 tokens), landing at the
+            // start of the V area
+            if (lane >= 32 && ((live4 >> ((lane - 32) >> 3)) & 1u)) {
+#pragma unroll
+                for (int a = 0; a < P; ++a)
+                    if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + vcode0(P) + a * CODE_AREA - 512);
+            }
         }
-    }
-    // (scale, zero) areas, two kv heads per instruction: lane i < 32 takes
-    // chunk i of head 2 a2, lane i >= 32 chunk i - 32 of head 2 a2 + 1;
-    // chunk c < 16 holds token c's K pairs, c >= 16 token c - 16's V pairs
-    if ((m16 >> (lane & 15)) & 1u) {
-        const uint32_t soff = (uint32_t)(lane >> 5) * RB + CB + ((uint32_t)lane & 31u) * 16u;
+        // (scale, zero) areas, two kv heads per instruction: lane i < 32 takes
+        // chunk i of head 2 a2, lane i >= 32 chunk i - 32 of head 2 a2 + 1;
+        // chunk c < 16 holds token c's K pairs, c >= 16 token c - 16's V pairs
+        if ((m16 >> (lane & 15)) & 1u) {
+            const uint32_t soff = (uint32_t)(lane >> 5) * RB + CB + ((uint32_t)lane & 31u) * 16u;
 #pragma unroll
-        for (int a2 = 0; a2 < (P + 1) / 2; ++a2)
-            if (2 * a2 + (lane >> 5) < np) lds_load16(blk + (2u * a2 * RB + soff), stage + a2 * 1024);
+            for (int a2 = 0; a2 < (P + 1) / 2; ++a2)
+                if (2 * a2 + (lane >> 5) < np) lds_load16(blk + (2u * a2 * RB + soff), stage + a2 * 1024);
+        }
+        if (posb != nullptr && lane < 4 && ((m16 >> (4 * lane)) & 15u))
+            lds_load16(reinterpret_cast<const uint8_t *>(posb) + loff, stage + P * 512);
     }
-    if (posb != nullptr && lane < 4 && ((m16 >> (4 * lane)) & 15u))
-        lds_load16(reinterpret_cast<const uint8_t *>(posb) + loff, stage + P * 512);
 }
 
-// The next block-pack's loads, issued by attend_block once it holds the
-// current one in registers.
+// The next block-pack's loads, issued by attend_block in two parts: the V
+// part once the current block's V codes, pairs and positions are in
+// registers, the K part once its QK^T products have read the K codes.
 struct NoNext {
-    __device__ void operator()() const {}
+    __device__ void operator()(int) const {}
 };
 
 template <int G, int BITS, class Next>
@@ -249,7 +271,6 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
                                     bool has_pos, const uint4 *const *qa, const float *qsum, float scale2,
                                     WaveState &st, const Next &next) {
     constexpr int P = PACK(G);
-    constexpr uint32_t CB = 512u * BITS;
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
     const int a_rho = min(lo / G, np - 1);
     const bool row_ok = lo < np * G;
@@ -263,17 +284,17 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
     uint32_t vw[P][VW];
 #pragma unroll
     for (int a = 0; a < P; ++a) {
-        const uint8_t *lr = stage + code0(P) + (uint32_t)min(a, np - 1) * CB;
+        const uint8_t *lr = stage + vcode0(P) + (uint32_t)min(a, np - 1) * CODE_AREA;
         if constexpr (BITS == 8) {
-            const uint4 v0 = *reinterpret_cast<const uint4 *>(lr + 2048 + lane * 16);
-            const uint4 v1 = *reinterpret_cast<const uint4 *>(lr + 3072 + lane * 16);
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(lr + lane * 16);
+            const uint4 v1 = *reinterpret_cast<const uint4 *>(lr + 1024 + lane * 16);
             vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
             vw[a][4] = v1.x; vw[a][5] = v1.y; vw[a][6] = v1.z; vw[a][7] = v1.w;
         } else if constexpr (BITS == 4) {
-            const uint4 v0 = *reinterpret_cast<const uint4 *>(lr + 1024 + lane * 16);
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(lr + lane * 16);
             vw[a][0] = v0.x; vw[a][1] = v0.y; vw[a][2] = v0.z; vw[a][3] = v0.w;
         } else {
-            const uint2 v0 = *reinterpret_cast<const uint2 *>(lr + 512 + lane * 8);
+            const uint2 v0 = *reinterpret_cast<const uint2 *>(lr + lane * 8);
             vw[a][0] = v0.x; vw[a][1] = v0.y;
         }
     }
@@ -290,6 +311,10 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
     }
     int4 pos4 = make_int4(0, 0, 0, 0);
     if (has_pos && lo == 0) pos4 = reinterpret_cast<const int4 *>(stage + P * 512)[hi];
+    // -- those reads have landed: the next block-pack's V part may overwrite
+    //    them while this one's K codes are still read
+    wait_lgkm0();
+    next(PART_V);
 
     // -- QK^T per group: rows = tokens, columns = the pack's 16 query heads;
     //    a kv head's codes meet only its own heads (block-diagonal q: a
@@ -300,7 +325,7 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
     for (int g = 0; g < NGRP; ++g) acc[g] = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int a = 0; a < P; ++a) {
-        const uint8_t *lr = stage + code0(P) + (uint32_t)min(a, np - 1) * CB;
+        const uint8_t *lr = stage + kcode0(P) + (uint32_t)min(a, np - 1) * CODE_AREA;
         uint32_t kw[KW];
         if constexpr (BITS == 8) {
             const uint4 k0 = *reinterpret_cast<const uint4 *>(lr + lo * 128 + hi * 32);
@@ -321,11 +346,10 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
         }
     }
 
-    // -- the stage reads have landed: start the next block-pack.  No
-    //    LDS read follows in this block (an LDS read after the loads would
-    //    have to wait for them).
+    // -- the K reads have landed: the next block-pack's K part.  No LDS
+    //    read follows in this block.
     wait_lgkm0();
-    next();
+    next(PART_K);
 
     // -- scores of tokens 4hi..4hi+3 for head lo: fold the group scales and
     //    zeros, base-2 scale, mask cleared slots (a cleared slot's stage
@@ -447,9 +471,9 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
                                                         tv[2] ? pos4.z : -1, tv[3] ? pos4.w : -1);
 }
 
-// Workgroup LDS of the split kernel.  The stages and the wave-merge buffers
-// share one area (the merge runs after every wave has left its loop); the
-// prologue's scan buffer uses it too.
+// Workgroup LDS of the split kernel.  A wave's merged output rows reuse its
+// stage's code area once every wave has left its loop; the prologue's scan
+// buffer shares the stage area too.
 template <int P>
 struct SplitLds {
     uint32_t ent[E];
@@ -468,7 +492,7 @@ struct SplitLds {
     } u;
     __device__ float *merge_rows(int w) {
         return reinterpret_cast<float *>(u.stage + (P == 1 ? WAVES * stage_bytes(P) + w * 16 * HD * 4
-                                                           : w * stage_bytes(P) + code0(P)));
+                                                           : w * stage_bytes(P) + kcode0(P)));
     }
 };
 
@@ -562,26 +586,35 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     const int n_ent = __builtin_amdgcn_readfirstlane(sh.n);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     uint8_t *stg = sh.u.stage + wv * stage_bytes(P);
-    auto issue = [&](int k) {
+    auto issue = [&](int k, int part) {
         // block metadata is wave-uniform: keep it in scalar registers
         const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
         const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
         const int pool = (int)(ent >> 30);
         const uint32_t id = ent & 0x3fffffffu;
         const int *pb = pack == 0 ? c.pos[pool] + (size_t)id * BLK : nullptr;
-        if (pool == 0)
-            issue_block<8, P>(stg, c.kv[0] + ((size_t)id * c.Hkv + kh0) * (512u * 8 + 512u), np, msk, pb);
-        else if (pool == 1)
-            issue_block<4, P>(stg, c.kv[1] + ((size_t)id * c.Hkv + kh0) * (512u * 4 + 512u), np, msk, pb);
-        else
-            issue_block<2, P>(stg, c.kv[2] + ((size_t)id * c.Hkv + kh0) * (512u * 2 + 512u), np, msk, pb);
+        const uint8_t *blk0 = c.kv[0] + ((size_t)id * c.Hkv + kh0) * (512u * 8 + 512u);
+        const uint8_t *blk1 = c.kv[1] + ((size_t)id * c.Hkv + kh0) * (512u * 4 + 512u);
+        const uint8_t *blk2 = c.kv[2] + ((size_t)id * c.Hkv + kh0) * (512u * 2 + 512u);
+        if (part == PART_V) {
+            if (pool == 0) issue_block<8, P, PART_V>(stg, blk0, np, msk, pb);
+            else if (pool == 1) issue_block<4, P, PART_V>(stg, blk1, np, msk, pb);
+            else issue_block<2, P, PART_V>(stg, blk2, np, msk, pb);
+        } else {
+            if (pool == 0) issue_block<8, P, PART_K>(stg, blk0, np, msk, pb);
+            else if (pool == 1) issue_block<4, P, PART_K>(stg, blk1, np, msk, pb);
+            else issue_block<2, P, PART_K>(stg, blk2, np, msk, pb);
+        }
     };
-    if (wv < n_ent) issue(wv);
+    if (wv < n_ent) {
+        issue(wv, PART_V);
+        issue(wv, PART_K);
+    }
     for (int k = wv; k < n_ent; k += WAVES) {
         // entry k is in the stage once its loads are done.  The vector memory
         // counter also counts stores, and returns in issue order: after the
         // first entry, the previous entry's score tile (and position) stores
-        // were issued after these loads and may stay in flight.
+        // were issued after both parts' loads and may stay in flight.
         if (k == wv) wait_vm0();
         else if (pack == 0) wait_vm2();
         else wait_vm1();
@@ -592,8 +625,8 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         int *ptile = ws.spos + ek * 16;
         const int pool = (int)(ent >> 30);
         const int kn = k + WAVES;
-        auto next = [&]() {
-            if (kn < n_ent) issue(kn);
+        auto next = [&](int part) {
+            if (kn < n_ent) issue(kn, part);
         };
         if (pool == 0)
             attend_block<G, 8>(stg, np, msk, tile, ptile, pack == 0, qa, qsum, scale2, st, next);
