@@ -45,61 +45,75 @@ constexpr int WAVES = KVQ_WAVES;
 // kv heads packed into one wave: the 16 MFMA columns hold PACK(G) * G query heads
 __host__ __device__ constexpr int PACK(int G) { return 16 / G < 4 ? 16 / G : 4; }
 constexpr float P_HEADROOM = 60000.0f;    // P' = p * v_scale * mult must stay below fp16 max
-constexpr uint32_t BIAS2 = 0x64006400u;   // two fp16 1024.0: (1024 + c) has c in its low bits
 
-// Codes become exact integer-valued fp16 operands: the code bits are placed
-// under the exponent of 1024 (0x64 high byte), giving 1024 + c, and 1024 is
-// subtracted with one packed fp16 add.  (Operands with a zero exponent,
-// i.e. c * 2^-24 subnormals, would save the subtract but lose precision in
-// the MFMA products on this hardware.)
-__device__ inline uint32_t unbias(uint32_t x) {
+// Codes become exact integer-valued fp16 MFMA operands, each as B + c for a
+// power-of-two bias B whose exponent puts the code's bits at the top of the
+// mantissa: B = 1024 for 8-bit codes (0x64 high byte, code in the low byte),
+// 16 for 4-bit codes (0x4C00 | c << 6) and 4 for 2-bit codes (0x4400 |
+// c << 8).  B is then about the size of the codes, so the bias can stay in
+// the operand and be taken out of the fp32 sums at no cost in precision:
+// through the q sums for K (B * sum q) and through the zero-point sums for
+// V (B * sum P').  Only 8-bit K codes are unbiased before the product (one
+// packed fp16 subtract), because the scores feed the per-token mass, whose
+// tolerance is tighter than the 8 : 1 bias-to-code ratio allows.  (Operands
+// with a zero exponent, c * 2^-24 subnormals, would need no bias but lose
+// precision in the MFMA products on this hardware.)
+template <int BITS>
+struct Code {
+    static constexpr float BIAS = BITS == 8 ? 1024.0f : BITS == 4 ? 16.0f : 4.0f;
+    static constexpr uint32_t BIAS2 = BITS == 8 ? 0x64006400u : BITS == 4 ? 0x4C004C00u : 0x44004400u;
+    static constexpr uint32_t FIELDS = BITS == 4 ? 0x03C003C0u : 0x03000300u;   // mantissa top field
+    static constexpr int TOP = BITS == 4 ? 6 : 8;                              // its lowest bit
+};
+__device__ inline uint32_t unbias1024(uint32_t x) {
     half2v h = __builtin_bit_cast(half2v, x);
     h = h - (half2v){(_Float16)1024.0f, (_Float16)1024.0f};
     return __builtin_bit_cast(uint32_t, h);
 }
-// Bytes i and j of w as the exact fp16 pair (w.byte[i], w.byte[j]).
+// Bytes i and j of w as the fp16 pair (1024 + w.byte[i], 1024 + w.byte[j]).
 __device__ inline uint32_t byte_pair(uint32_t w, int i, int j) {
     const uint32_t sel = (uint32_t)(4 + i) | ((uint32_t)(4 + j) << 16);  // selector 0: a 0x64 byte
-    return unbias(__builtin_amdgcn_perm(w, 0x64646464u, sel));
+    return __builtin_amdgcn_perm(w, 0x64646464u, sel);
 }
-// Fields at bit offsets sh and sh+16 of w (mask m per field) as an exact fp16
-// pair.  vb holds BIAS2 in a vector register the compiler cannot see through,
-// so mask-and-bias is one v_and_or_b32 (a VOP3 instruction takes neither a
-// literal nor two scalar operands here).
-__device__ inline uint32_t field_pair(uint32_t w, int sh, uint32_t m, uint32_t vb) {
-    return unbias(((w >> sh) & m) | vb);
+__device__ inline uint32_t shift_signed(uint32_t w, int s) { return s >= 0 ? w << s : w >> -s; }
+// The 4- or 2-bit fields at bit offsets sh and sh+16 of w as the fp16 pair
+// (B + c0, B + c1): one shift and one v_and_or_b32.  vb holds BIAS2 in a
+// vector register the compiler cannot see through (a VOP3 instruction takes
+// neither a literal nor two scalar operands here).
+template <int BITS>
+__device__ inline uint32_t field_pair(uint32_t w, int sh, uint32_t vb) {
+    return (shift_signed(w, Code<BITS>::TOP - sh) & Code<BITS>::FIELDS) | vb;
 }
+template <int BITS>
 __device__ inline uint32_t opaque_bias() {
-    uint32_t vb = BIAS2;
+    uint32_t vb = Code<BITS>::BIAS2;
     asm volatile("" : "+v"(vb));
     return vb;
 }
 
 // QK A operand: the eight codes of group g held by this lane's K slice,
-// in channel order e0..e7 (see the K row layout).
+// in channel order e0..e7 (see the K row layout); 8-bit codes exact, 4- and
+// 2-bit codes as B + c.
 template <int BITS>
 __device__ inline half8 k_operand(const uint32_t *kw, int g, uint32_t vb) {
     uint32_t r[4];
     if constexpr (BITS == 8) {
-        r[0] = byte_pair(kw[2 * g], 0, 1);
-        r[1] = byte_pair(kw[2 * g], 2, 3);
-        r[2] = byte_pair(kw[2 * g + 1], 0, 1);
-        r[3] = byte_pair(kw[2 * g + 1], 2, 3);
+        r[0] = unbias1024(byte_pair(kw[2 * g], 0, 1));
+        r[1] = unbias1024(byte_pair(kw[2 * g], 2, 3));
+        r[2] = unbias1024(byte_pair(kw[2 * g + 1], 0, 1));
+        r[3] = unbias1024(byte_pair(kw[2 * g + 1], 2, 3));
     } else if constexpr (BITS == 4) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) r[k] = field_pair(kw[g], 4 * k, 0x000F000Fu, vb);
+        for (int k = 0; k < 4; ++k) r[k] = field_pair<4>(kw[g], 4 * k, vb);
     } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) r[k] = field_pair(kw[g >> 1], 2 * (4 * (g & 1) + k), 0x00030003u, vb);
+        for (int k = 0; k < 4; ++k) r[k] = field_pair<2>(kw[g >> 1], 2 * (4 * (g & 1) + k), vb);
     }
     return __builtin_bit_cast(half8, r);
 }
 
-// PV B operand: codes of tokens 4r..4r+3 at this lane's channel of tile n.
-// 8-bit codes keep the 1024 bias (1024 + c): the bias's contribution,
-// 1024 * sum P', is taken out through the zero-point sum instead (8-bit
-// codes are large enough next to 1024 for the fp32 accumulation to keep
-// them; 4- and 2-bit codes are not, and are unbiased exactly).
+// PV B operand: codes of tokens 4r..4r+3 at this lane's channel of tile n,
+// as B + c.
 template <int BITS>
 __device__ inline half4 v_operand(const uint32_t *vw, int n, uint32_t vb) {
     uint32_t r[2];
@@ -109,12 +123,12 @@ __device__ inline half4 v_operand(const uint32_t *vw, int n, uint32_t vb) {
         r[1] = __builtin_amdgcn_perm(w, 0x64646464u, 5u | (7u << 16));
     } else if constexpr (BITS == 4) {
         const int m = n & 1;
-        r[0] = field_pair(vw[n >> 1], 8 * m, 0x000F000Fu, vb);
-        r[1] = field_pair(vw[n >> 1], 8 * m + 4, 0x000F000Fu, vb);
+        r[0] = field_pair<4>(vw[n >> 1], 8 * m, vb);
+        r[1] = field_pair<4>(vw[n >> 1], 8 * m + 4, vb);
     } else {
         const int m = n & 3;
-        r[0] = field_pair(vw[n >> 2], 4 * m, 0x00030003u, vb);
-        r[1] = field_pair(vw[n >> 2], 4 * m + 2, 0x00030003u, vb);
+        r[0] = field_pair<2>(vw[n >> 2], 4 * m, vb);
+        r[1] = field_pair<2>(vw[n >> 2], 4 * m + 2, vb);
     }
     return __builtin_bit_cast(half4, r);
 }
@@ -172,15 +186,13 @@ __device__ inline void lds_load16(const void *gptr, uint8_t *lds_dst) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds)
                  : "memory", "m0");
 }
-// s_waitcnt encodings (gfx9): vmcnt(0..2), and lgkmcnt(0) alone
+// s_waitcnt encodings (gfx9): vmcnt(0), and lgkmcnt(0) alone
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-__device__ inline void wait_vm1() { __builtin_amdgcn_s_waitcnt(0x0F71); }
-__device__ inline void wait_vm2() { __builtin_amdgcn_s_waitcnt(0x0F72); }
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Issue the loads of one block-pack into `stage`, in two parts: PART_V
-// (V codes, both (scale, zero) areas and the positions) and PART_K (K
-// codes).  blk = the pack's first region (kv head kh0) in HBM; np kv heads
+// (V codes and both (scale, zero) areas) and PART_K (K codes and the
+// positions).  blk = the pack's first region (kv head kh0) in HBM; np kv heads
 // are real; posb = the block's positions or null.
 constexpr int PART_V = 1, PART_K = 2;
 template <int BITS, int P, int PART>
@@ -193,29 +205,37 @@ __device__ inline void issue_block(uint8_t *stage, const uint8_t *blk, int np, u
     // share a lane predicate are issued under one exec mask
     const uint32_t loff = (uint32_t)lane * 16u;
     if constexpr (PART == PART_K) {
+        // K rows are swizzled in LDS: a token's 16-byte chunks are stored in
+        // an order that depends on the token (chunk j of token t at chunk
+        // position j ^ k_swz(t)), so the sixteen token lanes that read the
+        // same chunk of their rows meet different banks.  Lane i lands at
+        // chunk position i and therefore loads the chunk stored there.
         if constexpr (BITS == 8) {
             // token (1024 j + 16 lane) / 128 = 8 j + lane / 8
+            const uint32_t koff = (((uint32_t)lane & ~7u) | (((uint32_t)lane ^ ((uint32_t)lane >> 3)) & 7u)) * 16u;
             if ((m16 >> (lane >> 3)) & 1u) {
 #pragma unroll
                 for (int a = 0; a < P; ++a)
-                    if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + kcode0(P) + a * CODE_AREA);
+                    if (a < np) lds_load16<0>(blk + (a * RB + koff), stage + kcode0(P) + a * CODE_AREA);
             }
             if ((m16 >> (8 + (lane >> 3))) & 1u) {
 #pragma unroll
                 for (int a = 0; a < P; ++a)
-                    if (a < np) lds_load16<1024>(blk + (a * RB + loff), stage + kcode0(P) + a * CODE_AREA + 1024);
+                    if (a < np) lds_load16<1024>(blk + (a * RB + koff), stage + kcode0(P) + a * CODE_AREA + 1024);
             }
         } else if constexpr (BITS == 4) {
+            const uint32_t koff = (((uint32_t)lane & ~3u) | (((uint32_t)lane ^ ((uint32_t)lane >> 3)) & 3u)) * 16u;
             if ((m16 >> (lane >> 2)) & 1u) {                          // token lane / 4
 #pragma unroll
                 for (int a = 0; a < P; ++a)
-                    if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + kcode0(P) + a * CODE_AREA);
+                    if (a < np) lds_load16<0>(blk + (a * RB + koff), stage + kcode0(P) + a * CODE_AREA);
             }
         } else {
+            const uint32_t koff = (((uint32_t)lane & ~1u) | (((uint32_t)lane ^ ((uint32_t)lane >> 3)) & 1u)) * 16u;
             if (lane < 32 && ((m16 >> (lane >> 1)) & 1u)) {           // token lane / 2
 #pragma unroll
                 for (int a = 0; a < P; ++a)
-                    if (a < np) lds_load16<0>(blk + (a * RB + loff), stage + kcode0(P) + a * CODE_AREA);
+                    if (a < np) lds_load16<0>(blk + (a * RB + koff), stage + kcode0(P) + a * CODE_AREA);
             }
         }
     } else {
@@ -254,6 +274,8 @@ __device__ inline void issue_block(uint8_t *stage, const uint8_t *blk, int np, u
             for (int a2 = 0; a2 < (P + 1) / 2; ++a2)
                 if (2 * a2 + (lane >> 5) < np) lds_load16(blk + (2u * a2 * RB + soff), stage + a2 * 1024);
         }
+    }
+    if constexpr (PART == PART_K) {
         if (posb != nullptr && lane < 4 && ((m16 >> (4 * lane)) & 15u))
             lds_load16(reinterpret_cast<const uint8_t *>(posb) + loff, stage + P * 512);
     }
@@ -267,14 +289,14 @@ struct NoNext {
 };
 
 template <int G, int BITS, class Next>
-__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, float *tile, int *ptile,
-                                    bool has_pos, const uint4 *const *qa, const float *qsum, float scale2,
+__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, float *score, int *spos,
+                                    int off, bool has_pos, const uint4 *const *qa, const float *qsum, float scale2,
                                     WaveState &st, const Next &next) {
     constexpr int P = PACK(G);
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
     const int a_rho = min(lo / G, np - 1);
     const bool row_ok = lo < np * G;
-    const uint32_t vb = opaque_bias();
+    const uint32_t vb = opaque_bias<BITS>();
 
     // -- the block-pack from the stage: K slice of token lo (channel slice
     //    hi), V slice of this lane, and the (scale, zero) pairs of tokens
@@ -309,10 +331,8 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
             vsz[4 * i + 0] = vq.x; vsz[4 * i + 1] = vq.y; vsz[4 * i + 2] = vq.z; vsz[4 * i + 3] = vq.w;
         }
     }
-    int4 pos4 = make_int4(0, 0, 0, 0);
-    if (has_pos && lo == 0) pos4 = reinterpret_cast<const int4 *>(stage + P * 512)[hi];
     // -- those reads have landed: the next block-pack's V part may overwrite
-    //    them while this one's K codes are still read
+    //    them while this one's K codes and positions are still read
     wait_lgkm0();
     next(PART_V);
 
@@ -323,20 +343,30 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
     floatx4 acc[NGRP];
 #pragma unroll
     for (int g = 0; g < NGRP; ++g) acc[g] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    // this lane's K slice in the swizzled rows: chunk j of token lo sits at
+    // chunk position j ^ k_swz(lo) of its row
+    uint32_t koff;
+    if constexpr (BITS == 8)
+        koff = (uint32_t)lo * 128u + (((2u * hi) ^ ((uint32_t)lo & 7u)) << 4);
+    else if constexpr (BITS == 4)
+        koff = (uint32_t)lo * 64u + (((uint32_t)hi ^ (((uint32_t)lo >> 1) & 3u)) << 4);
+    else
+        koff = (uint32_t)lo * 32u + ((((uint32_t)hi >> 1) ^ (((uint32_t)lo >> 2) & 1u)) << 4) + (((uint32_t)hi & 1u) << 3);
 #pragma unroll
     for (int a = 0; a < P; ++a) {
         const uint8_t *lr = stage + kcode0(P) + (uint32_t)min(a, np - 1) * CODE_AREA;
         uint32_t kw[KW];
         if constexpr (BITS == 8) {
-            const uint4 k0 = *reinterpret_cast<const uint4 *>(lr + lo * 128 + hi * 32);
-            const uint4 k1 = *reinterpret_cast<const uint4 *>(lr + lo * 128 + hi * 32 + 16);
+            // the lane's two chunks differ only in the lowest position bit
+            const uint4 k0 = *reinterpret_cast<const uint4 *>(lr + koff);
+            const uint4 k1 = *reinterpret_cast<const uint4 *>(lr + (koff ^ 16u));
             kw[0] = k0.x; kw[1] = k0.y; kw[2] = k0.z; kw[3] = k0.w;
             kw[4] = k1.x; kw[5] = k1.y; kw[6] = k1.z; kw[7] = k1.w;
         } else if constexpr (BITS == 4) {
-            const uint4 k0 = *reinterpret_cast<const uint4 *>(lr + lo * 64 + hi * 16);
+            const uint4 k0 = *reinterpret_cast<const uint4 *>(lr + koff);
             kw[0] = k0.x; kw[1] = k0.y; kw[2] = k0.z; kw[3] = k0.w;
         } else {
-            const uint2 k0 = *reinterpret_cast<const uint2 *>(lr + lo * 32 + hi * 8);
+            const uint2 k0 = *reinterpret_cast<const uint2 *>(lr + koff);
             kw[0] = k0.x; kw[1] = k0.y;
         }
 #pragma unroll
@@ -345,11 +375,6 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
             acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS>(kw, g, vb), qb, acc[g], 0, 0, 0);
         }
     }
-
-    // -- the K reads have landed: the next block-pack's K part.  No LDS
-    //    read follows in this block.
-    wait_lgkm0();
-    next(PART_K);
 
     // -- scores of tokens 4hi..4hi+3 for head lo: fold the group scales and
     //    zeros, base-2 scale, mask cleared slots (a cleared slot's stage
@@ -360,13 +385,16 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
         // group by group, so each group's scale and zero terms (which largely
         // cancel) meet before the next group is added; the four tokens'
         // chains are independent and interleave
+        // (4- and 2-bit products carry the code bias: B * sum q comes off)
+        constexpr float KB = BITS == 8 ? 0.f : Code<BITS>::BIAS;
         float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < NGRP; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t sz = ksz[4 * i + g];
-                v[i] = fmaf(lo_h(sz), acc[g][i], v[i]);
+                // acc - B * sum q in one rounding (B * sum q is exact)
+                v[i] = fmaf(lo_h(sz), BITS == 8 ? acc[g][i] : fmaf(-KB, qsum[g], acc[g][i]), v[i]);
                 v[i] = fmaf(hi_h(sz), qsum[g], v[i]);
             }
 #pragma unroll
@@ -375,6 +403,30 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
             s[i] = row_ok && tv[i] ? v[i] * scale2 : -INFINITY;
         }
     }
+    // -- the valid slots' scores, and from the first pack their positions,
+    //    in the split's compacted numbering: valid slot t of this block is
+    //    number off + (valid slots of the block before t)
+    {
+        int4 pos4 = make_int4(0, 0, 0, 0);
+        if (has_pos && lo == 0) pos4 = reinterpret_cast<const int4 *>(stage + P * 512)[hi];
+        const int pp[4] = {pos4.x, pos4.y, pos4.z, pos4.w};
+        int cn = off + __popc(m16 & ((1u << (4 * hi)) - 1u));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (tv[i]) {
+                if (row_ok) score[(cn >> 4) * 256 + lo * 16 + (cn & 15)] = s[i];
+                if (has_pos && lo == 0) spos[cn] = pp[i];
+                ++cn;
+            }
+        }
+    }
+
+    // -- the K and position reads have landed: the next block-pack's K part.
+    //    No LDS read follows in this block, and the stores above were issued
+    //    before it, so the next block waits for all of its wave's memory
+    //    operations.
+    wait_lgkm0();
+    next(PART_K);
     // -- online softmax; the max only moves when some score exceeds it
     float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     if (__ballot(bm > st.m)) {
@@ -434,17 +486,17 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
     for (int g = 0; g < NGRP; ++g)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pop[g][i] = (_Float16)(pm[i] * lo_h(vsz[4 * i + g]));
-    // zero-point term sum p * v_zero, less the 8-bit V operands' bias share
-    // 1024 * P' / mult
+    // zero-point term sum p * v_zero, less the V operands' bias share
+    // B * P' / mult
     {
-        const float kb = BITS == 8 ? -1024.0f / st.mult : 0.f;
+        const float kb = -Code<BITS>::BIAS / st.mult;
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
             float zg = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 zg = fmaf(p[i], hi_h(vsz[4 * i + g]), zg);
-                if constexpr (BITS == 8) zg = fmaf(kb, (float)pop[g][i], zg);
+                zg = fmaf(kb, (float)pop[g][i], zg);
             }
             st.z[g] += zg;
         }
@@ -461,14 +513,6 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
         }
     }
 
-    // -- the block-pack's scores as one contiguous 1 KB tile [head][slot]
-    //    (lane: head lo, slots 4hi..4hi+3; cleared slots and columns past
-    //    the pack hold -inf), and, from the first pack, the slot positions
-    //    (-1 where cleared)
-    reinterpret_cast<float4 *>(tile)[lo * 4 + hi] = make_float4(s[0], s[1], s[2], s[3]);
-    if (has_pos && lo == 0)
-        reinterpret_cast<int4 *>(ptile)[hi] = make_int4(tv[0] ? pos4.x : -1, tv[1] ? pos4.y : -1,
-                                                        tv[2] ? pos4.z : -1, tv[3] ? pos4.w : -1);
 }
 
 // Workgroup LDS of the split kernel.  A wave's merged output rows reuse its
@@ -477,6 +521,7 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
 template <int P>
 struct SplitLds {
     uint32_t ent[E];
+    int off[E];              // valid slots before entry k (compacted numbering)
     uint32_t msk[E];
     int n;
     uint4 qb[NGRP][65];      // [g][lane]: q of column head lane % 16, channel
@@ -496,7 +541,7 @@ struct SplitLds {
     }
 };
 
-// One work item (sequence, kv-head pack, run of E entries).
+// One work item (sequence, kv-head pack, run of at most E entries).
 template <int G>
 __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const DecodeWs &ws,
                                   float scale2, int S, int item, const int *s_first,
@@ -518,13 +563,16 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     const int kh0 = pack * P, np = min(P, c.Hkv - kh0);
     const bool row_ok = lo < np * G;
 
-    // -- non-empty table entries of this run, compacted (wave 0)
+    // -- non-empty table entries of this run, compacted (wave 0).  Run j of
+    //    a sequence with nr runs holds table entries j, j + nr, j + 2 nr, ...
+    //    (at most E): every run samples the whole sequence, so the runs of a
+    //    sequence cost about the same whatever the order of its block widths.
     const int nb = c.n_blocks[b];
-    const int e0 = split * E;
+    const int nr = (nb + E - 1) / E;
     if (wave == 0) {
-        int n = 0;
+        int n = 0, slots = 0;
         for (int base = 0; base < E; base += 64) {
-            const int e = e0 + base + lane;
+            const int e = split + nr * (base + lane);
             uint32_t ent = 0, m = 0;
             if (base + lane < E && e < nb) {
                 ent = c.table[(size_t)b * c.max_blocks + e];
@@ -532,15 +580,24 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
             }
             const uint64_t bal = __ballot(m != 0);
             const int at = n + __popcll(bal & ((1ull << lane) - 1));
+            // valid slots of the entries before this one: a wave prefix sum
+            int cnt = __popc(m), incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(incl, d);
+                if (lane >= d) incl += y;
+            }
             if (m != 0) {
                 sh.ent[at] = ent;
                 sh.msk[at] = m;
+                sh.off[at] = slots + incl - cnt;
             }
             n += __popcll(bal);
+            slots += __shfl(incl, 63);
         }
         if (lane == 0) {
             sh.n = n;
-            if (pack == 0) ws.ents[(size_t)b * S + split] = n;
+            if (pack == 0) ws.ents[(size_t)b * S + split] = slots;
         }
     }
 
@@ -610,30 +667,27 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         issue(wv, PART_V);
         issue(wv, PART_K);
     }
+    // the run's compacted scores of this pack, and its slot positions
+    float *score = ws.score + ((size_t)(b * S + split) * n_packs + pack) * E * 256;
+    int *spos = ws.spos + (size_t)(b * S + split) * E * 16;
     for (int k = wv; k < n_ent; k += WAVES) {
-        // entry k is in the stage once its loads are done.  The vector memory
-        // counter also counts stores, and returns in issue order: after the
-        // first entry, the previous entry's score tile (and position) stores
-        // were issued after both parts' loads and may stay in flight.
-        if (k == wv) wait_vm0();
-        else if (pack == 0) wait_vm2();
-        else wait_vm1();
+        // entry k is in the stage once its wave's memory operations are done
+        // (the last ones issued are its K part)
+        wait_vm0();
         const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
         const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
-        const size_t ek = (size_t)(b * S + split) * E + k;         // entry slot of the run
-        float *tile = ws.score + (ek * n_packs + pack) * 256;
-        int *ptile = ws.spos + ek * 16;
+        const int off = __builtin_amdgcn_readfirstlane(sh.off[k]);
         const int pool = (int)(ent >> 30);
         const int kn = k + WAVES;
         auto next = [&](int part) {
             if (kn < n_ent) issue(kn, part);
         };
         if (pool == 0)
-            attend_block<G, 8>(stg, np, msk, tile, ptile, pack == 0, qa, qsum, scale2, st, next);
+            attend_block<G, 8>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
         else if (pool == 1)
-            attend_block<G, 4>(stg, np, msk, tile, ptile, pack == 0, qa, qsum, scale2, st, next);
+            attend_block<G, 4>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
         else
-            attend_block<G, 2>(stg, np, msk, tile, ptile, pack == 0, qa, qsum, scale2, st, next);
+            attend_block<G, 2>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
     }
     // -- merge the waves of this workgroup and write the run's partial.  Each
     //    wave publishes its row maxima, then writes its output rows already
@@ -705,8 +759,8 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     }
 }
 
-// Work items are (sequence, kv-head pack, run of E table entries), ordered
-// by sequence, pack, run, for the runs that hold entries.  The kernel is
+// Work items are (sequence, kv-head pack, run of at most E table entries),
+// ordered by sequence, run, pack, for the runs that hold entries.  The kernel is
 // persistent: gridDim.x workgroups (what fits on the GPU at once) take the
 // items round-robin, so the dispatcher never has to refill slots and no
 // workgroup is launched for a run past a sequence's end.  The item prefix
@@ -765,14 +819,15 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
         split_item<G>(c, q, ws, scale2, S, item, s_first, lds);
 }
 
-// Finalize: one workgroup per (run of E entries, sequence); workgroup x
-// also writes the output rows of heads x, x + gridDim.x, ...  Each wave
-// takes whole entries: an entry's score tiles (one per kv-head pack,
-// [head][slot]) are read with 1 KB loads, each lane summing
-// exp2(s - M_h) / L_h over its head of every pack for 4 slots, and a fixed
-// 16-lane butterfly totals the heads of each slot.
+// Finalize: one workgroup per (run, sequence); workgroup x
+// also writes the output rows of heads x, x + gridDim.x, ...  The run's
+// valid slots were stored compacted; each wave takes whole groups of 16:
+// a group's scores (one 1 KB block [head][16 slots] per kv-head pack) are
+// read with 1 KB loads, each lane summing exp2(s - M_h) / L_h over its head
+// of every pack for 4 slots, and a fixed 16-lane butterfly totals the heads
+// of each slot.
 constexpr int FT = 256;
-constexpr int FB = 4;                         // entries a wave takes per round
+constexpr int FB = 4;                         // groups a wave takes per round
 
 __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
                                                     float decay, DecodeWs ws, int S, int G, int P, int n_packs) {
@@ -785,7 +840,9 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
     if (split >= s_act && split >= Hq) return;   // no entries and no output head
     __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
     __shared__ float4 red[FT];
-    const int n_ent = split < s_act ? ws.ents[(size_t)b * S + split] : 0;
+    // valid slots of this run, and the groups of 16 they fill
+    const int n_slots = split < s_act ? ws.ents[(size_t)b * S + split] : 0;
+    const int n_ent = (n_slots + 15) >> 4;
 
     // -- global max / sum per head: tpg lanes of one wave per head, each over
     //    a stride of splits with its loads issued together, then a butterfly
@@ -828,7 +885,8 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
     }
     __syncthreads();
 
-    // -- mass (and importance) of the valid slots of this run's entries
+    // -- mass (and importance) of the valid slots of this run, 16 at a time
+    //    (a group k: lane (head lo, hi) takes slots 16 k + 4 hi .. + 3)
     const size_t ek0 = (size_t)(b * S + split) * E;
     for (int k0 = wave * FB; k0 < n_ent; k0 += (FT / 64) * FB) {
         int4 pos[FB];
@@ -838,6 +896,12 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
             const int k = k0 + e;
             pos[e] = k < n_ent ? reinterpret_cast<const int4 *>(ws.spos + (ek0 + k) * 16)[hi]
                                : make_int4(-1, -1, -1, -1);
+            // slots past the run's last are stale
+            const int c0 = 16 * k + 4 * hi;
+            if (c0 + 0 >= n_slots) pos[e].x = -1;
+            if (c0 + 1 >= n_slots) pos[e].y = -1;
+            if (c0 + 2 >= n_slots) pos[e].z = -1;
+            if (c0 + 3 >= n_slots) pos[e].w = -1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
         }
@@ -850,7 +914,7 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
                 for (int q = 0; q < 2; ++q) {
                     const int k = k0 + e, p = p0 + q;
                     t[e][q] = k < n_ent && p < n_packs
-                                  ? reinterpret_cast<const float4 *>(ws.score + ((ek0 + k) * n_packs + p) * 256)[lo * 4 + hi]
+                                  ? reinterpret_cast<const float4 *>(ws.score + ((ek0 * n_packs + (size_t)p * E) + k) * 256)[lo * 4 + hi]
                                   : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
                 }
 #pragma unroll

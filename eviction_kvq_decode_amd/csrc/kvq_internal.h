@@ -7,8 +7,9 @@
 
 namespace kvq {
 
-// Decode split-K: a split covers this many table entries of one sequence
-// and kv-head pack.
+// Decode split-K: a split covers at most this many table entries of one
+// sequence and kv-head pack (a sequence with nr splits gives split j the
+// entries j, j + nr, j + 2 nr, ...).
 #ifndef KVQ_ENTRIES_PER_SPLIT
 #define KVQ_ENTRIES_PER_SPLIT 64
 #endif
@@ -46,9 +47,12 @@ inline int decode_n_packs(const kvq_cache &c) {
 struct DecodeWs {
     float *ml;         // [B][Hq][S][2]  split max (base-2 units), split sum
     float *o;          // [B][Hq][S][128] split output, unnormalised
-    int32_t *ents;     // [B][S] non-empty table entries of the split
-    int32_t *spos;     // [B][S][E][16] slot positions of those entries, -1 if cleared
-    float *score;      // [B][S][E][n_packs][16 heads][16 slots] base-2 scaled scores
+    // The valid slots of a split, in table and slot order, are numbered
+    // 0 .. n-1 (n <= 16 E); their scores and positions are stored compacted.
+    int32_t *ents;     // [B][S] valid slots n of the split
+    int32_t *spos;     // [B][S][16 E] position of valid slot c
+    float *score;      // [B][S][n_packs][E][16 heads][16] base-2 scaled score of
+                       // valid slot c at [c / 16][head][c % 16]
     static size_t bytes(const kvq_cache &c) {
         const size_t S = n_splits(c), E = ENTRIES_PER_SPLIT;
         return align256(8L * c.B * c.Hq * S) + align256(512L * c.B * c.Hq * S) + align256(4L * c.B * S) +
