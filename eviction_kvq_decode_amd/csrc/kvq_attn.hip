@@ -819,25 +819,31 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
         split_item<G>(c, q, ws, scale2, S, item, s_first, lds);
 }
 
-// Finalize: one workgroup per (run, sequence); workgroup x
-// also writes the output rows of heads x, x + gridDim.x, ...  The run's
-// valid slots were stored compacted; each wave takes whole groups of 16:
+// Finalize: FPART workgroups per (run, sequence), workgroup x taking run
+// x / FPART; workgroup x also writes the output rows of heads x, x +
+// gridDim.x, ...  A run's valid slots were stored compacted, in groups of
+// 16; the run's workgroups and their waves take whole groups in turn:
 // a group's scores (one 1 KB block [head][16 slots] per kv-head pack) are
 // read with 1 KB loads, each lane summing exp2(s - M_h) / L_h over its head
 // of every pack for 4 slots, and a fixed 16-lane butterfly totals the heads
 // of each slot.
 constexpr int FT = 256;
 constexpr int FB = 4;                         // groups a wave takes per round
+#ifndef KVQ_FPART
+#define KVQ_FPART 2
+#endif
+constexpr int FPART = KVQ_FPART;              // workgroups sharing one run's groups
 
 __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
                                                     float decay, DecodeWs ws, int S, int G, int P, int n_packs) {
-    const int split = blockIdx.x, b = blockIdx.y, X = gridDim.x;
+    const int x = blockIdx.x, b = blockIdx.y, X = gridDim.x;
+    const int split = x / FPART, part = x % FPART;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lo = lane & 15, hi = lane >> 4;
     const int nb = c.n_blocks[b];
     const int s_act = (nb + E - 1) / E;
     const int Hq = c.Hq;
-    if (split >= s_act && split >= Hq) return;   // no entries and no output head
+    if (split >= s_act && x >= Hq) return;   // no slots and no output head
     __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
     __shared__ float4 red[FT];
     // valid slots of this run, and the groups of 16 they fill
@@ -888,7 +894,7 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
     // -- mass (and importance) of the valid slots of this run, 16 at a time
     //    (a group k: lane (head lo, hi) takes slots 16 k + 4 hi .. + 3)
     const size_t ek0 = (size_t)(b * S + split) * E;
-    for (int k0 = wave * FB; k0 < n_ent; k0 += (FT / 64) * FB) {
+    for (int k0 = (part * (FT / 64) + wave) * FB; k0 < n_ent; k0 += FPART * (FT / 64) * FB) {
         int4 pos[FB];
         float acc[FB][4];
 #pragma unroll
@@ -959,7 +965,7 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
 
     // -- output rows of the heads this workgroup owns: 32 channel quads x
     //    8 split groups, merged in a fixed order
-    for (int h = split; h < Hq; h += X) {
+    for (int h = x; h < Hq; h += X) {
         const int c4 = tid & 31, sg = tid >> 5;
         const float *ml = ws.ml + ((size_t)b * Hq + h) * S * 2;
         const float4 *o = reinterpret_cast<const float4 *>(ws.o + ((size_t)b * Hq + h) * S * HD);
@@ -1045,7 +1051,7 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
     }
     {
         const int P = decode_pack(G);
-        hipLaunchKernelGGL(attn_finalize, dim3(S > c.Hq ? S : c.Hq, c.B), dim3(FT), 0, s, c, out, mass, importance,
+        hipLaunchKernelGGL(attn_finalize, dim3(S * FPART > c.Hq ? S * FPART : c.Hq, c.B), dim3(FT), 0, s, c, out, mass, importance,
                            decay, ws, S, G, P, decode_n_packs(c));
     }
     return hipGetLastError() == hipSuccess;
