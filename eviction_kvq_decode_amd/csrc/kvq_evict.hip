@@ -7,11 +7,12 @@
 // bytes never move; blocks that become empty leave the table and go back to
 // their pool's free list for in-place reuse.
 //
-// evict_select: one 1024-thread workgroup per sequence.  Candidate keys
-//   (order-preserving importance bits, then inverted position, so ties go to
-//   the lower position) are radix-selected for the k-th largest; losers'
-//   mask bits are cleared; the table row is compacted in order with a
-//   ballot prefix scan; freed entries are listed in table order.
+// evict_select: one 1024-thread workgroup per sequence, one thread per slot
+//   in each pass.  Candidate keys (order-preserving importance bits, then
+//   inverted position, so ties go to the lower position) are radix-selected
+//   for the k-th largest; losers' mask bits are cleared; the table row is
+//   compacted in order with a ballot prefix scan; freed entries are listed
+//   in table order.
 // evict_push: one workgroup per sequence pushes its freed ids at offsets
 //   ranked across sequences in batch order.
 #include <limits.h>
@@ -25,6 +26,9 @@ namespace {
 
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_UNROLL = 16;  // slots a thread takes per batch
+constexpr int RADIX_BITS = 11;  // digit width of the radix select
+constexpr int RADIX = 1 << RADIX_BITS;
 
 __device__ inline uint32_t order_bits(float f) {
     uint32_t u = __float_as_uint(f);
@@ -59,67 +63,119 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const f
                                                             const int32_t *keep_k, int q_window,
                                                             int recent_window, EvictWs ws) {
     const int b = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
     if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
     const int nb = c.n_blocks[b];
+    const int nslot = nb * BLK;
     const int lo = q_window, hi = c.seq_len[b] - recent_window;
     uint32_t *row = c.table + (size_t)b * c.max_blocks;
     const float *imp = importance + (size_t)b * c.n_cap;
-    uint64_t *cand = ws.cand + (size_t)b * c.max_blocks * BLK;
+    uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
 
-    __shared__ int n_cand;
-    __shared__ uint32_t hist[256];
-    __shared__ int s_digit, s_cum;
+    __shared__ uint32_t hist[RADIX];
+    __shared__ int s_digit, s_cum, s_ncand;
     __shared__ int wave_tot[SEL_WAVES];
     __shared__ int pool_cnt[4];
-    if (tid == 0) n_cand = 0;
+    if (tid == 0) s_ncand = 0;
     if (tid < 4) pool_cnt[tid] = 0;
     __syncthreads();
 
-    // 1. candidate keys (order of the list does not matter)
-    for (int e = tid; e < nb; e += SEL_THREADS) {
-        const uint32_t ent = row[e];
-        const int pool = (int)(ent >> 30);
-        const uint32_t id = ent & 0x3fffffffu;
-        const uint32_t m = c.mask[pool][id];
-        const int *pp = c.pos[pool] + (size_t)id * BLK;
-        for (int s = 0; s < BLK; ++s) {
-            if (!((m >> s) & 1)) continue;
-            const int p = pp[s];
-            if (p < lo || p >= hi) continue;
-            const int at = atomicAdd(&n_cand, 1);
-            cand[at] = sel_key(imp[p], p);
+    // 1. one word per slot, thread per slot (slot s of entry e at 16 e + s):
+    //    0 for a cleared slot, 1 for a valid slot in a window, else the
+    //    candidate's key (a finite importance gives a key >= 2^55).
+    //    SEL_UNROLL slots per thread and batch; the entry, then its mask and
+    //    positions, then the importance, each level's loads issued together.
+    int my_cand = 0;
+    for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
+        uint32_t ent[SEL_UNROLL], m[SEL_UNROLL];
+        int p[SEL_UNROLL];
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u) {
+            const int i = i0 + u * SEL_THREADS + tid;
+            ent[u] = i < nslot ? row[i >> 4] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u) {
+            const int i = i0 + u * SEL_THREADS + tid;
+            m[u] = i < nslot ? c.mask[ent[u] >> 30][ent[u] & 0x3fffffffu] : 0u;
+            p[u] = i < nslot ? c.pos[ent[u] >> 30][(size_t)(ent[u] & 0x3fffffffu) * BLK + (i & 15)] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u) {
+            const int i = i0 + u * SEL_THREADS + tid;
+            uint64_t kk = 0;
+            if ((m[u] >> (i & 15)) & 1u) {
+                kk = 1;
+                if (p[u] >= lo && p[u] < hi) {
+                    kk = sel_key(imp[p[u]], p[u]);
+                    ++my_cand;
+                }
+            }
+            if (i < nslot) key[i] = kk;
         }
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) my_cand += __shfl_xor(my_cand, off);
+    if (lane == 0) atomicAdd(&s_ncand, my_cand);
     __syncthreads();
-    const int n = n_cand;
+    const int n = s_ncand;
     const int k = max(keep_k[b], 0);
     const bool evicting = n > k;
 
-    // 2. radix-select the k-th largest key, 8 bits at a time, stopping as
-    //    soon as the boundary digit's whole bin is kept.
+    // 2. radix-select the k-th largest key, RADIX_BITS at a time from the
+    //    top (the last digit is narrower), stopping as soon as the boundary
+    //    digit's whole bin is kept.  Wide digits spread the keys, whose top
+    //    bits (sign and exponent of the importance) take few values, over
+    //    many bins: fewer passes and fewer same-bin atomics.
     uint64_t thr = 0;
     int thr_shift = 0;
     if (evicting && k > 0) {
         uint64_t prefix = 0;
         uint32_t need = (uint32_t)k;
-        for (int shift = 56;; shift -= 8) {
-            for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
+        for (int top = 64;;) {
+            const int width = top < RADIX_BITS ? top : RADIX_BITS;
+            const int shift = top - width;
+            const uint32_t dmask = (1u << width) - 1u;
+            for (int i = tid; i < RADIX; i += SEL_THREADS) hist[i] = 0;
             __syncthreads();
-            const uint64_t hmask = shift == 56 ? 0ull : (~0ull << (shift + 8));
-            for (int i = tid; i < n; i += SEL_THREADS) {
-                const uint64_t key = cand[i];
-                if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 255], 1u);
+            const uint64_t hmask = top == 64 ? 0ull : (~0ull << top);
+            for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
+                uint64_t kk[SEL_UNROLL];
+#pragma unroll
+                for (int u = 0; u < SEL_UNROLL; ++u) {
+                    const int i = i0 + u * SEL_THREADS + tid;
+                    kk[u] = i < nslot ? key[i] : 0ull;
+                }
+#pragma unroll
+                for (int u = 0; u < SEL_UNROLL; ++u)
+                    if (kk[u] > 1 && (kk[u] & hmask) == (prefix & hmask))
+                        atomicAdd(&hist[(uint32_t)(kk[u] >> shift) & dmask], 1u);
             }
             __syncthreads();
-            if (tid == 0) {
-                uint32_t cum = 0;
-                int dgt = 255;
-                for (; dgt > 0; --dgt) {
-                    if (cum + hist[dgt] >= need) break;
-                    cum += hist[dgt];
+            if (wv == 0) {
+                // bins from the top: lane l holds RADIX-1 - BPL l - j, j < BPL
+                constexpr int BPL = RADIX / 64;
+                uint32_t sum = 0;
+                for (int j = 0; j < BPL; ++j) sum += hist[RADIX - 1 - BPL * lane - j];
+                uint32_t incl = sum;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t y = __shfl_up(incl, off);
+                    if (lane >= off) incl += y;
                 }
-                s_digit = dgt;
-                s_cum = (int)cum;
+                const uint32_t excl = incl - sum;
+                // the boundary lane: its bins reach need, the bins above do not
+                if (excl < need && incl >= need) {
+                    uint32_t cum = excl;
+                    int j = 0;
+                    for (; j < BPL - 1; ++j) {
+                        const uint32_t h = hist[RADIX - 1 - BPL * lane - j];
+                        if (cum + h >= need) break;
+                        cum += h;
+                    }
+                    s_digit = RADIX - 1 - BPL * lane - j;
+                    s_cum = (int)cum;
+                }
             }
             __syncthreads();
             const int dgt = s_digit;
@@ -132,10 +188,40 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const f
                 thr_shift = shift;
                 break;
             }
+            top = shift;
         }
     }
 
-    // 3. clear losers, compact the table row, list freed entries
+    // 3a. clear losers, thread per slot: 16-lane ballots give each entry's
+    //     old and new masks; the entry's first slot's lane stores the new
+    //     mask if it changed, and parks it in that slot's word for the
+    //     compaction
+#pragma unroll 1
+    for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
+        uint32_t ent[SEL_UNROLL];
+        uint64_t kk[SEL_UNROLL];
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u) {
+            const int i = i0 + u * SEL_THREADS + tid;
+            ent[u] = i < nslot ? row[i >> 4] : 0u;
+            kk[u] = i < nslot ? key[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u) {
+            const int i = i0 + u * SEL_THREADS + tid;
+            bool bit = kk[u] != 0;
+            if (evicting && kk[u] > 1 && !(k > 0 && (kk[u] >> thr_shift) >= (thr >> thr_shift))) bit = false;
+            const uint32_t oldm = (uint32_t)(__ballot(kk[u] != 0) >> (lane & 48)) & 0xffffu;
+            const uint32_t newm = (uint32_t)(__ballot(bit) >> (lane & 48)) & 0xffffu;
+            if (i < nslot && (i & 15) == 0) {
+                if (newm != oldm) c.mask[ent[u] >> 30][ent[u] & 0x3fffffffu] = (uint16_t)newm;
+                key[i] = newm;
+            }
+        }
+    }
+    __syncthreads();
+
+    // 3b. compact the table row in order, list freed entries (thread per entry)
     int kept_base = 0, freed_base = 0;
     uint32_t *freed = ws.freed + (size_t)b * c.max_blocks;
     for (int c0 = 0; c0 < nb; c0 += SEL_THREADS) {
@@ -144,21 +230,7 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const f
         uint32_t ent = 0, newm = 0;
         if (has) {
             ent = row[e];
-            const int pool = (int)(ent >> 30);
-            const uint32_t id = ent & 0x3fffffffu;
-            const uint32_t m = c.mask[pool][id];
-            newm = m;
-            if (evicting) {
-                const int *pp = c.pos[pool] + (size_t)id * BLK;
-                for (int s = 0; s < BLK; ++s) {
-                    if (!((m >> s) & 1)) continue;
-                    const int p = pp[s];
-                    if (p < lo || p >= hi) continue;
-                    const bool keep = k > 0 && (sel_key(imp[p], p) >> thr_shift) >= (thr >> thr_shift);
-                    if (!keep) newm &= ~(1u << s);
-                }
-                if (newm != m) c.mask[pool][id] = (uint16_t)newm;
-            }
+            newm = (uint32_t)key[(size_t)e * BLK];
         }
         int nkept, nfreed;
         const int kr = block_prefix(has && newm != 0, wave_tot, nkept);
