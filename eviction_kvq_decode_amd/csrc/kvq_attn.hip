@@ -147,8 +147,8 @@ __device__ inline float hi_h(uint32_t x) { return h2f((uint16_t)(x >> 16)); }
 struct WaveState {
     float m;         // running max of head rho (base-2 scaled scores)
     float l;         // this lane's share of the running sum
-    float z[NGRP];   // this lane's share of sum p * v_zero per group
-    floatx4 o[8];    // sum p * v_scale * mult * code, per 16-channel tile
+    float z[NGRP];   // this lane's share of sum p * v_zero - B * P' / mult per group
+    floatx4 o[8];    // sum P' * (B + code), P' = p * v_scale * mult, per 16-channel tile
     float mult;      // power-of-two headroom factor applied to P'
 };
 
@@ -912,7 +912,7 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
             for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
         }
         for (int p0 = 0; p0 < n_packs; p0 += 2) {
-            // two packs' tiles of the round's entries, loads issued together
+            // two packs' scores of the round's groups, loads issued together
             float4 t[FB][2];
 #pragma unroll
             for (int e = 0; e < FB; ++e)
