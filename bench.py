@@ -16,6 +16,9 @@ bounded sample of the same workload.
 --workload budgeted (or another workload with an eviction budget) times the
 eviction step instead: decode with importance accumulation + windowed top-k
 evict, and reports the evict call beside the decode roofline.
+--workload ct_loop runs the continuous-thinking loop (a long generation
+under a cache budget, pruned every P tokens) and reports time per step and
+the cache footprint.
 """
 from __future__ import annotations
 
@@ -236,6 +239,96 @@ def evict_bench(args, w):
     print(json.dumps(result), flush=True)
 
 
+def ct_bench(args, w):
+    """Continuous-thinking loop: every step appends one token per sequence
+    and decodes (importance accumulated), and every `period` steps the cache
+    is pruned to the budget (ct_loop.ContinuousThinking).  The first --warmup
+    steps are untimed; all remaining steps of the generation are timed, each
+    with HIP events around its calls.  Reports per-step GPU time (the time
+    per output token of one layer), the prune steps apart, and the cache
+    footprint: table blocks and valid tokens before and after the loop."""
+    import torch
+
+    from eviction_kvq_decode_amd import workloads as wl
+    from eviction_kvq_decode_amd.ct_loop import ContinuousThinking
+
+    t0 = time.time()
+    n0 = int(wl.seq_lengths(w).max())
+    toks = wl.lockstep_tokens(w, n0 + w.extra_steps, threads=min(16, os.cpu_count() or 1))
+    g = wl.geometry_for(w, toks.seq_tags)
+    log(f"[gen] {w.name}: tokens generated in {time.time() - t0:.1f}s; geometry {g}")
+    cache = build_gpu_cache(w, toks, g)
+    del toks
+    tags_all = wl.loop_tags(w, n0 + w.loop_steps)
+    steps = [wl.loop_step_tokens(w, s, tags_all) for s in range(w.loop_steps)]
+    K = torch.from_numpy(np.stack([x[0] for x in steps])).cuda()
+    V = torch.from_numpy(np.stack([x[1] for x in steps])).cuda()
+    T = torch.from_numpy(np.stack([x[2] for x in steps])).cuda()
+    Q = torch.from_numpy(np.stack([wl.queries(w, s) for s in range(64)])).cuda()
+    del steps
+    B = w.B
+    out = torch.empty((B, w.Hq, 128), device="cuda")
+    mass = torch.empty((B, g.n_cap), device="cuda")
+    st0 = cache.state_numpy()
+    ct = ContinuousThinking(cache, w.keep, w.period, w.q_window, w.recent_window, w.decay)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(w.loop_steps)]
+    pruned = np.zeros(w.loop_steps, dtype=bool)
+    torch.cuda.synchronize()
+    for s in range(w.loop_steps):
+        ev[s][0].record()
+        pruned[s] = ct.step(K[s], V[s], T[s], Q[s % 64], out, mass)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    if cache.status != 0:
+        raise RuntimeError(f"status {cache.status} after the loop")
+    ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(w.loop_steps)])[args.warmup:]
+    pr = pruned[args.warmup:]
+    st1 = cache.state_numpy()
+
+    def footprint(st):
+        blocks = int(st["n_blocks"].sum())
+        valid = sum(bin(int(m)).count("1") for p in range(3)
+                    for m in st[f"mask{p}"][st[f"mask{p}"] != 0])
+        return blocks, valid
+
+    b0, v0 = footprint(st0)
+    b1, v1 = footprint(st1)
+    us = ms * 1e3
+    log(f"[gpu] {len(us)} timed steps: {us.mean():.1f} us/step (p50 {np.median(us):.1f}, "
+        f"p90 {np.quantile(us, 0.9):.1f}); prune steps {us[pr].mean():.1f} us, others "
+        f"{us[~pr].mean():.1f} us; table blocks {b0} -> {b1}, valid tokens {v0} -> {v1}")
+    result = {
+        "metric": METRIC,
+        "value": B / (ms.mean() * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": int(len(ms)),
+        "warmup": args.warmup,
+        "ms_per_step": float(ms.mean()),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, {n0} cached tokens/seq, "
+                               f"{w.loop_steps} generated; budget {w.keep} + windows "
+                               f"{w.q_window}/{w.recent_window}, pruned every {w.period} tokens; "
+                               f"step = append + decode (+ evict every {w.period})",
+                   "global_batch": B, "seq_len": n0 + w.loop_steps},
+        "roofline": None,
+        "ct": {"us_per_step_p50": float(np.median(us)), "us_per_step_p90": float(np.quantile(us, 0.9)),
+               "us_prune_step": float(us[pr].mean()) if pr.any() else None,
+               "us_other_step": float(us[~pr].mean()),
+               "table_blocks_before": b0, "table_blocks_after": b1,
+               "valid_tokens_before": v0, "valid_tokens_after": v1,
+               "tokens_appended": B * w.loop_steps,
+               "slot_fill_after": v1 / (16.0 * b1) if b1 else None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +355,9 @@ def main():
     kvq.lib()
     torch.cuda.set_device(0)
     w = wl.WORKLOADS[args.workload]
+    if w.period:
+        ct_bench(args, w)
+        return
     if w.keep or w.keep_frac:
         evict_bench(args, w)
         return

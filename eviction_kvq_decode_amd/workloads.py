@@ -59,6 +59,8 @@ class Workload:
     q_window: int = 0
     recent_window: int = 0
     extra_steps: int = 64           # head-room for extra appended tokens
+    period: int = 0                 # continuous-thinking loop: evict every `period` appends
+    loop_steps: int = 0             # and run this many append+decode steps
 
     @property
     def G(self) -> int:
@@ -76,6 +78,12 @@ WORKLOADS = {
     "ragged": Workload("ragged", 4, B=128, Hq=64, Hkv=8, n_min=1024, n_max=65536,
                        tag_p=(0.214, 0.286, 0.5), importance=True, keep_frac=0.05,
                        keep_min=256),
+    # continuous thinking: a long generation under a fixed cache budget, the
+    # cache pruned every `period` new tokens, so it oscillates between the
+    # budget and budget + period ("TAM", periodic compaction)
+    "ct_loop": Workload("ct_loop", 5, B=32, Hq=32, Hkv=8, n_min=4096, n_max=4096,
+                        importance=True, keep=2048, q_window=64, recent_window=128,
+                        period=256, loop_steps=4096, extra_steps=4096 + 64),
 }
 
 
@@ -144,6 +152,21 @@ def step_tokens(w: Workload, step: int):
     v = rng.standard_normal((w.B, w.Hkv, HD), dtype=np.float32)
     tags = rng.choice(3, size=w.B, p=np.asarray(w.tag_p) / sum(w.tag_p)).astype(np.uint8)
     return k.astype(np.float16), v.astype(np.float16), tags
+
+
+def loop_tags(w: Workload, n_total: int) -> np.ndarray:
+    """Thought tags [B][n_total] of a generation that continues past the
+    cached tokens: the same run process, drawn further (the first n tags of
+    sequence b are tag_runs(w, b, n))."""
+    return np.stack([tag_runs(w, b, n_total)[0] for b in range(w.B)])
+
+
+def loop_step_tokens(w: Workload, step: int, tags_all: np.ndarray):
+    """Token of loop step `step` for every sequence: k, v as step_tokens,
+    with the tag at position (cached length + step) of the run stream."""
+    k, v, _ = step_tokens(w, step)
+    n = seq_lengths(w)
+    return k, v, np.ascontiguousarray(tags_all[np.arange(w.B), n + step]).astype(np.uint8)
 
 
 def keep_plan(w: Workload, b: int, tags: np.ndarray, run_id: np.ndarray) -> np.ndarray:
