@@ -67,9 +67,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_plan(kvq_cache c, const u
     }
     if (tid == 0) {
         if (first != INT_MAX) {
-            const uint16_t m = mask[row[first] & 0x3fffffffu];
+            const uint32_t ent = row[first];
+            const uint16_t m = mask[ent & 0x3fffffffu];
             ws.need[b] = -1;
-            ws.entry[b] = first;
+            ws.entry[b] = (int32_t)ent;
             ws.slot[b] = __builtin_ctz(~(uint32_t)m);
         } else if (nb >= c.max_blocks) {
             ws.need[b] = -2;
@@ -84,9 +85,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_plan(kvq_cache c, const u
 // (lane l owns channels 2l, 2l+1; 16 lanes per 32-channel group).
 // Matches the TBQ reading: zero = min, scale = least fp16 >= (max-min)/lv,
 // code = clamp(rint((x - zero)/scale)), all in fp32.
-__device__ inline void quantise_pair(const uint16_t *row, int bits, int lane, uint32_t &c0,
-                                     uint32_t &c1, uint32_t &scale_zero) {
-    const uint32_t two = reinterpret_cast<const uint32_t *>(row)[lane];
+__device__ inline void quantise_pair(uint32_t two, int bits, uint32_t &c0, uint32_t &c1,
+                                     uint32_t &scale_zero) {
     const float x0 = h2f((uint16_t)(two & 0xffff)), x1 = h2f((uint16_t)(two >> 16));
     float mn = fminf(x0, x1), mx = fmaxf(x0, x1);
 #pragma unroll
@@ -115,6 +115,11 @@ __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *
                                                    const uint16_t *v_new, AppendWs ws) {
     const int b = blockIdx.x / c.Hkv, h = blockIdx.x % c.Hkv;
     const int lane = threadIdx.x;
+    // this lane's two channels of the new K and V rows, loaded before the
+    // plan so that the loads overlap the dependent plan/table reads
+    const size_t row_off = ((size_t)b * c.Hkv + h) * HD;
+    const uint32_t k_two = reinterpret_cast<const uint32_t *>(k_new + row_off)[lane];
+    const uint32_t v_two = reinterpret_cast<const uint32_t *>(v_new + row_off)[lane];
     if (blockIdx.x == 0 && lane < 3) {
         int cnt = 0;
         for (int bb = 0; bb < c.B; ++bb) cnt += ws.need[bb] == lane;
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *
     uint32_t id;
     bool fresh = false;
     if (need == -1) {
-        const uint32_t ent = c.table[(size_t)b * c.max_blocks + ws.entry[b]];
+        const uint32_t ent = (uint32_t)ws.entry[b];
         pool = (int)(ent >> 30);
         id = ent & 0x3fffffffu;
         slot = ws.slot[b];
@@ -150,10 +155,9 @@ __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *
 
     __shared__ uint8_t kcode[HD];  // by K-row code index
     __shared__ uint8_t vcode[HD];  // by channel
-    const size_t row_off = ((size_t)b * c.Hkv + h) * HD;
     uint32_t k0, k1, ksz, v0, v1, vsz;
-    quantise_pair(k_new + row_off, bits, lane, k0, k1, ksz);
-    quantise_pair(v_new + row_off, bits, lane, v0, v1, vsz);
+    quantise_pair(k_two, bits, k0, k1, ksz);
+    quantise_pair(v_two, bits, v0, v1, vsz);
     kcode[k_row_index(bits, 2 * lane)] = (uint8_t)k0;
     kcode[k_row_index(bits, 2 * lane + 1)] = (uint8_t)k1;
     vcode[2 * lane] = (uint8_t)v0;

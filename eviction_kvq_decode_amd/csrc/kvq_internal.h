@@ -24,7 +24,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Workspace carve-up.  Calls are stream-ordered, so they share one buffer.
 struct AppendWs {
     int32_t *need;     // [B] -2 nothing, -1 reuse slot, p >= 0 pop pool p
-    int32_t *entry;    // [B] table index of the reused block
+    int32_t *entry;    // [B] table entry (pool << 30 | id) of the reused block
     int32_t *slot;     // [B]
     int32_t *top;      // [4] free_top before the call
     static size_t bytes(const kvq_cache &c) { return align256(16 * 4) + 3 * align256(4L * c.B); }
