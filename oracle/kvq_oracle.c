@@ -546,6 +546,109 @@ void orc_evict(orc_cache *c, const float *importance, const int32_t *keep_k,
     }
 }
 
+/* Table compaction after mask changes: entries with an empty mask leave
+ * the row (order kept) and their ids go on their pool's free stack. */
+static void compact_row(orc_cache *c, int b)
+{
+    uint32_t *row = c->table + (long)b * c->max_blocks;
+    int kept = 0;
+    for (int e = 0; e < c->n_blocks[b]; ++e) {
+        int pool = (int)(row[e] >> 30);
+        uint32_t id = row[e] & 0x3fffffffu;
+        if (c->mask[pool][id] == 0)
+            c->free_ids[pool][c->free_top[pool]++] = id;
+        else
+            row[kept++] = row[e];
+    }
+    c->n_blocks[b] = kept;
+}
+
+static int pos_cmp(const void *a, const void *b)
+{
+    const cand *x = a, *y = b;
+    return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+/*
+ * Thought-adaptive eviction ("ThinKV", Methodology, think-before-evict):
+ * once a Transition thought starts, earlier Reasoning / Execution segments
+ * are pruned at segment granularity on an annealing schedule, and a small
+ * safety net of every earlier Transition segment stays.
+ *
+ * Per sequence: the candidates are the valid slots with q_window <= pos <
+ * seq_len - recent_window.  Taken in position order they form segments,
+ * maximal runs of one thought type.  A segment followed by k Transition
+ * segments keeps everything if k == 0; otherwise it keeps
+ * max(r_min, r0 >> (k - 1)) slots if it is a Reasoning or Execution segment
+ * (r0 after the first later Transition, r0 / 2 after the second, ...) and
+ * t_keep slots if it is a Transition segment.  A segment keeps its best
+ * slots: larger importance first, then lower position.  Then the table is
+ * compacted as in orc_evict.
+ */
+void orc_evict_tbe(orc_cache *c, const float *importance, int r0, int r_min, int t_keep,
+                   int q_window, int recent_window)
+{
+    for (int b = 0; b < c->B; ++b) {
+        uint32_t *row = c->table + (long)b * c->max_blocks;
+        const float *imp = importance + (long)b * c->n_cap;
+        int lo = q_window, hi = c->seq_len[b] - recent_window;
+        long cap = (long)c->n_blocks[b] * BLK + 1;
+        cand *cs = malloc(sizeof(cand) * cap);
+        int n = 0;
+        for (int e = 0; e < c->n_blocks[b]; ++e) {
+            int pool = (int)(row[e] >> 30);
+            uint32_t id = row[e] & 0x3fffffffu;
+            uint16_t m = c->mask[pool][id];
+            for (int s = 0; s < BLK; ++s) {
+                if (!((m >> s) & 1))
+                    continue;
+                int p = c->pos[pool][id * BLK + s];
+                if (p < lo || p >= hi)
+                    continue;
+                cs[n].imp = imp[p];
+                cs[n].pos = p;
+                cs[n].pool = pool;
+                cs[n].id = id;
+                cs[n].slot = s;
+                ++n;
+            }
+        }
+        qsort(cs, n, sizeof(cand), pos_cmp);
+        /* segments: [start, end) runs of one type; count the Transition
+         * segments after each one from the end */
+        int *seg_start = malloc(sizeof(int) * (n + 1));
+        int n_seg = 0;
+        for (int i = 0; i < n; ++i)
+            if (i == 0 || cs[i].pool != cs[i - 1].pool)
+                seg_start[n_seg++] = i;
+        seg_start[n_seg] = n;
+        int later_t = 0;
+        for (int sg = n_seg - 1; sg >= 0; --sg) {
+            int a = seg_start[sg], e = seg_start[sg + 1];
+            int is_t = cs[a].pool == 2;
+            if (later_t > 0) {
+                long keep;
+                if (is_t) {
+                    keep = t_keep;
+                } else {
+                    long r = later_t - 1 >= 31 ? 0 : ((long)r0 >> (later_t - 1));
+                    keep = r > r_min ? r : r_min;
+                }
+                if (keep < 0) keep = 0;
+                if (keep < e - a) {
+                    qsort(cs + a, e - a, sizeof(cand), cand_cmp);
+                    for (int i = a + (int)keep; i < e; ++i)
+                        c->mask[cs[i].pool][cs[i].id] &= (uint16_t)~(1u << cs[i].slot);
+                }
+            }
+            later_t += is_t;
+        }
+        free(seg_start);
+        free(cs);
+        compact_row(c, b);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Array forms of the scalar routines above, for the test suite         */
 /* ------------------------------------------------------------------ */

@@ -69,6 +69,8 @@ def lib():
         L.orc_decode.argtypes = [ctypes.POINTER(_Cache), P, ctypes.c_double, P, P, P, P,
                                  ctypes.c_double, P]
         L.orc_evict.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int, ctypes.c_int]
+        L.orc_evict_tbe.argtypes = [ctypes.POINTER(_Cache), P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int]
         L.orc_dequant_slot.argtypes = [ctypes.POINTER(_Cache), ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_int, ctypes.c_int, P, P]
         L.orc_slot_codes.argtypes = [ctypes.POINTER(_Cache), ctypes.c_int, ctypes.c_uint32,
@@ -186,6 +188,15 @@ class OracleCache:
         kk = np.ascontiguousarray(keep_k, dtype=np.int32)
         assert kk.shape == (g.B,)
         lib().orc_evict(self._c(), _p(imp), _p(kk), int(q_window), int(recent_window))
+
+    def evict_tbe(self, importance: np.ndarray, r0: int, r_min: int, t_keep: int, q_window: int,
+                  recent_window: int):
+        """Thought-adaptive eviction ("ThinKV", think-before-evict); see
+        orc_evict_tbe in kvq_oracle.c."""
+        g = self.g
+        imp = np.ascontiguousarray(importance, dtype=np.float32).reshape(g.B, g.n_cap)
+        lib().orc_evict_tbe(self._c(), _p(imp), int(r0), int(r_min), int(t_keep), int(q_window),
+                            int(recent_window))
 
     # -- inspection -----------------------------------------------------
     @property
