@@ -74,3 +74,17 @@ extern "C" kvq_status kvq_evict_topk(const kvq_cache *c, const float *importance
     return kvq::launch_evict(*c, importance, keep_k, q_window, recent_window, ws, stream) ? KVQ_OK
                                                                                            : KVQ_EHIP;
 }
+
+extern "C" kvq_status kvq_evict_tbe(const kvq_cache *c, const float *importance, int32_t r0,
+                                    int32_t r_min, int32_t t_keep, int32_t q_window,
+                                    int32_t recent_window, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (!importance || r0 < 0 || r_min < 0 || t_keep < 0 || q_window < 0 || recent_window < 0)
+        return KVQ_EINVAL;
+    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    return kvq::launch_evict_tbe(*c, importance, r0, r_min, t_keep, q_window, recent_window, ws, stream)
+               ? KVQ_OK
+               : KVQ_EHIP;
+}

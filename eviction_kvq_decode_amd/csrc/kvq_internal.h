@@ -70,20 +70,37 @@ struct DecodeWs {
 };
 
 struct EvictWs {
-    uint64_t *cand;    // [B][max_blocks*16] selection keys
+    uint64_t *cand;    // [B][max_blocks*16] selection keys, one word per slot
     uint32_t *freed;   // [B][max_blocks] freed table entries, table order
     int32_t *nfreed;   // [B][4] freed per pool
     int32_t *top;      // [4] free_top before the call
+    // segment-granular eviction only: candidates in position order
+    int32_t *pmap;     // [B][n_cap] slot of the candidate at a position, or -1
+    int32_t *ord;      // [B][max_blocks*16] slots of the candidates, by position
+    uint64_t *okey;    // [B][max_blocks*16] their keys, same order
+    int32_t *segof;    // [B][max_blocks*16] segment of each candidate, then its verdict
+    int32_t *segstart; // [B][max_blocks*16 + 1] first candidate of each segment
+    int32_t *segret;   // [B][max_blocks*16] thought type, then retention, of each segment
     static size_t bytes(const kvq_cache &c) {
-        return align256(8L * c.B * c.max_blocks * 16) + align256(4L * c.B * c.max_blocks) +
-               align256(16L * c.B) + align256(16);
+        const size_t ms = (size_t)c.max_blocks * 16;
+        return align256(8L * c.B * ms) + align256(4L * c.B * c.max_blocks) + align256(16L * c.B) +
+               align256(16) + align256(4L * c.B * c.n_cap) + align256(4L * c.B * ms) +
+               align256(8L * c.B * ms) + align256(4L * c.B * ms) + align256(4L * c.B * (ms + 1)) +
+               align256(4L * c.B * ms);
     }
     EvictWs(void *ws, const kvq_cache &c) {
+        const size_t ms = (size_t)c.max_blocks * 16;
         char *p = (char *)ws;
-        cand = (uint64_t *)p;  p += align256(8L * c.B * c.max_blocks * 16);
-        freed = (uint32_t *)p; p += align256(4L * c.B * c.max_blocks);
-        nfreed = (int32_t *)p; p += align256(16L * c.B);
-        top = (int32_t *)p;
+        cand = (uint64_t *)p;     p += align256(8L * c.B * ms);
+        freed = (uint32_t *)p;    p += align256(4L * c.B * c.max_blocks);
+        nfreed = (int32_t *)p;    p += align256(16L * c.B);
+        top = (int32_t *)p;       p += align256(16);
+        pmap = (int32_t *)p;      p += align256(4L * c.B * c.n_cap);
+        ord = (int32_t *)p;       p += align256(4L * c.B * ms);
+        okey = (uint64_t *)p;     p += align256(8L * c.B * ms);
+        segof = (int32_t *)p;     p += align256(4L * c.B * ms);
+        segstart = (int32_t *)p;  p += align256(4L * c.B * (ms + 1));
+        segret = (int32_t *)p;
     }
 };
 
@@ -94,5 +111,7 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
                    float decay, float sm_scale, void *ws, hipStream_t s);
 bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *keep_k, int q_window,
                   int recent_window, void *ws, hipStream_t s);
+bool launch_evict_tbe(const kvq_cache &c, const float *importance, int r0, int r_min, int t_keep,
+                      int q_window, int recent_window, void *ws, hipStream_t s);
 
 }  // namespace kvq

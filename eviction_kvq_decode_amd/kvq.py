@@ -19,7 +19,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EHIP, KVQ_ENOSPC = 0, -1, -2, -3, -4
 TAG_R, TAG_E, TAG_T, TAG_NONE = 0, 1, 2, 255
 
 EXPORTS = ("kvq_region_bytes", "kvq_workspace_bytes", "kvq_append_quantize",
-           "kvq_decode_attention", "kvq_evict_topk")
+           "kvq_decode_attention", "kvq_evict_topk", "kvq_evict_tbe")
 
 
 class KvqError(RuntimeError):
@@ -60,6 +60,9 @@ def lib():
                                            ctypes.c_size_t, P]
         L.kvq_evict_topk.restype = ctypes.c_int
         L.kvq_evict_topk.argtypes = [CS, P, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_size_t, P]
+        L.kvq_evict_tbe.restype = ctypes.c_int
+        L.kvq_evict_tbe.argtypes = [CS, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -135,6 +138,12 @@ class Cache:
         _check(lib().kvq_evict_topk(ctypes.byref(self.struct), _ptr(importance), _ptr(keep_k),
                                     int(q_window), int(recent_window), self.ws_ptr, self.ws_bytes,
                                     self._stream(stream)), "kvq_evict_topk")
+
+    def evict_tbe(self, importance, r0, r_min, t_keep, q_window, recent_window, stream=None):
+        """importance fp32 [B][n_cap]; thought-adaptive eviction by segment."""
+        _check(lib().kvq_evict_tbe(ctypes.byref(self.struct), _ptr(importance), int(r0), int(r_min),
+                                   int(t_keep), int(q_window), int(recent_window), self.ws_ptr,
+                                   self.ws_bytes, self._stream(stream)), "kvq_evict_tbe")
 
     def state_numpy(self) -> dict:
         """Host copy of every cache array (synchronises)."""

@@ -165,6 +165,29 @@ kvq_status kvq_evict_topk(const kvq_cache *cache, const float *importance, const
                           int32_t q_window, int32_t recent_window, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Thought-adaptive eviction by segment ("ThinKV", Methodology,
+ * think-before-evict): once a Transition thought starts, earlier Reasoning
+ * and Execution segments are pruned at segment granularity on an annealing
+ * schedule, and a small safety net of every earlier Transition segment stays.
+ *   importance : fp32 [B][n_cap], read at the positions of valid slots
+ *                (finite values; -0 counts as +0)
+ *   r0, r_min, t_keep : >= 0
+ * Per sequence, the valid slots with q_window <= pos < seq_len -
+ * recent_window are the candidates; the others are kept.  In position order
+ * the candidates form segments: maximal runs of one thought type.  A segment
+ * followed by k Transition segments keeps all its slots if k == 0;
+ * otherwise it keeps max(r_min, r0 >> (k - 1)) slots if it is a Reasoning or
+ * Execution segment (r0, r0 / 2, r0 / 4, ... as Transitions follow) and
+ * t_keep slots if it is a Transition segment.  A segment keeps its slots of
+ * largest importance (ties: lower position).  The rest are evicted, and the
+ * table is compacted and emptied blocks are freed as in kvq_evict_topk.
+ */
+kvq_status kvq_evict_tbe(const kvq_cache *cache, const float *importance, int32_t r0,
+                         int32_t r_min, int32_t t_keep, int32_t q_window,
+                         int32_t recent_window, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

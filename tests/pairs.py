@@ -13,6 +13,17 @@ from oracle import oracle as orc
 
 HD = 128
 BLK = 16
+# The five workload recipes at sizes the oracle finishes in seconds; each
+# spans several table splits, partial blocks of every type and, for the
+# ragged recipe, very different lengths.
+SMALL_WORKLOADS = {
+    "tiny": wl.WORKLOADS["tiny"],
+    "llama8b": wl.scaled(wl.WORKLOADS["llama8b"], B=3, n_min=1500, n_max=1500),
+    "long_evicted": wl.scaled(wl.WORKLOADS["long_evicted"], B=3, n_min=4100, n_max=4100),
+    "budgeted": wl.scaled(wl.WORKLOADS["budgeted"], B=3, n_min=2600, n_max=2600, keep=300),
+    "ragged": wl.scaled(wl.WORKLOADS["ragged"], B=5, n_min=40, n_max=5000, keep_min=24),
+}
+
 RTOL_OUT, ATOL_OUT = 2e-3, 1e-3    # attention output
 ATOL_MASS = 1e-5                   # mass and importance
 

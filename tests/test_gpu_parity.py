@@ -11,22 +11,13 @@ import numpy as np
 import pytest
 
 from eviction_kvq_decode_amd import workloads as wl
-from pairs import Pair, assert_attention_close, assert_mass_close, assert_same_cache, log
+from pairs import SMALL_WORKLOADS, Pair, assert_attention_close, assert_mass_close, assert_same_cache, log
 
 pytestmark = pytest.mark.gpu
 
 HD = 128
 
-# The five workload recipes at sizes the oracle finishes in seconds; each
-# spans several table splits, partial blocks of every type and, for the
-# ragged recipe, very different lengths.
-SMALL = {
-    "tiny": wl.WORKLOADS["tiny"],
-    "llama8b": wl.scaled(wl.WORKLOADS["llama8b"], B=3, n_min=1500, n_max=1500),
-    "long_evicted": wl.scaled(wl.WORKLOADS["long_evicted"], B=3, n_min=4100, n_max=4100),
-    "budgeted": wl.scaled(wl.WORKLOADS["budgeted"], B=3, n_min=2600, n_max=2600, keep=300),
-    "ragged": wl.scaled(wl.WORKLOADS["ragged"], B=5, n_min=40, n_max=5000, keep_min=24),
-}
+SMALL = SMALL_WORKLOADS
 
 
 @pytest.fixture(scope="module", params=list(SMALL))
