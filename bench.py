@@ -37,6 +37,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn tokens/s + effective compressed-KV GB/s (% of HBM peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0
+# segment-granular eviction timed beside top-k: retention 64 for a segment
+# with one later Transition segment, halved per further one down to 4, and
+# 8 tokens kept of each earlier Transition segment ("ThinKV", Methodology,
+# think-before-evict: 64, 32, 16, ... as its example schedule)
+TBE_PARAMS = (64, 4, 8)
 ROW_BYTES = (288, 160, 96)   # K+V codes + (scale, zero) per token per kv head, R/E/T
 
 
@@ -72,6 +77,23 @@ def build_gpu_cache(w, toks, g):
     if cache.status != 0:
         raise RuntimeError(f"cache build set status {cache.status}")
     return cache
+
+
+def valid_slot_count(cache) -> int:
+    """Valid slots of all table entries of all sequences (host copy of the
+    metadata only)."""
+    g = cache.g
+    nb = cache.t["n_blocks"].cpu().numpy()
+    table = cache.t["table"].cpu().numpy().reshape(g.B, g.max_blocks)
+    masks = [cache.t[f"mask{p}"].cpu().numpy().astype(np.int64) for p in range(3)]
+    total = 0
+    for b in range(g.B):
+        ent = table[b, : nb[b]].astype(np.int64)
+        pool, bid = ent >> 30, ent & 0x3FFFFFFF
+        for p in range(3):
+            m = masks[p][bid[pool == p]]
+            total += int(sum(bin(int(x)).count("1") for x in m))
+    return total
 
 
 def committed_traffic(workload: str):
@@ -198,14 +220,32 @@ def evict_bench(args, w):
         raise RuntimeError(f"status {cache.status} after timed steps")
     dec_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, total_steps)])
     evi_ms = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(args.warmup, total_steps)])
-    step_ms = dec_ms + evi_ms
-    achieved = kvb / (dec_ms.mean() * 1e-3) / 1e9
     # eviction: importance and position of every valid slot read once, the
     # table rewritten (4 B per entry), masks of the blocks touched (2 B)
     evb = n_valid * 8 + int(cache.t["n_blocks"].sum().item()) * 6
+    # segment-granular eviction on the same state and importance, timed alone
+    # (outside the step: an alternative to the top-k call, not a third stage)
+    tbe_ms = []
+    for s in range(total_steps):
+        for k, v in meta.items():
+            cache.t[k].copy_(v)
+        IMP.copy_(IMP0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.evict_tbe(IMP, *TBE_PARAMS, w.q_window, w.recent_window)
+        e1.record()
+        tbe_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    if cache.status != 0:
+        raise RuntimeError(f"status {cache.status} after segment eviction")
+    tbe_ms = np.array([a.elapsed_time(b) for a, b in tbe_ms[args.warmup:]])
+    tbe_kept = valid_slot_count(cache)
+    step_ms = dec_ms + evi_ms
+    achieved = kvb / (dec_ms.mean() * 1e-3) / 1e9
     ev_gbs = evb / (evi_ms.mean() * 1e-3) / 1e9
     log(f"[gpu] step {step_ms.mean() * 1e3:.1f} us: decode {dec_ms.mean() * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s of {kvb / 1e6:.1f} MB), evict {evi_ms.mean() * 1e3:.1f} us")
+        f"({achieved:.0f} GB/s of {kvb / 1e6:.1f} MB), evict {evi_ms.mean() * 1e3:.1f} us; "
+        f"segment eviction {tbe_ms.mean() * 1e3:.1f} us, {n_valid} -> {tbe_kept} valid slots")
     result = {
         "metric": METRIC,
         "value": B / (step_ms.mean() * 1e-3),
@@ -231,6 +271,10 @@ def evict_bench(args, w):
                      "avg_us": float(dec_ms.mean() * 1e3)},
         "evict": {"kernel": "kvq_evict_topk (select + push)", "avg_us": float(evi_ms.mean() * 1e3),
                   "bytes": evb, "achieved_gbs": ev_gbs, "frac": ev_gbs / HBM_PEAK_GBS},
+        "evict_tbe": {"kernel": "kvq_evict_tbe (select + push)", "avg_us": float(tbe_ms.mean() * 1e3),
+                      "r0_rmin_tkeep": list(TBE_PARAMS), "valid_before": n_valid,
+                      "valid_after": tbe_kept, "bytes": evb,
+                      "achieved_gbs": evb / (tbe_ms.mean() * 1e-3) / 1e9},
         "cpu_baseline": None,
     }
     del Q

@@ -13,7 +13,8 @@
 //   for the k-th largest; losers' mask bits are cleared; the table row is
 //   compacted in order with a ballot prefix scan; freed entries are listed
 //   in table order.
-// evict_tbe_select: thought-adaptive eviction by segment (below).
+// evict_tbe_prep / evict_tbe_drop / evict_tbe_compact: thought-adaptive
+//   eviction by segment (below).
 // evict_push: one workgroup per sequence pushes its freed ids at offsets
 //   ranked across sequences in batch order.
 #include <limits.h>
@@ -30,6 +31,12 @@ constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int SEL_UNROLL = 16;  // slots a thread takes per batch
 constexpr int RADIX_BITS = 11;  // digit width of the radix select
 constexpr int RADIX = 1 << RADIX_BITS;
+// segment eviction's selection: DROP_WGS workgroups of DROP_THREADS per
+// sequence, DROP_WAVES waves in all
+constexpr int DROP_THREADS = 256;
+constexpr int DROP_WGS = 16;
+constexpr int DROP_WAVES = DROP_WGS * DROP_THREADS / 64;
+constexpr int TBE_RUN = 16;  // chunks of 64 positions / candidates a wave takes per pass
 
 __device__ inline uint32_t order_bits(float f) {
     uint32_t u = __float_as_uint(f);
@@ -129,11 +136,12 @@ __device__ inline void clear_and_compact(const kvq_cache &c, int b, uint64_t *ke
 // 0 for a cleared slot, 1 for a valid slot outside [lo, hi), else the
 // candidate's key (a finite importance gives a key >= 2^55).  SEL_UNROLL
 // slots per thread and batch; the entry, then its mask and positions, then
-// the importance, each level's loads issued together.  pmap, if given,
-// receives the slot of each candidate position.  Returns this thread's
+// the importance, each level's loads issued together.  Without an
+// importance a candidate's word is 3.  pmap, if given, receives
+// (pool << 30) | slot for each candidate position.  Returns this thread's
 // candidate count.
 __device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const float *imp, int nslot, int lo,
-                                int hi, uint64_t *key, int32_t *pmap) {
+                                int hi, uint64_t *key, uint32_t *pmap) {
     const int tid = threadIdx.x;
     int my_cand = 0;
     for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
@@ -157,9 +165,9 @@ __device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const f
             if ((m[u] >> (i & 15)) & 1u) {
                 kk = 1;
                 if (p[u] >= lo && p[u] < hi) {
-                    kk = sel_key(imp[p[u]], p[u]);
+                    kk = imp ? sel_key(imp[p[u]], p[u]) : 3ull;
                     ++my_cand;
-                    if (pmap) pmap[p[u]] = i;
+                    if (pmap) pmap[p[u]] = (uint32_t)i | (ent[u] & 0xc0000000u);
                 }
             }
             if (i < nslot) key[i] = kk;
@@ -276,145 +284,342 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const f
                       });
 }
 
-// evict_tbe_select: thought-adaptive eviction ("ThinKV", Methodology,
-// think-before-evict), one 1024-thread workgroup per sequence.  The
-// candidates (valid slots with q_window <= pos < seq_len - recent_window),
-// taken in position order, form segments: maximal runs of one thought type.
-// A segment followed by k Transition segments keeps everything if k == 0,
-// else its best max(r_min, r0 >> (k - 1)) slots (Reasoning, Execution) or
-// t_keep slots (Transition): larger importance, then lower position.
-//   1. one word per slot (as evict_select) and a position -> slot map;
-//   2. the candidates in position order (a ballot prefix over positions);
-//   3. segment starts where the type changes (a ballot prefix);
-//   4. each segment's retention from the count of later Transition segments;
-//   5. each candidate's rank in its segment, counted until it reaches the
-//      retention;
-//   6. clear and compact as evict_select.
-__global__ __launch_bounds__(SEL_THREADS) void evict_tbe_select(kvq_cache c, const float *importance, int r0,
-                                                                int r_min, int t_keep, int q_window,
-                                                                int recent_window, EvictWs ws) {
+// Exclusive prefix sum over the waves of a value each wave holds
+// (uniform within the wave), and the total.  All threads must call it.
+__device__ inline int wave_offsets(int x, int *wave_tot, int &total) {
+    const int wv = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) wave_tot[wv] = x;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) {
+        const int v = wave_tot[w];
+        before += w < wv ? v : 0;
+        total += v;
+    }
+    __syncthreads();
+    return before;
+}
+
+// Drops of one segment [a, e) of position-ordered candidates, taken by one
+// wave: all but the best `keep` of them (larger importance, then lower
+// position) get word 2 in the slot words; the kept ones keep their word 3.
+// ob[k] is candidate k's importance as 32 order bits.  The keep-th largest
+// value t is found bit by bit from the top: the largest t with at least
+// `keep` values >= t, counted with ballots.  Every value above t is kept,
+// and of the values equal to t the first keep - #(above t) in position
+// order.  A missing candidate holds 0, which no tested threshold (a bit
+// set) or value above t counts.  R > 0: the segment's values and slots stay
+// in registers, R chunks of 64 (L <= 64 R), loaded together; R == 0: any
+// length, by 8-bit digits through the wave's 256-word LDS histogram hist.
+template <int R>
+__device__ inline void tbe_segment(const uint32_t *ob, const int32_t *ord, uint64_t *key, int a, int e,
+                                   int keep, uint32_t *hist) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t t = 0;
+    int above = 0, seen = 0;
+    if constexpr (R > 0) {
+        uint32_t v[R];
+        int32_t sl[R];
+        bool live[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int k = a + 64 * r + lane;
+            live[r] = k < e;
+            v[r] = live[r] ? ob[k] : 0u;
+            sl[r] = live[r] ? ord[k] & 0x3fffffff : 0;
+        }
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = t | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(v[r] >= c));
+            if (cnt >= keep) t = c;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) above += __popcll(__ballot(v[r] > t));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint64_t eq = __ballot(live[r] && v[r] == t);
+            const int rk = seen + __popcll(eq & below);
+            if (live[r] && !(v[r] > t || (v[r] == t && rk < keep - above))) key[sl[r]] = 2ull;
+            seen += __popcll(eq);
+        }
+    } else {
+        // any length: radix select on 8-bit digits from the top, one
+        // 256-bin LDS histogram per wave (hist), 4 passes over the values
+        // and one for the verdicts.  need = how many of the values that
+        // match the digits chosen so far are still to be kept.
+        int need = keep;
+        uint32_t pre = 0, pre_mask = 0;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int k = a + lane; k < e; k += 64) {
+                const uint32_t x = ob[k];
+                if ((x & pre_mask) == pre) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // suffix counts: S(d) = matching values with digit >= d; lane
+            // holds digits 4 lane .. 4 lane + 3
+            uint32_t h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = hist[4 * lane + i];
+            const int tot = (int)(h[0] + h[1] + h[2] + h[3]);
+            int incl = tot;  // sum over lanes >= this one
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_down(incl, d);
+                incl += lane + d < 64 ? y : 0;
+            }
+            int sfx[4];
+            sfx[3] = incl - tot + (int)h[3];
+            sfx[2] = sfx[3] + (int)h[2];
+            sfx[1] = sfx[2] + (int)h[1];
+            sfx[0] = sfx[1] + (int)h[0];
+            // digit = largest d with S(d) >= need (S falls as d rises)
+            int ge = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ge += __popcll(__ballot(sfx[i] >= need));
+            const int dig = ge - 1;
+            // matching values with a larger digit are all kept
+            int gt = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gt += 4 * lane + i > dig ? (int)h[i] : 0;
+#pragma unroll
+            for (int d = 32; d > 0; d >>= 1) gt += __shfl_xor(gt, d);
+            need -= gt;
+            pre |= (uint32_t)dig << shift;
+            pre_mask |= 255u << shift;
+        }
+        t = pre;
+        above = keep - need;
+        for (int k = a + lane; k - lane < e; k += 64) {
+            const bool live = k < e;
+            const uint32_t v = live ? ob[k] : 0u;
+            const uint64_t eq = __ballot(live && v == t);
+            const int rk = seen + __popcll(eq & below);
+            if (live && !(v > t || (v == t && rk < keep - above))) key[ord[k] & 0x3fffffff] = 2ull;
+            seen += __popcll(eq);
+        }
+    }
+}
+
+// One segment: nothing to do when everything is kept (keep >= L),
+// everything dropped when keep is 0, else the selection above: in registers
+// up to 512 candidates, by LDS histogram beyond.
+__device__ inline void tbe_segment_any(const uint32_t *ob, const int32_t *ord, uint64_t *key, int a, int e,
+                                       int keep, uint32_t *hist) {
+    const int lane = threadIdx.x & 63;
+    const int L = e - a;
+    if (keep >= L) return;
+    if (keep <= 0) {
+        for (int k = a + lane; k < e; k += 64) key[ord[k] & 0x3fffffff] = 2ull;
+    } else if (L <= 64) {
+        tbe_segment<1>(ob, ord, key, a, e, keep, hist);
+    } else if (L <= 128) {
+        tbe_segment<2>(ob, ord, key, a, e, keep, hist);
+    } else if (L <= 256) {
+        tbe_segment<4>(ob, ord, key, a, e, keep, hist);
+    } else if (L <= 512) {
+        tbe_segment<8>(ob, ord, key, a, e, keep, hist);
+    } else {
+        tbe_segment<0>(ob, ord, key, a, e, keep, hist);
+    }
+}
+
+// Thought-adaptive eviction ("ThinKV", Methodology, think-before-evict).
+// The candidates (valid slots with q_window <= pos < seq_len -
+// recent_window), taken in position order, form segments: maximal runs of
+// one thought type.  A segment followed by k Transition segments keeps
+// everything if k == 0, else its best max(r_min, r0 >> (k - 1)) slots
+// (Reasoning, Execution) or t_keep slots (Transition): larger importance,
+// then lower position.  Three kernels, then evict_push:
+//
+// evict_tbe_prep, one 1024-thread workgroup per sequence:
+//   1. one word per slot (3 for a candidate, kept unless evict_tbe_drop
+//      drops it) and a position -> (pool, slot) map of the candidates;
+//   2. the candidates in position order, each wave taking TBE_RUN chunks of
+//      64 consecutive positions (ballots number them inside the wave, one
+//      scan of the wave totals places the waves): their (pool, slot) words
+//      and importance bits;
+//   3. segment starts, laid out the same way over the candidates: each
+//      segment's first candidate and the Transition segments up to and
+//      including it, then the counts.
+__global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const float *importance, int q_window,
+                                                              int recent_window, EvictWs ws) {
     const int b = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
     if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
     const int nb = c.n_blocks[b];
     const int nslot = nb * BLK;
     const int lo = q_window, hi = min(c.seq_len[b] - recent_window, c.n_cap);
-    uint32_t *row = c.table + (size_t)b * c.max_blocks;
+    const uint32_t *row = c.table + (size_t)b * c.max_blocks;
     const float *imp = importance + (size_t)b * c.n_cap;
     const size_t ms = (size_t)c.max_blocks * BLK;
     uint64_t *key = ws.cand + (size_t)b * ms;
-    int32_t *pmap = ws.pmap + (size_t)b * c.n_cap;
+    uint32_t *pmap = ws.pmap + (size_t)b * c.n_cap;
     int32_t *ord = ws.ord + (size_t)b * ms;
-    uint64_t *okey = ws.okey + (size_t)b * ms;
-    int32_t *segof = ws.segof + (size_t)b * ms;
+    uint32_t *ob = ws.ob + (size_t)b * ms;
     int32_t *segstart = ws.segstart + (size_t)b * (ms + 1);
-    int32_t *segret = ws.segret + (size_t)b * ms;
+    int32_t *segtc = ws.segtc + (size_t)b * ms;
 
     __shared__ int wave_tot[SEL_WAVES];
-    __shared__ int pool_cnt[4];
-    if (tid < 4) pool_cnt[tid] = 0;
-    for (int p = lo + tid; p < hi; p += SEL_THREADS) pmap[p] = -1;
+    for (int p = lo + tid; p < hi; p += SEL_THREADS) pmap[p] = 0xffffffffu;
     __syncthreads();
 
-    // 1. slot words and the position map of the candidates
-    slot_keys(c, row, imp, nslot, lo, hi, key, pmap);
+    // 1.
+    slot_keys(c, row, nullptr, nslot, lo, hi, key, pmap);
     __syncthreads();
 
-    // 2. candidates in position order, with their keys
+    // 2.
+    const uint64_t below = (1ull << lane) - 1ull;
     int n = 0;
-    for (int p0 = lo; p0 < hi; p0 += SEL_THREADS) {
-        const int p = p0 + tid;
-        const int v = p < hi ? pmap[p] : -1;
+    for (int p0 = lo; p0 < hi; p0 += SEL_THREADS * TBE_RUN) {
+        const int wb = p0 + wv * 64 * TBE_RUN;
+        uint32_t v[TBE_RUN];
+        float im[TBE_RUN];
+#pragma unroll
+        for (int u = 0; u < TBE_RUN; ++u) {
+            const int p = wb + 64 * u + lane;
+            v[u] = p < hi ? pmap[p] : 0xffffffffu;
+            im[u] = p < hi ? imp[p] : 0.0f;
+        }
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < TBE_RUN; ++u) cnt += __popcll(__ballot(v[u] != 0xffffffffu));
         int tot;
-        const int r = block_prefix(v >= 0, wave_tot, tot);
-        if (v >= 0) {
-            ord[n + r] = v;
-            okey[n + r] = key[v];
+        int at = n + wave_offsets(cnt, wave_tot, tot);
+#pragma unroll
+        for (int u = 0; u < TBE_RUN; ++u) {
+            const uint64_t bal = __ballot(v[u] != 0xffffffffu);
+            if (v[u] != 0xffffffffu) {
+                const int i = at + __popcll(bal & below);
+                ord[i] = (int32_t)v[u];
+                ob[i] = order_bits(im[u]);
+            }
+            at += __popcll(bal);
         }
         n += tot;
     }
     __syncthreads();
 
-    // 3. segments; segof[k] = segment of candidate k, segret[s] = its type
-    int nseg = 0;
-    for (int k0 = 0; k0 < n; k0 += SEL_THREADS) {
-        const int k = k0 + tid;
-        bool start = false;
-        int pool = 0;
-        if (k < n) {
-            pool = (int)(row[ord[k] >> 4] >> 30);
-            start = k == 0 || (int)(row[ord[k - 1] >> 4] >> 30) != pool;
+    // 3. a start is a pool change from the previous candidate; the starts
+    //    and the Transition starts are counted together (16 bits each) for
+    //    the wave scan
+    int nseg = 0, n_t = 0;
+    for (int k0 = 0; k0 < n; k0 += SEL_THREADS * TBE_RUN) {
+        const int wb = k0 + wv * 64 * TBE_RUN;
+        int pool[TBE_RUN];
+#pragma unroll
+        for (int u = 0; u < TBE_RUN; ++u) {
+            const int k = wb + 64 * u + lane;
+            pool[u] = k < n ? (int)((uint32_t)ord[k] >> 30) : -1;
+        }
+        const int before0 = wb > 0 && wb <= n ? (int)((uint32_t)ord[wb - 1] >> 30) : -1;
+        uint32_t stm = 0;  // bit u: candidate of chunk u starts a segment
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < TBE_RUN; ++u) {
+            const int up = __shfl_up(pool[u], 1);
+            const int carry = u == 0 ? before0 : __builtin_amdgcn_readlane(pool[u > 0 ? u - 1 : 0], 63);
+            const int prev = lane == 0 ? carry : up;
+            const bool st = pool[u] >= 0 && pool[u] != prev;
+            stm |= (uint32_t)st << u;
+            cnt += __popcll(__ballot(st)) + (__popcll(__ballot(st && pool[u] == 2)) << 16);
         }
         int tot;
-        const int r = block_prefix(start, wave_tot, tot);
-        if (start) {
-            segstart[nseg + r] = k;
-            segret[nseg + r] = pool;
+        const int off = wave_offsets(cnt, wave_tot, tot);
+        int sg = nseg + (off & 0xffff), tc = n_t + (off >> 16);
+#pragma unroll
+        for (int u = 0; u < TBE_RUN; ++u) {
+            const bool st = (stm >> u) & 1u;
+            const uint64_t bs = __ballot(st);
+            const uint64_t bt = __ballot(st && pool[u] == 2);
+            if (st) {
+                const int i = sg + __popcll(bs & below);
+                segstart[i] = wb + 64 * u + lane;
+                segtc[i] = tc + __popcll(bt & below) + (pool[u] == 2 ? 1 : 0);
+            }
+            sg += __popcll(bs);
+            tc += __popcll(bt);
         }
-        if (k < n) segof[k] = nseg + r + (start ? 1 : 0) - 1;
-        nseg += tot;
+        nseg += tot & 0xffff;
+        n_t += tot >> 16;
     }
-    if (tid == 0) segstart[nseg] = n;
-    __syncthreads();
+    if (tid == 0) {
+        segstart[nseg] = n;
+        ws.segn[2 * b] = nseg;
+        ws.segn[2 * b + 1] = n_t;
+    }
+}
 
-    // 4. retention: Transition segments after each segment
-    int n_t = 0;
-    for (int s0 = 0; s0 < nseg; s0 += SEL_THREADS) {
-        const int sg = s0 + tid;
-        int tot;
-        block_prefix(sg < nseg && segret[sg] == 2, wave_tot, tot);
-        n_t += tot;
-    }
-    int t_before = 0;
-    for (int s0 = 0; s0 < nseg; s0 += SEL_THREADS) {
-        const int sg = s0 + tid;
-        const bool is_t = sg < nseg && segret[sg] == 2;
-        int tot;
-        const int r = block_prefix(is_t, wave_tot, tot);
-        if (sg < nseg) {
-            const int later = n_t - (t_before + r + (is_t ? 1 : 0));
-            int keep = INT_MAX;
+// evict_tbe_drop: DROP_WGS workgroups per sequence, one wave per segment
+// (segments gw, gw + DROP_WAVES, ... for the sequence's wave gw): each lane
+// loads the bounds and retention of one of the wave's next 64 segments,
+// then the wave takes them in turn (tbe_segment_any).  Spreading a
+// sequence's segments over many workgroups puts the selection, which is
+// bound by instruction issue, on every compute unit.
+__global__ __launch_bounds__(DROP_THREADS) void evict_tbe_drop(kvq_cache c, int r0, int r_min, int t_keep,
+                                                               EvictWs ws) {
+    const int b = blockIdx.x / DROP_WGS;
+    const int gw = (blockIdx.x % DROP_WGS) * (DROP_THREADS / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const size_t ms = (size_t)c.max_blocks * BLK;
+    uint64_t *key = ws.cand + (size_t)b * ms;
+    const int32_t *ord = ws.ord + (size_t)b * ms;
+    const uint32_t *ob = ws.ob + (size_t)b * ms;
+    const int32_t *segstart = ws.segstart + (size_t)b * (ms + 1);
+    const int32_t *segtc = ws.segtc + (size_t)b * ms;
+    const int nseg = ws.segn[2 * b], n_t = ws.segn[2 * b + 1];
+    __shared__ uint32_t s_hist[DROP_THREADS / 64][256];
+    for (int s0 = gw; s0 < nseg; s0 += DROP_WAVES * 64) {
+        const int my = s0 + DROP_WAVES * lane;
+        int ma = 0, me = 0, mkeep = 0;
+        if (my < nseg) {
+            ma = segstart[my];
+            me = segstart[my + 1];
+            const int later = n_t - segtc[my];
+            const bool is_t = ((uint32_t)ord[ma] >> 30) == 2u;
+            mkeep = INT_MAX;
             if (later > 0) {
                 if (is_t) {
-                    keep = t_keep;
+                    mkeep = t_keep;
                 } else {
                     const int sh = later - 1;
-                    keep = max(sh >= 31 ? 0 : (r0 >> sh), r_min);
+                    mkeep = max(sh >= 31 ? 0 : (r0 >> sh), r_min);
                 }
-                keep = max(keep, 0);
+                mkeep = max(mkeep, 0);
             }
-            segret[sg] = keep;
         }
-        t_before += tot;
-    }
-    __syncthreads();
-
-    // 5. each candidate's verdict: fewer than `retention` better candidates
-    //    in its segment (keys are unique: the position is part of them)
-    for (int k0 = 0; k0 < n; k0 += SEL_THREADS) {
-        const int k = k0 + tid;
-        if (k < n) {
-            const int sg = segof[k];
-            const int a = segstart[sg], e = segstart[sg + 1];
-            const int keep = segret[sg];
-            bool kept = true;
-            if (keep < e - a) {
-                const uint64_t kk = okey[k];
-                int better = 0;
-                for (int j = a; j < e && better < keep; ++j) better += okey[j] > kk ? 1 : 0;
-                kept = better < keep;
-            }
-            segof[k] = kept ? 1 : 0;
+        const int cnt = min(64, (nseg - s0 + DROP_WAVES - 1) / DROP_WAVES);
+        for (int j = 0; j < cnt; ++j) {
+            const int a = __builtin_amdgcn_readlane(ma, j);
+            const int e = __builtin_amdgcn_readlane(me, j);
+            const int keep = __builtin_amdgcn_readlane(mkeep, j);
+            tbe_segment_any(ob, ord, key, a, e, keep, s_hist[threadIdx.x >> 6]);
         }
     }
-    __syncthreads();
-    for (int k0 = 0; k0 < n; k0 += SEL_THREADS) {
-        const int k = k0 + tid;
-        if (k < n) key[ord[k]] = segof[k] ? 1ull : 2ull;
-    }
-    __syncthreads();
+}
 
-    // 6. clear the dropped candidates (word 2), compact the table row
-    clear_and_compact(c, b, key, nslot, nb, row, ws, wave_tot, pool_cnt,
+// evict_tbe_compact: clear the dropped slots (word 2) and compact the table
+// row as evict_select does, one workgroup per sequence.
+__global__ __launch_bounds__(SEL_THREADS) void evict_tbe_compact(kvq_cache c, EvictWs ws) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int nb = c.n_blocks[b];
+    uint32_t *row = c.table + (size_t)b * c.max_blocks;
+    uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
+    __shared__ int wave_tot[SEL_WAVES];
+    __shared__ int pool_cnt[4];
+    if (tid < 4) pool_cnt[tid] = 0;
+    __syncthreads();
+    clear_and_compact(c, b, key, nb * BLK, nb, row, ws, wave_tot, pool_cnt,
                       [](uint64_t kk) { return kk != 0 && kk != 2; });
 }
 
@@ -476,8 +681,10 @@ bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *ke
 bool launch_evict_tbe(const kvq_cache &c, const float *importance, int r0, int r_min, int t_keep,
                       int q_window, int recent_window, void *ws_ptr, hipStream_t s) {
     EvictWs ws(ws_ptr, c);
-    hipLaunchKernelGGL(evict_tbe_select, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, r0, r_min,
-                       t_keep, q_window, recent_window, ws);
+    hipLaunchKernelGGL(evict_tbe_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, q_window,
+                       recent_window, ws);
+    hipLaunchKernelGGL(evict_tbe_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, r0, r_min, t_keep, ws);
+    hipLaunchKernelGGL(evict_tbe_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws);
     hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);
     return hipGetLastError() == hipSuccess;
 }

@@ -75,18 +75,18 @@ struct EvictWs {
     int32_t *nfreed;   // [B][4] freed per pool
     int32_t *top;      // [4] free_top before the call
     // segment-granular eviction only: candidates in position order
-    int32_t *pmap;     // [B][n_cap] slot of the candidate at a position, or -1
-    int32_t *ord;      // [B][max_blocks*16] slots of the candidates, by position
-    uint64_t *okey;    // [B][max_blocks*16] their keys, same order
-    int32_t *segof;    // [B][max_blocks*16] segment of each candidate, then its verdict
+    uint32_t *pmap;    // [B][n_cap] (pool << 30) | slot of the candidate at a position, or ~0
+    int32_t *ord;      // [B][max_blocks*16] (pool << 30) | slot of the candidates, by position
+    uint32_t *ob;      // [B][max_blocks*16] their importance as order bits, same order
     int32_t *segstart; // [B][max_blocks*16 + 1] first candidate of each segment
-    int32_t *segret;   // [B][max_blocks*16] thought type, then retention, of each segment
+    int32_t *segtc;    // [B][max_blocks*16] Transition segments up to and including each segment
+    int32_t *segn;     // [B][2] segments, Transition segments
     static size_t bytes(const kvq_cache &c) {
         const size_t ms = (size_t)c.max_blocks * 16;
         return align256(8L * c.B * ms) + align256(4L * c.B * c.max_blocks) + align256(16L * c.B) +
                align256(16) + align256(4L * c.B * c.n_cap) + align256(4L * c.B * ms) +
-               align256(8L * c.B * ms) + align256(4L * c.B * ms) + align256(4L * c.B * (ms + 1)) +
-               align256(4L * c.B * ms);
+               align256(4L * c.B * ms) + align256(4L * c.B * (ms + 1)) + align256(4L * c.B * ms) +
+               align256(8L * c.B);
     }
     EvictWs(void *ws, const kvq_cache &c) {
         const size_t ms = (size_t)c.max_blocks * 16;
@@ -95,12 +95,12 @@ struct EvictWs {
         freed = (uint32_t *)p;    p += align256(4L * c.B * c.max_blocks);
         nfreed = (int32_t *)p;    p += align256(16L * c.B);
         top = (int32_t *)p;       p += align256(16);
-        pmap = (int32_t *)p;      p += align256(4L * c.B * c.n_cap);
+        pmap = (uint32_t *)p;     p += align256(4L * c.B * c.n_cap);
         ord = (int32_t *)p;       p += align256(4L * c.B * ms);
-        okey = (uint64_t *)p;     p += align256(8L * c.B * ms);
-        segof = (int32_t *)p;     p += align256(4L * c.B * ms);
+        ob = (uint32_t *)p;       p += align256(4L * c.B * ms);
         segstart = (int32_t *)p;  p += align256(4L * c.B * (ms + 1));
-        segret = (int32_t *)p;
+        segtc = (int32_t *)p;     p += align256(4L * c.B * ms);
+        segn = (int32_t *)p;
     }
 };
 

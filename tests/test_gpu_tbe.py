@@ -131,3 +131,26 @@ def test_workload_tbe_bit_exact(pair):
     ref, got = pair.decode(wl.queries(w, 3))
     assert_attention_close(ref, got)
     assert_mass_close(pair.oc.st["seq_len"], ref, got)
+
+
+def test_long_window_and_long_segments():
+    """A 42k-token sequence of mixed runs beside one whose Reasoning and
+    Execution segments (700 and 1300 candidates) have later Transitions:
+    segments longer than 512 candidates are selected from values reloaded
+    at every step rather than held in registers."""
+    import torch
+
+    rng = np.random.default_rng(31)
+    n_long = 42_000
+    long_row = list(np.repeat(rng.integers(0, 3, n_long // 20), rng.integers(1, 40, n_long // 20)))[:n_long]
+    seg_row = [E] * 700 + [T] * 5 + [R] * 1300 + [T] * 5 + [E] * 20
+    log(f"[gpu tbe] long window and segments: {len(long_row)} and {len(seg_row)} tokens")
+    oc, gc, g = _pair_from_tags([long_row, seg_row])
+    imp = (np.round(rng.exponential(1.0, (g.B, g.n_cap)) * 16) / 16).astype(np.float32)
+    for args in [(64, 4, 8, 16, 32), (4, 1, 2, 0, 0)]:
+        log(f"[gpu tbe] long window and segments, (r0, r_min, t_keep, qw, rw) = {args}")
+        gc.evict_tbe(_dev(imp), *args)
+        oc.evict_tbe(imp, *args)
+        torch.cuda.synchronize()
+        assert gc.status == 0
+        assert_same_cache(oc, gc.state_numpy())
