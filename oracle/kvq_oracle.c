@@ -649,6 +649,194 @@ void orc_evict_tbe(orc_cache *c, const float *importance, int r0, int r_min, int
     }
 }
 
+/* Window score in fixed point, 16 fractional bits: floor(score * 2^16) for
+ * 0 < score < 2^16, 2^32 - 1 from 2^16 up, 0 for score <= 0 or NaN. */
+static uint32_t tam_fix(float score)
+{
+    if (!(score > 0.0f))
+        return 0;
+    if (score >= 65536.0f)
+        return 0xffffffffu;
+    return (uint32_t)(score * 65536.0f);
+}
+
+/* floor(sqrt(x)) for x < 2^64, by bisection on the root. */
+static uint64_t isqrt_u64(uint64_t x)
+{
+    uint64_t lo = 0, hi = 1ull << 32;
+    while (hi - lo > 1) {
+        uint64_t mid = lo + (hi - lo) / 2;
+        if (mid * mid <= x)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+/*
+ * Thought-aware budgets ("Thought-Aware KV Cache Compaction ... (TAM)",
+ * section 2: A segmentation, B adaptive budget allocation, C pivotal-token
+ * protection), with compaction read as keeping a subset of the cached
+ * tokens.
+ *
+ * Per sequence, the candidates are the valid slots with q_window <= pos <
+ * seq_len - recent_window; the others are kept.  score[p] is the attention
+ * mass position p received from the selection window (the R most recent
+ * queries), taken in fixed point s = tam_fix(score).
+ *  C. A candidate is pivotal when s * N > pivot_c * S (in doubles), N the
+ *     candidates and S the sum of their s: its mass is above pivot_c times
+ *     the mean.  Pivotal candidates are all kept; the budget left,
+ *     T = max(0, keep_k - pivotal), goes to the others.
+ *  A. In position order the candidates form segments: a change of thought
+ *     type opens a new segment once the open one holds min_seg candidates
+ *     (shorter runs merge into the segment they follow).
+ *  B. Segment i has n_i candidates, m_i of them not pivotal, and the sum S_i
+ *     of their s.  Its weight is a_i = isqrt(floor(S_i / n_i) * 2^16) * m_i,
+ *     i.e. sqrt(w_i) * m_i with w_i its mean window score.  Budgets are
+ *     t_i = T a_i / A (A the sum of the weights) except that a segment whose
+ *     share reaches m_i is capped at m_i and the rest shared again among the
+ *     others, until no share reaches its segment's size.  Integer budgets
+ *     come from the running sums C_j of the uncapped weights in position
+ *     order: t = floor(T' C_j / A) - floor(T' C_(j-1) / A), T' the budget
+ *     left after the capped segments; they add up to T' exactly.  With A = 0
+ *     the uncapped segments get nothing.
+ * Each segment keeps its pivotal candidates and its t_i others of largest
+ * score (ties: lower position); then the table is compacted as in orc_evict.
+ */
+void orc_evict_tam(orc_cache *c, const float *score, const int32_t *keep_k, float pivot_c, int min_seg,
+                   int q_window, int recent_window)
+{
+    if (min_seg < 1)
+        min_seg = 1;
+    for (int b = 0; b < c->B; ++b) {
+        uint32_t *row = c->table + (long)b * c->max_blocks;
+        const float *sc = score + (long)b * c->n_cap;
+        int lo = q_window, hi = c->seq_len[b] - recent_window;
+        long cap = (long)c->n_blocks[b] * BLK + 1;
+        cand *cs = malloc(sizeof(cand) * cap);
+        int n = 0;
+        for (int e = 0; e < c->n_blocks[b]; ++e) {
+            int pool = (int)(row[e] >> 30);
+            uint32_t id = row[e] & 0x3fffffffu;
+            uint16_t m = c->mask[pool][id];
+            for (int s = 0; s < BLK; ++s) {
+                if (!((m >> s) & 1))
+                    continue;
+                int p = c->pos[pool][id * BLK + s];
+                if (p < lo || p >= hi)
+                    continue;
+                cs[n].imp = sc[p];
+                cs[n].pos = p;
+                cs[n].pool = pool;
+                cs[n].id = id;
+                cs[n].slot = s;
+                ++n;
+            }
+        }
+        qsort(cs, n, sizeof(cand), pos_cmp);
+
+        /* C. pivotal candidates */
+        uint64_t s_all = 0;
+        for (int i = 0; i < n; ++i)
+            s_all += tam_fix(cs[i].imp);
+        char *piv = calloc(n + 1, 1);
+        long n_piv = 0;
+        for (int i = 0; i < n; ++i) {
+            piv[i] = (double)tam_fix(cs[i].imp) * (double)n > (double)pivot_c * (double)s_all;
+            n_piv += piv[i];
+        }
+        long T = (long)keep_k[b] - n_piv;
+        if (T < 0)
+            T = 0;
+
+        /* A. segments */
+        int *seg_start = malloc(sizeof(int) * (n + 1));
+        int n_seg = 0, open = 0;
+        for (int i = 0; i < n; ++i) {
+            if (i == 0 || (cs[i].pool != cs[i - 1].pool && open >= min_seg)) {
+                seg_start[n_seg++] = i;
+                open = 0;
+            }
+            ++open;
+        }
+        seg_start[n_seg] = n;
+
+        /* B. weights, capped shares, cumulative rounding */
+        uint64_t *a = malloc(sizeof(uint64_t) * (n_seg + 1));
+        long *mm = malloc(sizeof(long) * (n_seg + 1));
+        long *t = malloc(sizeof(long) * (n_seg + 1));
+        char *capped = calloc(n_seg + 1, 1);
+        for (int sg = 0; sg < n_seg; ++sg) {
+            uint64_t ssum = 0;
+            long nn = seg_start[sg + 1] - seg_start[sg], m = 0;
+            for (int i = seg_start[sg]; i < seg_start[sg + 1]; ++i) {
+                ssum += tam_fix(cs[i].imp);
+                m += !piv[i];
+            }
+            mm[sg] = m;
+            a[sg] = isqrt_u64((ssum / (uint64_t)nn) << 16) * (uint64_t)m;
+            capped[sg] = m == 0;
+            t[sg] = 0;
+        }
+        long t_left = T;
+        for (;;) {
+            t_left = T;
+            unsigned __int128 A = 0;
+            for (int sg = 0; sg < n_seg; ++sg) {
+                if (capped[sg])
+                    t_left -= mm[sg];
+                else
+                    A += a[sg];
+            }
+            int more = 0;
+            if (A > 0) {
+                for (int sg = 0; sg < n_seg; ++sg) {
+                    if (!capped[sg] && (unsigned __int128)t_left * a[sg] >= (unsigned __int128)mm[sg] * A) {
+                        capped[sg] = 1;
+                        more = 1;
+                    }
+                }
+            }
+            if (!more) {
+                unsigned __int128 run = 0, q_prev = 0;
+                for (int sg = 0; sg < n_seg; ++sg) {
+                    if (capped[sg]) {
+                        t[sg] = mm[sg];
+                    } else if (A > 0) {
+                        run += a[sg];
+                        unsigned __int128 q = (unsigned __int128)t_left * run / A;
+                        t[sg] = (long)(q - q_prev);
+                        q_prev = q;
+                    }
+                }
+                break;
+            }
+        }
+
+        /* each segment: pivotal kept, t others by score */
+        cand *np = malloc(sizeof(cand) * (n + 1));
+        for (int sg = 0; sg < n_seg; ++sg) {
+            int k = 0;
+            for (int i = seg_start[sg]; i < seg_start[sg + 1]; ++i)
+                if (!piv[i])
+                    np[k++] = cs[i];
+            qsort(np, k, sizeof(cand), cand_cmp);
+            for (int i = (int)t[sg]; i < k; ++i)
+                c->mask[np[i].pool][np[i].id] &= (uint16_t)~(1u << np[i].slot);
+        }
+        free(np);
+        free(capped);
+        free(t);
+        free(mm);
+        free(a);
+        free(seg_start);
+        free(piv);
+        free(cs);
+        compact_row(c, b);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Array forms of the scalar routines above, for the test suite         */
 /* ------------------------------------------------------------------ */

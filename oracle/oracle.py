@@ -71,6 +71,8 @@ def lib():
         L.orc_evict.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int, ctypes.c_int]
         L.orc_evict_tbe.argtypes = [ctypes.POINTER(_Cache), P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int]
+        L.orc_evict_tam.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_float, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int]
         L.orc_dequant_slot.argtypes = [ctypes.POINTER(_Cache), ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_int, ctypes.c_int, P, P]
         L.orc_slot_codes.argtypes = [ctypes.POINTER(_Cache), ctypes.c_int, ctypes.c_uint32,
@@ -196,6 +198,16 @@ class OracleCache:
         g = self.g
         imp = np.ascontiguousarray(importance, dtype=np.float32).reshape(g.B, g.n_cap)
         lib().orc_evict_tbe(self._c(), _p(imp), int(r0), int(r_min), int(t_keep), int(q_window),
+                            int(recent_window))
+
+    def evict_tam(self, score: np.ndarray, keep_k, pivot_c: float, min_seg: int, q_window: int,
+                  recent_window: int):
+        """Thought-aware budgets ("TAM", section 2: segments, sqrt(w) n
+        budgets, pivotal tokens); see orc_evict_tam in kvq_oracle.c."""
+        g = self.g
+        sc = np.ascontiguousarray(score, dtype=np.float32).reshape(g.B, g.n_cap)
+        kk = np.ascontiguousarray(np.broadcast_to(np.asarray(keep_k, dtype=np.int32), (g.B,)))
+        lib().orc_evict_tam(self._c(), _p(sc), _p(kk), float(pivot_c), int(min_seg), int(q_window),
                             int(recent_window))
 
     # -- inspection -----------------------------------------------------
