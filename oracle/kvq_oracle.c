@@ -688,9 +688,9 @@ static uint64_t isqrt_u64(uint64_t x)
  *     candidates and S the sum of their s: its mass is above pivot_c times
  *     the mean.  Pivotal candidates are all kept; the budget left,
  *     T = max(0, keep_k - pivotal), goes to the others.
- *  A. In position order the candidates form segments: a change of thought
- *     type opens a new segment once the open one holds min_seg candidates
- *     (shorter runs merge into the segment they follow).
+ *  A. In position order the candidates form runs of one thought type; a
+ *     run of at least min_seg candidates opens a new segment, a shorter run
+ *     merges into the segment before it (the first run always opens one).
  *  B. Segment i has n_i candidates, m_i of them not pivotal, and the sum S_i
  *     of their s.  Its weight is a_i = isqrt(floor(S_i / n_i) * 2^16) * m_i,
  *     i.e. sqrt(w_i) * m_i with w_i its mean window score.  Budgets are
@@ -750,15 +750,16 @@ void orc_evict_tam(orc_cache *c, const float *score, const int32_t *keep_k, floa
         if (T < 0)
             T = 0;
 
-        /* A. segments */
+        /* A. segments: runs, then the short ones merged */
         int *seg_start = malloc(sizeof(int) * (n + 1));
-        int n_seg = 0, open = 0;
-        for (int i = 0; i < n; ++i) {
-            if (i == 0 || (cs[i].pool != cs[i - 1].pool && open >= min_seg)) {
+        int n_seg = 0;
+        for (int i = 0; i < n;) {
+            int j = i + 1;
+            while (j < n && cs[j].pool == cs[i].pool)
+                ++j;
+            if (i == 0 || j - i >= min_seg)
                 seg_start[n_seg++] = i;
-                open = 0;
-            }
-            ++open;
+            i = j;
         }
         seg_start[n_seg] = n;
 

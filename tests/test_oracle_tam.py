@@ -88,21 +88,23 @@ def test_weights_use_segment_mean_and_non_pivotal_count():
 
 
 def test_short_runs_merge_into_the_segment_before():
-    # R R E E E R R R, scores 9 9 1 1 1 4 4 4, keep 4.
-    # min_seg 3: segments {0..4} (mean 4.2) and {5,6,7} (mean 4): weights
-    # about 2.05*5 and 2*3, shares 2.52 and 1.48 -> running floors 2, 4 ->
-    # budgets 2 and 2: positions 0, 1 and 5, 6.
-    # min_seg 1: segments {0,1} (mean 9), {2,3,4} (1), {5,6,7} (4): weights
-    # 6, 3, 6, shares 1.6, 0.8, 1.6 -> running floors 1, 2, 4 -> budgets
-    # 1, 1, 2: positions 0, 2, 5, 6.
-    tags = [R, R, E, E, E, R, R, R]
-    scores = [9, 9, 1, 1, 1, 4, 4, 4]
-    oc, sc = _build(tags, scores)
-    oc.evict_tam(sc, 4, INF, 3, 0, 0)
-    assert _kept(oc) == [0, 1, 5, 6]
-    oc, sc = _build(tags, scores)
-    oc.evict_tam(sc, 4, INF, 1, 0, 0)
-    assert _kept(oc) == [0, 2, 5, 6]
+    # R R R E R R R E E E, scores 9 9 9 1 4 4 4 2 2 2, keep 5.
+    # min_seg 2: the lone E (a run of 1) joins the first segment:
+    # {0..3} (mean 7, sqrt 2.65, weight 10.6), {4,5,6} (mean 4, weight 6),
+    # {7,8,9} (mean 2, weight 4.2): shares 2.55, 1.44, 1.01 -> running floors
+    # 2, 3, 5 -> budgets 2, 1, 2: positions 0, 1 | 4 | 7, 8.
+    # min_seg 1: {0,1,2} (mean 9, weight 9), {3} (mean 1, weight 1), {4,5,6}
+    # (weight 6), {7,8,9} (weight 4.2): shares 2.23, 0.25, 1.49, 1.04 ->
+    # running floors 2, 2, 3, 5 -> budgets 2, 0, 1, 2: the same positions.
+    # min_seg 4: every run after the first is shorter than 4, so all of them
+    # join the first segment: one segment keeps its best 5, the three 9s and
+    # the first two 4s: positions 0, 1, 2, 4, 5.
+    tags = [R, R, R, E, R, R, R, E, E, E]
+    scores = [9, 9, 9, 1, 4, 4, 4, 2, 2, 2]
+    for min_seg, expect in [(2, [0, 1, 4, 7, 8]), (1, [0, 1, 4, 7, 8]), (4, [0, 1, 2, 4, 5])]:
+        oc, sc = _build(tags, scores)
+        oc.evict_tam(sc, 5, INF, min_seg, 0, 0)
+        assert _kept(oc) == expect, min_seg
 
 
 def test_windows_and_degenerate_budgets():
