@@ -42,6 +42,10 @@ HBM_PEAK_GBS = 8000.0
 # 8 tokens kept of each earlier Transition segment ("ThinKV", Methodology,
 # think-before-evict: 64, 32, 16, ... as its example schedule)
 TBE_PARAMS = (64, 4, 8)
+# thought-aware budgets timed beside them: the workload's keep as the budget,
+# the importance as the window score, pivotal above 8x the mean, runs
+# shorter than 16 candidates merged ("TAM", section 2)
+TAM_PARAMS = (8.0, 16)
 ROW_BYTES = (288, 160, 96)   # K+V codes + (scale, zero) per token per kv head, R/E/T
 
 
@@ -240,12 +244,28 @@ def evict_bench(args, w):
         raise RuntimeError(f"status {cache.status} after segment eviction")
     tbe_ms = np.array([a.elapsed_time(b) for a, b in tbe_ms[args.warmup:]])
     tbe_kept = valid_slot_count(cache)
+    tam_ms = []
+    for s in range(total_steps):
+        for k, v in meta.items():
+            cache.t[k].copy_(v)
+        IMP.copy_(IMP0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.evict_tam(IMP, KK, *TAM_PARAMS, w.q_window, w.recent_window)
+        e1.record()
+        tam_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    if cache.status != 0:
+        raise RuntimeError(f"status {cache.status} after budgeted eviction")
+    tam_ms = np.array([a.elapsed_time(b) for a, b in tam_ms[args.warmup:]])
+    tam_kept = valid_slot_count(cache)
     step_ms = dec_ms + evi_ms
     achieved = kvb / (dec_ms.mean() * 1e-3) / 1e9
     ev_gbs = evb / (evi_ms.mean() * 1e-3) / 1e9
     log(f"[gpu] step {step_ms.mean() * 1e3:.1f} us: decode {dec_ms.mean() * 1e3:.1f} us "
         f"({achieved:.0f} GB/s of {kvb / 1e6:.1f} MB), evict {evi_ms.mean() * 1e3:.1f} us; "
-        f"segment eviction {tbe_ms.mean() * 1e3:.1f} us, {n_valid} -> {tbe_kept} valid slots")
+        f"segment eviction {tbe_ms.mean() * 1e3:.1f} us, {n_valid} -> {tbe_kept} valid slots; "
+        f"segment budgets {tam_ms.mean() * 1e3:.1f} us, {n_valid} -> {tam_kept}")
     result = {
         "metric": METRIC,
         "value": B / (step_ms.mean() * 1e-3),
@@ -271,10 +291,14 @@ def evict_bench(args, w):
                      "avg_us": float(dec_ms.mean() * 1e3)},
         "evict": {"kernel": "kvq_evict_topk (select + push)", "avg_us": float(evi_ms.mean() * 1e3),
                   "bytes": evb, "achieved_gbs": ev_gbs, "frac": ev_gbs / HBM_PEAK_GBS},
-        "evict_tbe": {"kernel": "kvq_evict_tbe (select + push)", "avg_us": float(tbe_ms.mean() * 1e3),
+        "evict_tbe": {"kernel": "kvq_evict_tbe (prep + drop + compact + push)", "avg_us": float(tbe_ms.mean() * 1e3),
                       "r0_rmin_tkeep": list(TBE_PARAMS), "valid_before": n_valid,
                       "valid_after": tbe_kept, "bytes": evb,
                       "achieved_gbs": evb / (tbe_ms.mean() * 1e-3) / 1e9},
+        "evict_tam": {"kernel": "kvq_evict_tam (prep + drop + compact + push)",
+                      "avg_us": float(tam_ms.mean() * 1e3), "pivot_c_min_seg": list(TAM_PARAMS),
+                      "valid_before": n_valid, "valid_after": tam_kept, "bytes": evb,
+                      "achieved_gbs": evb / (tam_ms.mean() * 1e-3) / 1e9},
         "cpu_baseline": None,
     }
     del Q

@@ -88,3 +88,17 @@ extern "C" kvq_status kvq_evict_tbe(const kvq_cache *c, const float *importance,
                ? KVQ_OK
                : KVQ_EHIP;
 }
+
+extern "C" kvq_status kvq_evict_tam(const kvq_cache *c, const float *score, const int32_t *keep_k,
+                                    float pivot_c, int32_t min_seg, int32_t q_window,
+                                    int32_t recent_window, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (!score || !keep_k || !(pivot_c >= 0.0f) || min_seg < 1 || q_window < 0 || recent_window < 0)
+        return KVQ_EINVAL;
+    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    return kvq::launch_evict_tam(*c, score, keep_k, pivot_c, min_seg, q_window, recent_window, ws, stream)
+               ? KVQ_OK
+               : KVQ_EHIP;
+}

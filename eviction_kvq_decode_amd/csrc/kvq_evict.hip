@@ -13,8 +13,9 @@
 //   for the k-th largest; losers' mask bits are cleared; the table row is
 //   compacted in order with a ballot prefix scan; freed entries are listed
 //   in table order.
-// evict_tbe_prep / evict_tbe_drop / evict_tbe_compact: thought-adaptive
-//   eviction by segment (below).
+// evict_tbe_prep / evict_tam_prep + evict_seg_drop + evict_seg_compact:
+//   segment-granular eviction, thought-adaptive (TBE) or by thought-aware
+//   budgets (TAM) (below).
 // evict_push: one workgroup per sequence pushes its freed ids at offsets
 //   ranked across sequences in batch order.
 #include <limits.h>
@@ -304,7 +305,9 @@ __device__ inline int wave_offsets(int x, int *wave_tot, int &total) {
 // Drops of one segment [a, e) of position-ordered candidates, taken by one
 // wave: all but the best `keep` of them (larger importance, then lower
 // position) get word 2 in the slot words; the kept ones keep their word 3.
-// ob[k] is candidate k's importance as 32 order bits.  The keep-th largest
+// ob[k] is candidate k's importance as 32 order bits, or 0 for a candidate
+// that is never dropped and does not count toward `keep` (which is at most
+// the number of the others).  The keep-th largest
 // value t is found bit by bit from the top: the largest t with at least
 // `keep` values >= t, counted with ballots.  Every value above t is kept,
 // and of the values equal to t the first keep - #(above t) in position
@@ -343,7 +346,7 @@ __device__ inline void tbe_segment(const uint32_t *ob, const int32_t *ord, uint6
         for (int r = 0; r < R; ++r) {
             const uint64_t eq = __ballot(live[r] && v[r] == t);
             const int rk = seen + __popcll(eq & below);
-            if (live[r] && !(v[r] > t || (v[r] == t && rk < keep - above))) key[sl[r]] = 2ull;
+            if (live[r] && v[r] != 0 && !(v[r] > t || (v[r] == t && rk < keep - above))) key[sl[r]] = 2ull;
             seen += __popcll(eq);
         }
     } else {
@@ -361,7 +364,7 @@ __device__ inline void tbe_segment(const uint32_t *ob, const int32_t *ord, uint6
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             for (int k = a + lane; k < e; k += 64) {
                 const uint32_t x = ob[k];
-                if ((x & pre_mask) == pre) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+                if (x != 0 && (x & pre_mask) == pre) atomicAdd(&hist[(x >> shift) & 255u], 1u);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -405,14 +408,14 @@ __device__ inline void tbe_segment(const uint32_t *ob, const int32_t *ord, uint6
             const uint32_t v = live ? ob[k] : 0u;
             const uint64_t eq = __ballot(live && v == t);
             const int rk = seen + __popcll(eq & below);
-            if (live && !(v > t || (v == t && rk < keep - above))) key[ord[k] & 0x3fffffff] = 2ull;
+            if (live && v != 0 && !(v > t || (v == t && rk < keep - above))) key[ord[k] & 0x3fffffff] = 2ull;
             seen += __popcll(eq);
         }
     }
 }
 
-// One segment: nothing to do when everything is kept (keep >= L),
-// everything dropped when keep is 0, else the selection above: in registers
+// One segment: nothing to do when everything is kept (keep >= L), every
+// droppable candidate dropped when keep is 0, else the selection above: in registers
 // up to 512 candidates, by LDS histogram beyond.
 __device__ inline void tbe_segment_any(const uint32_t *ob, const int32_t *ord, uint64_t *key, int a, int e,
                                        int keep, uint32_t *hist) {
@@ -420,7 +423,8 @@ __device__ inline void tbe_segment_any(const uint32_t *ob, const int32_t *ord, u
     const int L = e - a;
     if (keep >= L) return;
     if (keep <= 0) {
-        for (int k = a + lane; k < e; k += 64) key[ord[k] & 0x3fffffff] = 2ull;
+        for (int k = a + lane; k < e; k += 64)
+            if (ob[k] != 0) key[ord[k] & 0x3fffffff] = 2ull;
     } else if (L <= 64) {
         tbe_segment<1>(ob, ord, key, a, e, keep, hist);
     } else if (L <= 128) {
@@ -434,34 +438,95 @@ __device__ inline void tbe_segment_any(const uint32_t *ob, const int32_t *ord, u
     }
 }
 
-// Thought-adaptive eviction ("ThinKV", Methodology, think-before-evict).
-// The candidates (valid slots with q_window <= pos < seq_len -
-// recent_window), taken in position order, form segments: maximal runs of
-// one thought type.  A segment followed by k Transition segments keeps
-// everything if k == 0, else its best max(r_min, r0 >> (k - 1)) slots
-// (Reasoning, Execution) or t_keep slots (Transition): larger importance,
-// then lower position.  Three kernels, then evict_push:
-//
-// evict_tbe_prep, one 1024-thread workgroup per sequence:
-//   1. one word per slot (3 for a candidate, kept unless evict_tbe_drop
+// Window score in fixed point, 16 fractional bits: floor(score * 2^16) for
+// 0 < score < 2^16, 2^32 - 1 from 2^16 up, 0 for score <= 0 or NaN.
+__device__ inline uint32_t tam_fix(float score) {
+    if (!(score > 0.0f)) return 0u;
+    if (score >= 65536.0f) return 0xffffffffu;
+    return (uint32_t)(score * 65536.0f);
+}
+
+// floor(sqrt(x)), by bisection on the root (exact integer arithmetic).
+__device__ inline uint64_t isqrt_u64(uint64_t x) {
+    uint64_t lo = 0, hi = 1ull << 32;
+    while (hi - lo > 1) {
+        const uint64_t mid = lo + (hi - lo) / 2;
+        if (mid * mid <= x) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Sum of a 64-bit value over the workgroup (all threads get it).
+__device__ inline uint64_t block_sum_u64(uint64_t x, uint64_t *wave_u64) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d);
+    if (lane == 0) wave_u64[wv] = x;
+    __syncthreads();
+    uint64_t t = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) t += wave_u64[w];
+    __syncthreads();
+    return t;
+}
+
+// Inclusive prefix sum of a 64-bit value over the workgroup (thread order)
+// and the total.
+__device__ inline uint64_t block_scan_u64(uint64_t x, uint64_t *wave_u64, uint64_t &total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint64_t incl = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t y = __shfl_up(incl, d);
+        incl += lane >= d ? y : 0ull;
+    }
+    if (lane == 63) wave_u64[wv] = incl;
+    __syncthreads();
+    uint64_t before = 0;
+    total = 0;
+    for (int w = 0; w < SEL_WAVES; ++w) {
+        const uint64_t v = wave_u64[w];
+        before += w < wv ? v : 0ull;
+        total += v;
+    }
+    __syncthreads();
+    return before + incl;
+}
+
+// Segment-granular eviction, two policies on one pipeline: a prep kernel
+// per policy (one 1024-thread workgroup per sequence) orders the candidates
+// (valid slots with q_window <= pos < seq_len - recent_window) by position,
+// cuts them into segments and gives each segment the number of its
+// droppable candidates it keeps (segkeep); evict_seg_drop then drops the
+// rest of each segment, lowest value first (ties: higher position first),
+// and evict_seg_compact clears and compacts; evict_push frees the emptied
+// blocks.
+
+struct SegOrder {
+    int n, nseg, n_t;
+    uint64_t s_all;  // sum of the fixed-point scores (when sfx is written)
+};
+
+// Steps shared by the prep kernels:
+//   1. one word per slot (3 for a candidate, kept unless evict_seg_drop
 //      drops it) and a position -> (pool, slot) map of the candidates;
 //   2. the candidates in position order, each wave taking TBE_RUN chunks of
 //      64 consecutive positions (ballots number them inside the wave, one
-//      scan of the wave totals places the waves): their (pool, slot) words
-//      and importance bits;
-//   3. segment starts, laid out the same way over the candidates: each
-//      segment's first candidate and the Transition segments up to and
-//      including it, then the counts.
-__global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const float *importance, int q_window,
-                                                              int recent_window, EvictWs ws) {
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+//      scan of the wave totals places the waves): their (pool, slot) words,
+//      their value's order bits and, if sfx is given, its fixed point;
+//   3. runs of one thought type, laid out the same way over the
+//      candidates: the first candidate of each run and the Transition runs
+//      up to and including it (segstart, segtc), then the counts.
+__device__ inline SegOrder seg_order(const kvq_cache &c, int b, const float *value, int q_window,
+                                     int recent_window, EvictWs &ws, uint32_t *sfx, int *wave_tot,
+                                     uint64_t *wave_u64) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
     const int nb = c.n_blocks[b];
     const int nslot = nb * BLK;
     const int lo = q_window, hi = min(c.seq_len[b] - recent_window, c.n_cap);
     const uint32_t *row = c.table + (size_t)b * c.max_blocks;
-    const float *imp = importance + (size_t)b * c.n_cap;
+    const float *val = value + (size_t)b * c.n_cap;
     const size_t ms = (size_t)c.max_blocks * BLK;
     uint64_t *key = ws.cand + (size_t)b * ms;
     uint32_t *pmap = ws.pmap + (size_t)b * c.n_cap;
@@ -470,7 +535,6 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const
     int32_t *segstart = ws.segstart + (size_t)b * (ms + 1);
     int32_t *segtc = ws.segtc + (size_t)b * ms;
 
-    __shared__ int wave_tot[SEL_WAVES];
     for (int p = lo + tid; p < hi; p += SEL_THREADS) pmap[p] = 0xffffffffu;
     __syncthreads();
 
@@ -481,6 +545,7 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const
     // 2.
     const uint64_t below = (1ull << lane) - 1ull;
     int n = 0;
+    uint64_t my_s = 0;
     for (int p0 = lo; p0 < hi; p0 += SEL_THREADS * TBE_RUN) {
         const int wb = p0 + wv * 64 * TBE_RUN;
         uint32_t v[TBE_RUN];
@@ -489,7 +554,7 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const
         for (int u = 0; u < TBE_RUN; ++u) {
             const int p = wb + 64 * u + lane;
             v[u] = p < hi ? pmap[p] : 0xffffffffu;
-            im[u] = p < hi ? imp[p] : 0.0f;
+            im[u] = p < hi ? val[p] : 0.0f;
         }
         int cnt = 0;
 #pragma unroll
@@ -503,16 +568,22 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const
                 const int i = at + __popcll(bal & below);
                 ord[i] = (int32_t)v[u];
                 ob[i] = order_bits(im[u]);
+                if (sfx) {
+                    const uint32_t f = tam_fix(im[u]);
+                    sfx[i] = f;
+                    my_s += f;
+                }
             }
             at += __popcll(bal);
         }
         n += tot;
     }
+    const uint64_t s_all = sfx ? block_sum_u64(my_s, wave_u64) : 0ull;
     __syncthreads();
 
-    // 3. a start is a pool change from the previous candidate; the starts
-    //    and the Transition starts are counted together (16 bits each) for
-    //    the wave scan
+    // 3. a run starts at a pool change from the previous candidate; the
+    //    starts and the Transition starts are counted together (16 bits
+    //    each) for the wave scan
     int nseg = 0, n_t = 0;
     for (int k0 = 0; k0 < n; k0 += SEL_THREADS * TBE_RUN) {
         const int wb = k0 + wv * 64 * TBE_RUN;
@@ -523,7 +594,7 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const
             pool[u] = k < n ? (int)((uint32_t)ord[k] >> 30) : -1;
         }
         const int before0 = wb > 0 && wb <= n ? (int)((uint32_t)ord[wb - 1] >> 30) : -1;
-        uint32_t stm = 0;  // bit u: candidate of chunk u starts a segment
+        uint32_t stm = 0;  // bit u: candidate of chunk u starts a run
         int cnt = 0;
 #pragma unroll
         for (int u = 0; u < TBE_RUN; ++u) {
@@ -553,21 +624,243 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const
         nseg += tot & 0xffff;
         n_t += tot >> 16;
     }
-    if (tid == 0) {
-        segstart[nseg] = n;
-        ws.segn[2 * b] = nseg;
-        ws.segn[2 * b + 1] = n_t;
-    }
+    if (tid == 0) segstart[nseg] = n;
+    __syncthreads();
+    return SegOrder{n, nseg, n_t, s_all};
 }
 
-// evict_tbe_drop: DROP_WGS workgroups per sequence, one wave per segment
+// evict_tbe_prep: thought-adaptive eviction ("ThinKV", Methodology,
+// think-before-evict).  Segments are the runs of one thought type.  A
+// segment followed by k Transition segments keeps everything if k == 0,
+// else its best max(r_min, r0 >> (k - 1)) slots (Reasoning, Execution) or
+// t_keep slots (Transition), by importance.
+__global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const float *importance, int r0,
+                                                              int r_min, int t_keep, int q_window,
+                                                              int recent_window, EvictWs ws) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    __shared__ int wave_tot[SEL_WAVES];
+    __shared__ uint64_t wave_u64[SEL_WAVES];
+    const SegOrder so = seg_order(c, b, importance, q_window, recent_window, ws, nullptr, wave_tot, wave_u64);
+    const size_t ms = (size_t)c.max_blocks * BLK;
+    const int32_t *ord = ws.ord + (size_t)b * ms;
+    const int32_t *segstart = ws.segstart + (size_t)b * (ms + 1);
+    const int32_t *segtc = ws.segtc + (size_t)b * ms;
+    int32_t *segkeep = ws.segkeep + (size_t)b * ms;
+    for (int sg = tid; sg < so.nseg; sg += SEL_THREADS) {
+        const int later = so.n_t - segtc[sg];
+        const bool is_t = ((uint32_t)ord[segstart[sg]] >> 30) == 2u;
+        int keep = INT_MAX;
+        if (later > 0) {
+            if (is_t) {
+                keep = t_keep;
+            } else {
+                const int sh = later - 1;
+                keep = max(sh >= 31 ? 0 : (r0 >> sh), r_min);
+            }
+            keep = max(keep, 0);
+        }
+        segkeep[sg] = keep;
+    }
+    if (tid == 0) ws.segn[2 * b] = so.nseg;
+}
+
+// evict_tam_prep: thought-aware budgets ("Thought-Aware KV Cache Compaction
+// ... (TAM)", section 2), compaction read as keeping a subset of the cache.
+// value = the window score (mass from the R most recent queries), taken in
+// fixed point s (tam_fix).
+//   C. pivotal: s * N > pivot_c * S in doubles (N candidates, S the sum of
+//      their s); their order bits become 0, so they are never dropped.
+//      The budget left is T = max(0, keep_k - pivotal).
+//   A. segments: a run of one thought type with at least min_seg
+//      candidates opens a segment; a shorter run merges into the segment
+//      before it (the first run always opens one).
+//   B. per segment: n_i candidates, m_i droppable, S_i the sum of s (from
+//      running sums over the candidates); weight
+//      a_i = isqrt(floor(S_i / n_i) * 2^16) * m_i.  Rounds of
+//      capped shares: a segment with T' a_i >= m_i A (T' the budget left
+//      after the capped ones, A the sum of the uncapped weights) keeps all
+//      m_i and leaves the pool; then the uncapped ones get
+//      floor(T' C_j / A) - floor(T' C_(j-1) / A) from the running sums C_j
+//      of their weights in position order (nothing when A = 0).  All of it
+//      in integers (128-bit products), as exact as the rule.
+
+__global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const float *score,
+                                                              const int32_t *keep_k, float pivot_c, int min_seg,
+                                                              int q_window, int recent_window, EvictWs ws) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    __shared__ int wave_tot[SEL_WAVES];
+    __shared__ uint64_t wave_u64[SEL_WAVES];
+    __shared__ int s_any;
+    const size_t ms = (size_t)c.max_blocks * BLK;
+    uint32_t *sfx = ws.sfx + (size_t)b * ms;
+    const SegOrder so = seg_order(c, b, score, q_window, recent_window, ws, sfx, wave_tot, wave_u64);
+    const int n = so.n;
+    uint32_t *ob = ws.ob + (size_t)b * ms;
+    int32_t *segstart = ws.segstart + (size_t)b * (ms + 1);
+    int32_t *segkeep = ws.segkeep + (size_t)b * ms;
+    uint64_t *sega = ws.sega + (size_t)b * ms;
+    int32_t *segm = ws.segm + (size_t)b * ms;
+    uint64_t *psum = ws.psum + (size_t)b * (ms + 1);
+    int32_t *pcnt = ws.pcnt + (size_t)b * (ms + 1);
+
+    // C. pivotal candidates
+    int my_piv = 0;
+    for (int k = tid; k < n; k += SEL_THREADS) {
+        if ((double)sfx[k] * (double)n > (double)pivot_c * (double)so.s_all) {
+            ob[k] = 0u;
+            ++my_piv;
+        }
+    }
+    const long n_piv = (long)block_sum_u64((uint64_t)my_piv, wave_u64);
+    const long T = max((long)keep_k[b] - n_piv, 0L);
+
+    // A. a run of at least min_seg candidates opens a segment, a shorter one
+    //    merges into the segment before it: a block prefix over the runs
+    //    compacts the run starts that open one (each chunk reads its starts
+    //    before the prefix's barrier and writes below them after it)
+    int nseg = so.nseg;
+    if (min_seg > 1 && nseg > 1) {
+        int out = 0;
+        for (int r0 = 0; r0 < so.nseg; r0 += SEL_THREADS) {
+            const int j = r0 + tid;
+            const bool in = j < so.nseg;
+            const int st = in ? segstart[j] : 0, en = in ? segstart[j + 1] : 0;
+            const bool opens = in && (j == 0 || en - st >= min_seg);
+            int tot;
+            const int r = block_prefix(opens, wave_tot, tot);
+            if (opens) segstart[out + r] = st;
+            out += tot;
+        }
+        nseg = out;
+        __syncthreads();
+        if (tid == 0) segstart[nseg] = n;
+        __syncthreads();
+    }
+
+    // B. weights from running sums over the candidates: psum[k] = sum of s
+    //    before candidate k, pcnt[k] = droppable candidates before it, packed
+    //    in one word (s in the low 48 bits, the count above).  Each wave takes
+    //    TBE_RUN coalesced chunks of 64 candidates: its total, one scan of the
+    //    wave totals, then a wave scan per chunk.  Then a thread per segment.
+    {
+        constexpr uint64_t LOW = (1ull << 48) - 1;
+        uint64_t carry = 0;
+        for (int k0 = 0; k0 < n; k0 += SEL_THREADS * TBE_RUN) {
+            const int wb = k0 + wv * 64 * TBE_RUN;
+            uint64_t mine = 0;
+#pragma unroll
+            for (int u = 0; u < TBE_RUN; ++u) {
+                const int k = wb + 64 * u + lane;
+                if (k < n) mine += (uint64_t)sfx[k] | ((uint64_t)(ob[k] != 0u ? 1 : 0) << 48);
+            }
+#pragma unroll
+            for (int d = 32; d > 0; d >>= 1) mine += __shfl_xor(mine, d);
+            if (lane == 0) wave_u64[wv] = mine;
+            __syncthreads();
+            uint64_t run = carry, tot = 0;
+            for (int w = 0; w < SEL_WAVES; ++w) {
+                const uint64_t v = wave_u64[w];
+                run += w < wv ? v : 0ull;
+                tot += v;
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int u = 0; u < TBE_RUN; ++u) {
+                const int k = wb + 64 * u + lane;
+                const uint64_t v = k < n ? ((uint64_t)sfx[k] | ((uint64_t)(ob[k] != 0u ? 1 : 0) << 48)) : 0ull;
+                uint64_t incl = v;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const uint64_t y = __shfl_up(incl, d);
+                    incl += lane >= d ? y : 0ull;
+                }
+                if (k < n) {
+                    const uint64_t ex = run + incl - v;
+                    psum[k] = ex & LOW;
+                    pcnt[k] = (int32_t)(ex >> 48);
+                }
+                run += __shfl(incl, 63);
+            }
+            carry += tot;
+        }
+        if (tid == 0) {
+            psum[n] = carry & LOW;
+            pcnt[n] = (int32_t)(carry >> 48);
+        }
+    }
+    __syncthreads();
+    for (int sg = tid; sg < nseg; sg += SEL_THREADS) {
+        const int a = segstart[sg], e = segstart[sg + 1];
+        const uint64_t ssum = psum[e] - psum[a];
+        const int m = pcnt[e] - pcnt[a];
+        sega[sg] = isqrt_u64((ssum / (uint64_t)(e - a)) << 16) * (uint64_t)m;
+        segm[sg] = m > 0 ? m : -1;  // -m-1: capped (an empty segment keeps its 0)
+    }
+    __syncthreads();
+
+    // B. rounds of capped shares
+    uint64_t A;
+    long t_left;
+    for (;;) {
+        uint64_t my_a = 0, my_cap = 0;
+        for (int sg = tid; sg < nseg; sg += SEL_THREADS) {
+            const int m = segm[sg];
+            if (m >= 0) my_a += sega[sg];
+            else my_cap += (uint64_t)(-m - 1);
+        }
+        A = block_sum_u64(my_a, wave_u64);
+        t_left = T - (long)block_sum_u64(my_cap, wave_u64);
+        if (tid == 0) s_any = 0;
+        __syncthreads();
+        if (A > 0) {
+            for (int sg = tid; sg < nseg; sg += SEL_THREADS) {
+                const int m = segm[sg];
+                if (m >= 0 && (unsigned __int128)(uint64_t)t_left * sega[sg] >=
+                                  (unsigned __int128)(uint64_t)m * A) {
+                    segm[sg] = -m - 1;
+                    s_any = 1;
+                }
+            }
+        }
+        __syncthreads();
+        const int any = s_any;
+        __syncthreads();
+        if (!any) break;
+    }
+
+    // B. cumulative rounding over the uncapped weights, in segment order
+    uint64_t carry = 0;
+    for (int s0 = 0; s0 < nseg; s0 += SEL_THREADS) {
+        const int sg = s0 + tid;
+        const int m = sg < nseg ? segm[sg] : -1;
+        const uint64_t w = m >= 0 ? sega[sg] : 0ull;
+        uint64_t tot;
+        const uint64_t run = carry + block_scan_u64(w, wave_u64, tot);
+        if (sg < nseg) {
+            long t = (long)(-m - 1);
+            if (m >= 0) {
+                t = 0;
+                if (A > 0) {
+                    const unsigned __int128 tl = (uint64_t)t_left;
+                    const uint64_t q = (uint64_t)(tl * run / A), q0 = (uint64_t)(tl * (run - w) / A);
+                    t = (long)(q - q0);
+                }
+            }
+            segkeep[sg] = (int32_t)t;
+        }
+        carry += tot;
+    }
+    if (tid == 0) ws.segn[2 * b] = nseg;
+}
+
+// evict_seg_drop: DROP_WGS workgroups per sequence, one wave per segment
 // (segments gw, gw + DROP_WAVES, ... for the sequence's wave gw): each lane
 // loads the bounds and retention of one of the wave's next 64 segments,
 // then the wave takes them in turn (tbe_segment_any).  Spreading a
 // sequence's segments over many workgroups puts the selection, which is
 // bound by instruction issue, on every compute unit.
-__global__ __launch_bounds__(DROP_THREADS) void evict_tbe_drop(kvq_cache c, int r0, int r_min, int t_keep,
-                                                               EvictWs ws) {
+__global__ __launch_bounds__(DROP_THREADS) void evict_seg_drop(kvq_cache c, EvictWs ws) {
     const int b = blockIdx.x / DROP_WGS;
     const int gw = (blockIdx.x % DROP_WGS) * (DROP_THREADS / 64) + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -576,8 +869,8 @@ __global__ __launch_bounds__(DROP_THREADS) void evict_tbe_drop(kvq_cache c, int 
     const int32_t *ord = ws.ord + (size_t)b * ms;
     const uint32_t *ob = ws.ob + (size_t)b * ms;
     const int32_t *segstart = ws.segstart + (size_t)b * (ms + 1);
-    const int32_t *segtc = ws.segtc + (size_t)b * ms;
-    const int nseg = ws.segn[2 * b], n_t = ws.segn[2 * b + 1];
+    const int32_t *segkeep = ws.segkeep + (size_t)b * ms;
+    const int nseg = ws.segn[2 * b];
     __shared__ uint32_t s_hist[DROP_THREADS / 64][256];
     for (int s0 = gw; s0 < nseg; s0 += DROP_WAVES * 64) {
         const int my = s0 + DROP_WAVES * lane;
@@ -585,18 +878,7 @@ __global__ __launch_bounds__(DROP_THREADS) void evict_tbe_drop(kvq_cache c, int 
         if (my < nseg) {
             ma = segstart[my];
             me = segstart[my + 1];
-            const int later = n_t - segtc[my];
-            const bool is_t = ((uint32_t)ord[ma] >> 30) == 2u;
-            mkeep = INT_MAX;
-            if (later > 0) {
-                if (is_t) {
-                    mkeep = t_keep;
-                } else {
-                    const int sh = later - 1;
-                    mkeep = max(sh >= 31 ? 0 : (r0 >> sh), r_min);
-                }
-                mkeep = max(mkeep, 0);
-            }
+            mkeep = segkeep[my];
         }
         const int cnt = min(64, (nseg - s0 + DROP_WAVES - 1) / DROP_WAVES);
         for (int j = 0; j < cnt; ++j) {
@@ -608,9 +890,9 @@ __global__ __launch_bounds__(DROP_THREADS) void evict_tbe_drop(kvq_cache c, int 
     }
 }
 
-// evict_tbe_compact: clear the dropped slots (word 2) and compact the table
+// evict_seg_compact: clear the dropped slots (word 2) and compact the table
 // row as evict_select does, one workgroup per sequence.
-__global__ __launch_bounds__(SEL_THREADS) void evict_tbe_compact(kvq_cache c, EvictWs ws) {
+__global__ __launch_bounds__(SEL_THREADS) void evict_seg_compact(kvq_cache c, EvictWs ws) {
     const int b = blockIdx.x, tid = threadIdx.x;
     const int nb = c.n_blocks[b];
     uint32_t *row = c.table + (size_t)b * c.max_blocks;
@@ -681,10 +963,21 @@ bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *ke
 bool launch_evict_tbe(const kvq_cache &c, const float *importance, int r0, int r_min, int t_keep,
                       int q_window, int recent_window, void *ws_ptr, hipStream_t s) {
     EvictWs ws(ws_ptr, c);
-    hipLaunchKernelGGL(evict_tbe_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, q_window,
-                       recent_window, ws);
-    hipLaunchKernelGGL(evict_tbe_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, r0, r_min, t_keep, ws);
-    hipLaunchKernelGGL(evict_tbe_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_tbe_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, r0, r_min, t_keep,
+                       q_window, recent_window, ws);
+    hipLaunchKernelGGL(evict_seg_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);
+    return hipGetLastError() == hipSuccess;
+}
+
+bool launch_evict_tam(const kvq_cache &c, const float *score, const int32_t *keep_k, float pivot_c,
+                      int min_seg, int q_window, int recent_window, void *ws_ptr, hipStream_t s) {
+    EvictWs ws(ws_ptr, c);
+    hipLaunchKernelGGL(evict_tam_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, score, keep_k, pivot_c, min_seg,
+                       q_window, recent_window, ws);
+    hipLaunchKernelGGL(evict_seg_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws);
     hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);
     return hipGetLastError() == hipSuccess;
 }

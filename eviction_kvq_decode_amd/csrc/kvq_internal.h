@@ -77,29 +77,41 @@ struct EvictWs {
     // segment-granular eviction only: candidates in position order
     uint32_t *pmap;    // [B][n_cap] (pool << 30) | slot of the candidate at a position, or ~0
     int32_t *ord;      // [B][max_blocks*16] (pool << 30) | slot of the candidates, by position
-    uint32_t *ob;      // [B][max_blocks*16] their importance as order bits, same order
+    uint32_t *ob;      // [B][max_blocks*16] their importance as order bits (0: never dropped)
+    uint32_t *sfx;     // [B][max_blocks*16] their window score in fixed point (budgets)
     int32_t *segstart; // [B][max_blocks*16 + 1] first candidate of each segment
     int32_t *segtc;    // [B][max_blocks*16] Transition segments up to and including each segment
+    int32_t *segkeep;  // [B][max_blocks*16] how many droppable candidates each segment keeps
+    uint64_t *sega;    // [B][max_blocks*16] budget weight of each segment
+    int32_t *segm;     // [B][max_blocks*16] droppable candidates of each segment (-m-1: capped)
+    uint64_t *psum;    // [B][max_blocks*16 + 1] running sum of sfx before each candidate
+    int32_t *pcnt;     // [B][max_blocks*16 + 1] droppable candidates before each candidate
     int32_t *segn;     // [B][2] segments, Transition segments
     static size_t bytes(const kvq_cache &c) {
-        const size_t ms = (size_t)c.max_blocks * 16;
+        const size_t ms = (size_t)c.max_blocks * 16, slot4 = align256(4L * c.B * ms);
         return align256(8L * c.B * ms) + align256(4L * c.B * c.max_blocks) + align256(16L * c.B) +
-               align256(16) + align256(4L * c.B * c.n_cap) + align256(4L * c.B * ms) +
-               align256(4L * c.B * ms) + align256(4L * c.B * (ms + 1)) + align256(4L * c.B * ms) +
-               align256(8L * c.B);
+               align256(16) + align256(4L * c.B * c.n_cap) + 3 * slot4 + align256(4L * c.B * (ms + 1)) +
+               2 * slot4 + align256(8L * c.B * ms) + slot4 + align256(8L * c.B * (ms + 1)) +
+               align256(4L * c.B * (ms + 1)) + align256(8L * c.B);
     }
     EvictWs(void *ws, const kvq_cache &c) {
-        const size_t ms = (size_t)c.max_blocks * 16;
+        const size_t ms = (size_t)c.max_blocks * 16, slot4 = align256(4L * c.B * ms);
         char *p = (char *)ws;
         cand = (uint64_t *)p;     p += align256(8L * c.B * ms);
         freed = (uint32_t *)p;    p += align256(4L * c.B * c.max_blocks);
         nfreed = (int32_t *)p;    p += align256(16L * c.B);
         top = (int32_t *)p;       p += align256(16);
         pmap = (uint32_t *)p;     p += align256(4L * c.B * c.n_cap);
-        ord = (int32_t *)p;       p += align256(4L * c.B * ms);
-        ob = (uint32_t *)p;       p += align256(4L * c.B * ms);
+        ord = (int32_t *)p;       p += slot4;
+        ob = (uint32_t *)p;       p += slot4;
+        sfx = (uint32_t *)p;      p += slot4;
         segstart = (int32_t *)p;  p += align256(4L * c.B * (ms + 1));
-        segtc = (int32_t *)p;     p += align256(4L * c.B * ms);
+        segtc = (int32_t *)p;     p += slot4;
+        segkeep = (int32_t *)p;   p += slot4;
+        sega = (uint64_t *)p;     p += align256(8L * c.B * ms);
+        segm = (int32_t *)p;      p += slot4;
+        psum = (uint64_t *)p;     p += align256(8L * c.B * (ms + 1));
+        pcnt = (int32_t *)p;      p += align256(4L * c.B * (ms + 1));
         segn = (int32_t *)p;
     }
 };
@@ -113,5 +125,7 @@ bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *ke
                   int recent_window, void *ws, hipStream_t s);
 bool launch_evict_tbe(const kvq_cache &c, const float *importance, int r0, int r_min, int t_keep,
                       int q_window, int recent_window, void *ws, hipStream_t s);
+bool launch_evict_tam(const kvq_cache &c, const float *score, const int32_t *keep_k, float pivot_c,
+                      int min_seg, int q_window, int recent_window, void *ws, hipStream_t s);
 
 }  // namespace kvq

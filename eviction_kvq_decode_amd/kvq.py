@@ -19,7 +19,8 @@ KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EHIP, KVQ_ENOSPC = 0, -1, -2, -3, -4
 TAG_R, TAG_E, TAG_T, TAG_NONE = 0, 1, 2, 255
 
 EXPORTS = ("kvq_region_bytes", "kvq_workspace_bytes", "kvq_append_quantize",
-           "kvq_decode_attention", "kvq_evict_topk", "kvq_evict_tbe")
+           "kvq_decode_attention", "kvq_evict_topk", "kvq_evict_tbe",
+           "kvq_evict_tam")
 
 
 class KvqError(RuntimeError):
@@ -63,6 +64,9 @@ def lib():
         L.kvq_evict_tbe.restype = ctypes.c_int
         L.kvq_evict_tbe.argtypes = [CS, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, P, ctypes.c_size_t, P]
+        L.kvq_evict_tam.restype = ctypes.c_int
+        L.kvq_evict_tam.argtypes = [CS, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -144,6 +148,13 @@ class Cache:
         _check(lib().kvq_evict_tbe(ctypes.byref(self.struct), _ptr(importance), int(r0), int(r_min),
                                    int(t_keep), int(q_window), int(recent_window), self.ws_ptr,
                                    self.ws_bytes, self._stream(stream)), "kvq_evict_tbe")
+
+    def evict_tam(self, score, keep_k, pivot_c, min_seg, q_window, recent_window, stream=None):
+        """kvq_evict_tam: thought-aware segment budgets (score fp32 [B][n_cap],
+        keep_k int32 [B], device tensors)."""
+        _check(lib().kvq_evict_tam(ctypes.byref(self.struct), _ptr(score), _ptr(keep_k), float(pivot_c),
+                                   int(min_seg), int(q_window), int(recent_window), self.ws_ptr,
+                                   self.ws_bytes, self._stream(stream)), "kvq_evict_tam")
 
     def state_numpy(self) -> dict:
         """Host copy of every cache array (synchronises)."""

@@ -188,6 +188,41 @@ kvq_status kvq_evict_tbe(const kvq_cache *cache, const float *importance, int32_
                          int32_t recent_window, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/*
+ * Thought-aware segment budgets ("Thought-Aware KV Cache Compaction for
+ * Reasoning via Adaptive Attention Matching (TAM)", section 2: A thought
+ * segmentation, B adaptive budget allocation, C pivotal-token protection),
+ * with compaction read as keeping a subset of the cached tokens.
+ *   score   : fp32 [B][n_cap], the attention mass each position received
+ *             from the selection window (the R most recent queries; e.g.
+ *             the importance accumulated by R decode calls with decay 1
+ *             from zero), read at the positions of valid slots; taken in
+ *             fixed point s = floor(score * 2^16) for 0 < score < 2^16,
+ *             2^32 - 1 above, 0 for score <= 0
+ *   keep_k  : int32 [B] token budget per sequence (the windows aside)
+ *   pivot_c : >= 0 (+inf: no pivotal tokens)
+ *   min_seg : >= 1
+ * Per sequence, the valid slots with q_window <= pos < seq_len -
+ * recent_window are the candidates; the others are kept.  A candidate is
+ * pivotal if s * N > pivot_c * S (in doubles; N candidates, S the sum of
+ * their s) and is kept; the budget left, T = max(0, keep_k - pivotal), goes
+ * to the others.  In position order the candidates form segments: a change
+ * of thought type opens a new segment once the open one holds min_seg
+ * candidates.  Segment i (n_i candidates, m_i not pivotal, S_i the sum of
+ * their s) has weight a_i = isqrt(floor(S_i / n_i) * 2^16) * m_i, that is
+ * sqrt(mean score) * m_i.  A segment whose share T' a_i / A reaches m_i
+ * (T' the budget left after such segments, A the sum of the others'
+ * weights) keeps all m_i, and the shares are recomputed without it until
+ * none does; the others keep floor(T' C_j / A) - floor(T' C_(j-1) / A),
+ * C_j the running sum of their weights in position order (none if A = 0).
+ * A segment keeps its pivotal candidates and that many others of largest
+ * score (ties: lower position).  The rest are evicted, and the table is
+ * compacted and emptied blocks are freed as in kvq_evict_topk.
+ */
+kvq_status kvq_evict_tam(const kvq_cache *cache, const float *score, const int32_t *keep_k,
+                         float pivot_c, int32_t min_seg, int32_t q_window, int32_t recent_window,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,6 +84,7 @@ def test_host_side_validation(over, code):
     assert L.kvq_decode_attention(ctypes.byref(s), buf, buf, buf, None, 0.9, 0.1, buf, 1 << 40, None) == code
     assert L.kvq_evict_topk(ctypes.byref(s), buf, buf, 0, 0, buf, 1 << 40, None) == code
     assert L.kvq_evict_tbe(ctypes.byref(s), buf, 64, 1, 4, 0, 0, buf, 1 << 40, None) == code
+    assert L.kvq_evict_tam(ctypes.byref(s), buf, buf, 2.0, 1, 0, 0, buf, 1 << 40, None) == code
 
 
 def test_bad_arguments_rejected_before_launch():
@@ -102,3 +103,10 @@ def test_bad_arguments_rejected_before_launch():
     assert L.kvq_evict_tbe(ctypes.byref(s), ok, 64, 1, -4, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_tbe(ctypes.byref(s), ok, 64, 1, 4, 0, -1, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_tbe(ctypes.byref(s), ok, 64, 1, 4, 0, 0, ok, need - 1, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tam(ctypes.byref(s), None, ok, 2.0, 1, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tam(ctypes.byref(s), ok, None, 2.0, 1, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, -1.0, 1, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, float("nan"), 1, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, 2.0, 0, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, 2.0, 1, -1, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, 2.0, 1, 0, 0, ok, need - 1, None) == kvq.KVQ_EINVAL
