@@ -61,6 +61,7 @@ class Workload:
     extra_steps: int = 64           # head-room for extra appended tokens
     period: int = 0                 # continuous-thinking loop: evict every `period` appends
     loop_steps: int = 0             # and run this many append+decode steps
+    codec: int = 0                  # 1: ThinKV's FP8 / FP4 / ternary formats
 
     @property
     def G(self) -> int:
@@ -230,6 +231,7 @@ class Geometry:
     max_blocks: int
     n_cap: int
     pool_blocks: tuple
+    codec: int = 0   # 0: integer min/max codes; 1: ThinKV's FP8 / FP4 / ternary formats
 
     def region_bytes(self, pool: int) -> int:
         return region_bytes(POOL_BITS[pool])
@@ -247,7 +249,7 @@ def geometry_for(w: Workload, all_tags: list | None = None, spare_per_seq: int =
             counts[p] += int(math.ceil(int((tags == p).sum()) / BLK))
     spare = w.B * (spare_per_seq + int(math.ceil(extra / BLK)))
     pool_blocks = tuple(int(c + spare) for c in counts)
-    return Geometry(w.B, w.Hq, w.Hkv, max_blocks, int(n.max()) + extra, pool_blocks)
+    return Geometry(w.B, w.Hq, w.Hkv, max_blocks, int(n.max()) + extra, pool_blocks, w.codec)
 
 
 def empty_state(g: Geometry, identity_ids: bool, seed_key=(0,)) -> dict:

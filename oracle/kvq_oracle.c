@@ -154,6 +154,107 @@ void orc_quantize_group(const uint16_t *x, int bits, uint16_t *scale_h,
 }
 
 /* ------------------------------------------------------------------ */
+/* ThinKV's own formats [ThinKV, Methodology, TBQ]: FP8 for Reasoning,  */
+/* FP4 for Execution, ternary for Transition                          */
+/* ------------------------------------------------------------------ */
+
+/* A sign-magnitude minifloat with E exponent bits (bias), M mantissa bits,
+ * subnormals at exponent field 0 and no infinities: the OCP formats
+ * E4M3 (bias 7, largest magnitude code 0x7E = 448; 0x7F is NaN) and E2M1
+ * (bias 1, largest 7 = 6).  Value of a magnitude code. */
+double orc_mini_value(unsigned mag, int E, int M, int bias)
+{
+    unsigned e = mag >> M, m = mag & ((1u << M) - 1);
+    if (e == 0)
+        return ldexp((double)m, 1 - bias - M);
+    return ldexp(1.0 + ldexp((double)m, -M), (int)e - bias);
+}
+
+/* Nearest code to y (ties to the even code), magnitudes above the largest
+ * code saturating to it; the sign bit is set only for a nonzero magnitude
+ * of a negative y. */
+unsigned orc_mini_encode(float y, int E, int M, int bias, unsigned max_mag)
+{
+    double a = fabs((double)y);
+    unsigned mag;
+    double emin_pow = ldexp(1.0, 1 - bias);        /* least normal magnitude */
+    if (a < emin_pow) {
+        /* subnormal grid, step 2^(1 - bias - M); q == 2^M is the least normal */
+        mag = (unsigned)nearbyint(ldexp(a, bias - 1 + M));
+    } else {
+        int ex;
+        frexp(a, &ex);                             /* a in [2^(ex-1), 2^ex) */
+        int e = ex - 1;
+        double q = nearbyint(ldexp(a, M - e));     /* M+1 significant bits */
+        if (q == ldexp(1.0, M + 1)) {
+            q = ldexp(1.0, M);
+            e += 1;
+        }
+        long eb = (long)e + bias;
+        if (eb > (1L << E) - 1)
+            mag = max_mag;
+        else
+            mag = (unsigned)((eb << M) | (long)(q - ldexp(1.0, M)));
+    }
+    if (mag > max_mag)
+        mag = max_mag;
+    unsigned sign = (y < 0.0f && mag != 0) ? 1u : 0u;
+    return (sign << (E + M)) | mag;
+}
+
+static const int MINI_E[2] = {4, 2}, MINI_M[2] = {3, 1}, MINI_BIAS[2] = {7, 1};
+static const unsigned MINI_MAX[2] = {0x7e, 0x7};
+static const float MINI_TOP[2] = {448.0f, 6.0f};
+
+/* Value of a native code of pool 0 (E4M3) or 1 (E2M1), before the scale. */
+double orc_native_value(int pool, unsigned code)
+{
+    int E = MINI_E[pool], M = MINI_M[pool];
+    double v = orc_mini_value(code & ((1u << (E + M)) - 1), E, M, MINI_BIAS[pool]);
+    return (code >> (E + M)) & 1 ? -v : v;
+}
+
+/* Symmetric group quantisation in the native formats.  amax = max |x|
+ * (-0 as +0); scale = the least fp16 >= amax / top in fp32 (top = 448, 6,
+ * 1 for E4M3, E2M1, ternary); y = x / scale in fp32.  Pools 0 and 1 store
+ * the minifloat code of y and zero 0 (x^ = value(code) * scale).  Pool 2
+ * stores t + 1 for t = rint(y) clamped to [-1, 1] (ties to even) and
+ * zero = -scale, so that x^ = code * scale + zero is -scale, 0 or +scale.
+ * A group of zeros stores scale 0, zero 0 and the code of 0. */
+void orc_quantize_group_native(const uint16_t *x, int pool, uint16_t *scale_h, uint16_t *zero_h,
+                               uint8_t *codes)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < GS; ++i) {
+        float v = fabsf((float)orc_half_to_double(x[i]));
+        if (v > amax) amax = v;
+    }
+    float top = pool == 2 ? 1.0f : MINI_TOP[pool];
+    float s32 = amax / top;
+    uint16_t sh = orc_float_to_half(s32);
+    if (orc_half_to_double(sh) < (double)s32)
+        sh = (uint16_t)(sh + 1);
+    *scale_h = sh;
+    *zero_h = (pool == 2 && sh != 0) ? (uint16_t)(sh | 0x8000) : 0;
+    float sc = (float)orc_half_to_double(sh);
+    for (int i = 0; i < GS; ++i) {
+        if (sc == 0.0f) {
+            codes[i] = pool == 2 ? 1 : 0;
+            continue;
+        }
+        float y = (float)orc_half_to_double(x[i]) / sc;
+        if (pool == 2) {
+            float t = rintf(y);
+            if (t < -1.0f) t = -1.0f;
+            if (t > 1.0f) t = 1.0f;
+            codes[i] = (uint8_t)(t + 1.0f);
+        } else {
+            codes[i] = (uint8_t)orc_mini_encode(y, MINI_E[pool], MINI_M[pool], MINI_BIAS[pool], MINI_MAX[pool]);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Cache format (one region per (pool, block, kv head))                 */
 /*   [K codes 256*b B][V codes 256*b B][K (scale,zero) 256 B][V ... ]    */
 /* ------------------------------------------------------------------ */
@@ -219,6 +320,7 @@ static const uint16_t *sz_ptr(const uint8_t *region, int bits, int is_v, int t, 
 typedef struct {
     int32_t B, Hq, Hkv, max_blocks, n_cap;
     int32_t pool_blocks[3];
+    int32_t codec;           /* 0 integer min/max, 1 ThinKV's formats */
     uint8_t *kv[3];          /* [pool_blocks][Hkv] regions            */
     uint16_t *mask[3];       /* [pool_blocks] valid-slot bitmask      */
     int32_t *pos[3];         /* [pool_blocks][16] logical positions   */
@@ -246,13 +348,19 @@ static void write_token(orc_cache *c, int pool, uint32_t id, int h, int t,
         uint16_t sc, zr;
         uint8_t codes[GS];
         uint16_t *kz = (uint16_t *)sz_ptr(reg, bits, 0, t, g);
-        orc_quantize_group(k + g * GS, bits, &sc, &zr, codes);
+        if (c->codec == 1)
+            orc_quantize_group_native(k + g * GS, pool, &sc, &zr, codes);
+        else
+            orc_quantize_group(k + g * GS, bits, &sc, &zr, codes);
         kz[0] = sc;
         kz[1] = zr;
         for (int i = 0; i < GS; ++i)
             put_code(kc, orc_k_bit_offset(bits, t, g * GS + i), bits, codes[i]);
         uint16_t *vz = (uint16_t *)sz_ptr(reg, bits, 1, t, g);
-        orc_quantize_group(v + g * GS, bits, &sc, &zr, codes);
+        if (c->codec == 1)
+            orc_quantize_group_native(v + g * GS, pool, &sc, &zr, codes);
+        else
+            orc_quantize_group(v + g * GS, bits, &sc, &zr, codes);
         vz[0] = sc;
         vz[1] = zr;
         for (int i = 0; i < GS; ++i)
@@ -260,7 +368,8 @@ static void write_token(orc_cache *c, int pool, uint32_t id, int h, int t,
     }
 }
 
-/* Dequantised K and V of slot t for kv head h, in fp64: x = code*scale + zero. */
+/* Dequantised K and V of slot t for kv head h, in fp64: x = code*scale + zero,
+ * or for the native formats of pools 0 and 1, value(code)*scale + zero. */
 void orc_dequant_slot(const orc_cache *c, int pool, uint32_t id, int h, int t,
                       double *k_out, double *v_out)
 {
@@ -272,8 +381,13 @@ void orc_dequant_slot(const orc_cache *c, int pool, uint32_t id, int h, int t,
         const uint16_t *vz = sz_ptr(reg, bits, 1, t, d / GS);
         unsigned ck = get_code(kc, orc_k_bit_offset(bits, t, d), bits);
         unsigned cv = get_code(vc, orc_v_bit_offset(bits, t, d), bits);
-        if (k_out) k_out[d] = ck * orc_half_to_double(kz[0]) + orc_half_to_double(kz[1]);
-        if (v_out) v_out[d] = cv * orc_half_to_double(vz[0]) + orc_half_to_double(vz[1]);
+        double qk = ck, qv = cv;
+        if (c->codec == 1 && pool < 2) {
+            qk = orc_native_value(pool, ck);
+            qv = orc_native_value(pool, cv);
+        }
+        if (k_out) k_out[d] = qk * orc_half_to_double(kz[0]) + orc_half_to_double(kz[1]);
+        if (v_out) v_out[d] = qv * orc_half_to_double(vz[0]) + orc_half_to_double(vz[1]);
     }
 }
 
@@ -852,6 +966,26 @@ void orc_float_to_half_array(const float *f, uint16_t *out, long n)
 {
     for (long i = 0; i < n; ++i)
         out[i] = orc_float_to_half(f[i]);
+}
+
+/* Native formats, array forms (pool 0 E4M3, 1 E2M1, 2 ternary). */
+void orc_quantize_groups_native(const uint16_t *x, long n_groups, int pool, uint16_t *scale,
+                                uint16_t *zero, uint8_t *codes)
+{
+    for (long i = 0; i < n_groups; ++i)
+        orc_quantize_group_native(x + i * GS, pool, scale + i, zero + i, codes + i * GS);
+}
+
+void orc_native_values(int pool, const uint8_t *codes, long n, double *out)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = orc_native_value(pool, codes[i]);
+}
+
+void orc_mini_encode_array(const float *y, long n, int pool, uint8_t *out)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = (uint8_t)orc_mini_encode(y[i], MINI_E[pool], MINI_M[pool], MINI_BIAS[pool], MINI_MAX[pool]);
 }
 
 /* x: fp16 [n_groups][32] -> scale, zero [n_groups], codes [n_groups][32] */

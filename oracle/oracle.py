@@ -36,7 +36,7 @@ class _Cache(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
         ("max_blocks", ctypes.c_int32), ("n_cap", ctypes.c_int32),
-        ("pool_blocks", ctypes.c_int32 * 3),
+        ("pool_blocks", ctypes.c_int32 * 3), ("codec", ctypes.c_int32),
         ("kv", ctypes.c_void_p * 3), ("mask", ctypes.c_void_p * 3), ("pos", ctypes.c_void_p * 3),
         ("table", ctypes.c_void_p), ("n_blocks", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
         ("free_ids", ctypes.c_void_p * 3), ("free_top", ctypes.c_void_p), ("status", ctypes.c_void_p),
@@ -57,6 +57,9 @@ def lib():
         L.orc_half_to_double_array.argtypes = [P, P, ctypes.c_long]
         L.orc_float_to_half_array.argtypes = [P, P, ctypes.c_long]
         L.orc_quantize_groups.argtypes = [P, ctypes.c_long, ctypes.c_int, P, P, P]
+        L.orc_quantize_groups_native.argtypes = [P, ctypes.c_long, ctypes.c_int, P, P, P]
+        L.orc_native_values.argtypes = [ctypes.c_int, P, ctypes.c_long, P]
+        L.orc_mini_encode_array.argtypes = [P, ctypes.c_long, ctypes.c_int, P]
         L.orc_k_row_index.restype = ctypes.c_int
         L.orc_k_row_index.argtypes = [ctypes.c_int, ctypes.c_int]
         L.orc_k_bit_offset.restype = ctypes.c_long
@@ -118,6 +121,34 @@ def quantize_groups(x_fp16: np.ndarray, bits: int):
     return sc, zr, codes
 
 
+def quantize_groups_native(x_fp16: np.ndarray, pool: int):
+    """ThinKV's formats (pool 0 E4M3, 1 E2M1, 2 ternary): x fp16 [..., 32] ->
+    (scale bits, zero bits, codes)."""
+    x = np.ascontiguousarray(x_fp16, dtype=np.float16).view(np.uint16)
+    assert x.shape[-1] == 32
+    sc = np.empty(x.shape[:-1], dtype=np.uint16)
+    zr = np.empty(x.shape[:-1], dtype=np.uint16)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_quantize_groups_native(_p(x), x.size // 32, int(pool), _p(sc), _p(zr), _p(codes))
+    return sc, zr, codes
+
+
+def native_values(pool: int, codes: np.ndarray) -> np.ndarray:
+    """Values of E4M3 (pool 0) or E2M1 (pool 1) codes, before the scale."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib().orc_native_values(int(pool), _p(c), c.size, _p(out))
+    return out
+
+
+def mini_encode(y: np.ndarray, pool: int) -> np.ndarray:
+    """Nearest E4M3 (pool 0) or E2M1 (pool 1) code of fp32 values."""
+    yy = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(yy.shape, dtype=np.uint8)
+    lib().orc_mini_encode_array(_p(yy), yy.size, int(pool), _p(out))
+    return out
+
+
 def k_bit_offset(bits: int, t: int, d: int) -> int:
     return lib().orc_k_bit_offset(bits, t, d)
 
@@ -145,6 +176,7 @@ class OracleCache:
         s = _Cache()
         g, st = self.g, self.st
         s.B, s.Hq, s.Hkv, s.max_blocks, s.n_cap = g.B, g.Hq, g.Hkv, g.max_blocks, g.n_cap
+        s.codec = getattr(g, "codec", 0)
         for p in range(3):
             s.pool_blocks[p] = g.pool_blocks[p]
             s.kv[p] = _p(st[f"kv{p}"])

@@ -12,7 +12,7 @@ HD = 128
 BLK = 16
 
 
-def small_geometry(B, Hq, Hkv, n_max, pool_blocks=None, max_blocks=None, n_cap=None):
+def small_geometry(B, Hq, Hkv, n_max, pool_blocks=None, max_blocks=None, n_cap=None, codec=0):
     if max_blocks is None:
         max_blocks = math.ceil(n_max / BLK) + 8
     if pool_blocks is None:
@@ -20,7 +20,7 @@ def small_geometry(B, Hq, Hkv, n_max, pool_blocks=None, max_blocks=None, n_cap=N
         pool_blocks = (pb, pb, pb)
     if n_cap is None:
         n_cap = n_max + 64
-    return wl.Geometry(B, Hq, Hkv, max_blocks, n_cap, tuple(pool_blocks))
+    return wl.Geometry(B, Hq, Hkv, max_blocks, n_cap, tuple(pool_blocks), codec)
 
 
 def oracle_cache(g, identity_ids=False, seed_key=(0,)):
