@@ -403,6 +403,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_evicted")
+    ap.add_argument("--codec", choices=("int", "native"), default="int",
+                    help="integer min/max codes, or ThinKV's E4M3 / E2M1 / ternary formats")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -423,6 +425,8 @@ def main():
     kvq.lib()
     torch.cuda.set_device(0)
     w = wl.WORKLOADS[args.workload]
+    if args.codec == "native":
+        w = wl.scaled(w, codec=1)
     if w.period:
         ct_bench(args, w)
         return
@@ -510,11 +514,13 @@ def main():
         "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, "
                                f"{int(n.max())} logical positions/seq, "
                                f"{100 * (1 - toks.keep[:, : int(n.max())].mean()):.0f}% evicted, "
-                               f"R/E/T at 8/4/2 bits; step = append 1 token/seq + decode",
+                               + ("R/E/T as E4M3/E2M1/ternary" if w.codec else "R/E/T at 8/4/2 bits")
+                               + "; step = append 1 token/seq + decode",
                    "global_batch": B, "seq_len": int(n.max()),
                    "compressed_kv_mb_per_step": round(dec_bytes[-1] / 1e6, 1)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": committed_traffic(args.workload),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": committed_traffic(args.workload) if not w.codec else None,
                      "kernel": "kvq_decode_attention (split + finalize)",
                      "avg_us": float(np.mean(dec_ms) * 1e3)},
         "cpu_baseline": None,

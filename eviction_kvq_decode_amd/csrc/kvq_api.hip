@@ -15,6 +15,7 @@ kvq_status check_cache(const kvq_cache *c) {
     if (c->B < 1 || c->Hkv < 1 || c->Hq < 1 || c->Hq % c->Hkv != 0) return KVQ_EINVAL;
     if (c->Hq / c->Hkv > KVQ_MAX_GQA || c->Hq > 256 || c->B > 1024) return KVQ_EUNSUPPORTED;
     if (c->max_blocks < 1 || c->n_cap < 1) return KVQ_EINVAL;
+    if (c->codec != KVQ_CODEC_INT && c->codec != KVQ_CODEC_NATIVE) return KVQ_EINVAL;
     for (int p = 0; p < 3; ++p) {
         if (c->pool_blocks[p] < 0 || c->pool_blocks[p] >= (1 << 30)) return KVQ_EINVAL;
         if (c->pool_blocks[p] > 0 && (!c->kv[p] || !c->mask[p] || !c->pos[p] || !c->free_ids[p]))

@@ -111,6 +111,68 @@ __device__ inline void quantise_pair(uint32_t two, int bits, uint32_t &c0, uint3
     scale_zero = (uint32_t)sh | ((uint32_t)f2h_rn(mn) << 16);
 }
 
+// Nearest code of y in a sign-magnitude minifloat with E exponent bits, M
+// mantissa bits and the given bias (subnormals at exponent field 0, no
+// infinities), ties to the even code, magnitudes saturating at max_mag;
+// the sign bit only for a nonzero magnitude of a negative y.  Normal range:
+// the fp32 mantissa rounded to M bits on its bit pattern (a carry moves into
+// the exponent); below it, the subnormal grid by an exact power-of-two
+// scaling and rintf.
+template <int E, int M, int BIAS>
+__device__ inline uint32_t minifloat_code(float y, uint32_t max_mag) {
+    const float a = fabsf(y);
+    constexpr float least_normal = BIAS == 7 ? 0.015625f : 1.0f;  // 2^(1 - BIAS)
+    constexpr float to_steps = BIAS == 7 ? 512.0f : 2.0f;         // 2^(BIAS - 1 + M)
+    uint32_t mag;
+    if (a < least_normal) {
+        mag = (uint32_t)rintf(a * to_steps);
+    } else {
+        constexpr int drop = 23 - M;
+        uint32_t u = __float_as_uint(a);
+        u += (1u << (drop - 1)) - 1u + ((u >> drop) & 1u);
+        const int eb = (int)(u >> 23) - 127 + BIAS;
+        mag = eb > (1 << E) - 1 ? max_mag : ((uint32_t)eb << M) | ((u >> drop) & ((1u << M) - 1u));
+    }
+    mag = min(mag, max_mag);
+    return (y < 0.0f && mag != 0u ? 1u << (E + M) : 0u) | mag;
+}
+
+// ThinKV's own formats ("ThinKV", Methodology, TBQ), same row layout:
+// symmetric groups of 32 with scale = least fp16 >= max|x| / top (top 448,
+// 6, 1); pool 0 stores E4M3 codes of x / scale, pool 1 E2M1 codes, both
+// with zero 0; pool 2 stores t + 1 for t = rint(x / scale) in [-1, 1] with
+// zero = -scale (so the integer decode gives -scale, 0, +scale).  A group
+// of zeros stores scale 0, zero 0 and the code of 0.
+__device__ inline void quantise_pair_native(uint32_t two, int pool, uint32_t &c0, uint32_t &c1,
+                                            uint32_t &scale_zero) {
+    const float x0 = h2f((uint16_t)(two & 0xffff)), x1 = h2f((uint16_t)(two >> 16));
+    float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float top = pool == 0 ? 448.0f : pool == 1 ? 6.0f : 1.0f;
+    const float s32 = amax / top;
+    uint16_t sh = f2h_rn(s32);
+    if (h2f(sh) < s32) sh = (uint16_t)(sh + 1);
+    const float sc = h2f(sh);
+    const uint16_t zh = pool == 2 && sh != 0 ? (uint16_t)(sh | 0x8000u) : (uint16_t)0;
+    if (sc == 0.0f) {
+        c0 = c1 = pool == 2 ? 1u : 0u;
+    } else {
+        const float y0 = x0 / sc, y1 = x1 / sc;
+        if (pool == 0) {
+            c0 = minifloat_code<4, 3, 7>(y0, 0x7eu);
+            c1 = minifloat_code<4, 3, 7>(y1, 0x7eu);
+        } else if (pool == 1) {
+            c0 = minifloat_code<2, 1, 1>(y0, 0x7u);
+            c1 = minifloat_code<2, 1, 1>(y1, 0x7u);
+        } else {
+            c0 = (uint32_t)(fminf(fmaxf(rintf(y0), -1.0f), 1.0f) + 1.0f);
+            c1 = (uint32_t)(fminf(fmaxf(rintf(y1), -1.0f), 1.0f) + 1.0f);
+        }
+    }
+    scale_zero = (uint32_t)sh | ((uint32_t)zh << 16);
+}
+
 __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *k_new,
                                                    const uint16_t *v_new, AppendWs ws) {
     const int b = blockIdx.x / c.Hkv, h = blockIdx.x % c.Hkv;
@@ -156,8 +218,13 @@ __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *
     __shared__ uint8_t kcode[HD];  // by K-row code index
     __shared__ uint8_t vcode[HD];  // by channel
     uint32_t k0, k1, ksz, v0, v1, vsz;
-    quantise_pair(k_two, bits, k0, k1, ksz);
-    quantise_pair(v_two, bits, v0, v1, vsz);
+    if (c.codec == KVQ_CODEC_NATIVE) {
+        quantise_pair_native(k_two, pool, k0, k1, ksz);
+        quantise_pair_native(v_two, pool, v0, v1, vsz);
+    } else {
+        quantise_pair(k_two, bits, k0, k1, ksz);
+        quantise_pair(v_two, bits, v0, v1, vsz);
+    }
     kcode[k_row_index(bits, 2 * lane)] = (uint8_t)k0;
     kcode[k_row_index(bits, 2 * lane + 1)] = (uint8_t)k1;
     vcode[2 * lane] = (uint8_t)v0;

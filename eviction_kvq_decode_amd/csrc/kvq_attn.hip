@@ -91,13 +91,44 @@ __device__ inline uint32_t opaque_bias() {
     return vb;
 }
 
+// ThinKV's own formats (the native codec) as exact fp16 operands, no bias:
+// a code's sign goes to bit 15 and its exponent and mantissa bits to the
+// top of fp16's, which reads as value * 2^-8 (E4M3) or value * 2^-14
+// (E2M1), a subnormal for the formats' subnormals; one packed multiply by
+// the power of two then gives the value itself, a normal fp16 (every E4M3
+// and E2M1 value is one), so no operand reaches the MFMA subnormal.
+__device__ inline uint32_t scale_pair(uint32_t x, float f) {
+    half2v h = __builtin_bit_cast(half2v, x);
+    h = h * (half2v){(_Float16)f, (_Float16)f};
+    return __builtin_bit_cast(uint32_t, h);
+}
+// E4M3 codes in bytes i and j of w as an fp16 pair.
+__device__ inline uint32_t e4m3_pair(uint32_t w, int i, int j) {
+    const uint32_t sel = 0x0Cu | ((uint32_t)(4 + i) << 8) | (0x0Cu << 16) | ((uint32_t)(4 + j) << 24);
+    const uint32_t t = __builtin_amdgcn_perm(w, 0u, sel);  // codes in the high bytes
+    return scale_pair(((t >> 1) & 0x3F803F80u) | (t & 0x80008000u), 256.0f);
+}
+// E2M1 codes in the 4-bit fields at bit offsets sh and sh+16 of w as an fp16 pair.
+__device__ inline uint32_t e2m1_pair(uint32_t w, int sh) {
+    const uint32_t x = (shift_signed(w, 9 - sh) & 0x0E000E00u) | (shift_signed(w, 12 - sh) & 0x80008000u);
+    return scale_pair(x, 16384.0f);
+}
+
 // QK A operand: the eight codes of group g held by this lane's K slice,
 // in channel order e0..e7 (see the K row layout); 8-bit codes exact, 4- and
-// 2-bit codes as B + c.
-template <int BITS>
+// 2-bit codes as B + c; native E4M3 / E2M1 codes as their values.
+template <int BITS, bool NAT>
 __device__ inline half8 k_operand(const uint32_t *kw, int g, uint32_t vb) {
     uint32_t r[4];
-    if constexpr (BITS == 8) {
+    if constexpr (NAT && BITS == 8) {
+        r[0] = e4m3_pair(kw[2 * g], 0, 1);
+        r[1] = e4m3_pair(kw[2 * g], 2, 3);
+        r[2] = e4m3_pair(kw[2 * g + 1], 0, 1);
+        r[3] = e4m3_pair(kw[2 * g + 1], 2, 3);
+    } else if constexpr (NAT && BITS == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = e2m1_pair(kw[g], 4 * k);
+    } else if constexpr (BITS == 8) {
         r[0] = unbias1024(byte_pair(kw[2 * g], 0, 1));
         r[1] = unbias1024(byte_pair(kw[2 * g], 2, 3));
         r[2] = unbias1024(byte_pair(kw[2 * g + 1], 0, 1));
@@ -113,11 +144,18 @@ __device__ inline half8 k_operand(const uint32_t *kw, int g, uint32_t vb) {
 }
 
 // PV B operand: codes of tokens 4r..4r+3 at this lane's channel of tile n,
-// as B + c.
-template <int BITS>
+// as B + c (native E4M3 / E2M1 codes: their values).
+template <int BITS, bool NAT>
 __device__ inline half4 v_operand(const uint32_t *vw, int n, uint32_t vb) {
     uint32_t r[2];
-    if constexpr (BITS == 8) {
+    if constexpr (NAT && BITS == 8) {
+        r[0] = e4m3_pair(vw[n], 0, 2);
+        r[1] = e4m3_pair(vw[n], 1, 3);
+    } else if constexpr (NAT && BITS == 4) {
+        const int m = n & 1;
+        r[0] = e2m1_pair(vw[n >> 1], 8 * m);
+        r[1] = e2m1_pair(vw[n >> 1], 8 * m + 4);
+    } else if constexpr (BITS == 8) {
         const uint32_t w = vw[n];
         r[0] = __builtin_amdgcn_perm(w, 0x64646464u, 4u | (6u << 16));
         r[1] = __builtin_amdgcn_perm(w, 0x64646464u, 5u | (7u << 16));
@@ -288,7 +326,8 @@ struct NoNext {
     __device__ void operator()(int) const {}
 };
 
-template <int G, int BITS, class Next>
+// NAT: the block holds native E4M3 / E2M1 codes (symmetric, zero 0).
+template <int G, int BITS, bool NAT, class Next>
 __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, float *score, int *spos,
                                     int off, bool has_pos, const uint4 *const *qa, const float *qsum, float scale2,
                                     WaveState &st, const Next &next) {
@@ -372,7 +411,7 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
             const half8 qb = __builtin_bit_cast(half8, qa[a][65 * g]);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS>(kw, g, vb), qb, acc[g], 0, 0, 0);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS, NAT>(kw, g, vb), qb, acc[g], 0, 0, 0);
         }
     }
 
@@ -385,17 +424,22 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
         // group by group, so each group's scale and zero terms (which largely
         // cancel) meet before the next group is added; the four tokens'
         // chains are independent and interleave
-        // (4- and 2-bit products carry the code bias: B * sum q comes off)
-        constexpr float KB = BITS == 8 ? 0.f : Code<BITS>::BIAS;
+        // (4- and 2-bit products carry the code bias: B * sum q comes off;
+        // native codes carry no bias and their zero is 0)
+        constexpr float KB = BITS == 8 || NAT ? 0.f : Code<BITS>::BIAS;
         float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < NGRP; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t sz = ksz[4 * i + g];
-                // acc - B * sum q in one rounding (B * sum q is exact)
-                v[i] = fmaf(lo_h(sz), BITS == 8 ? acc[g][i] : fmaf(-KB, qsum[g], acc[g][i]), v[i]);
-                v[i] = fmaf(hi_h(sz), qsum[g], v[i]);
+                if constexpr (NAT) {
+                    v[i] = fmaf(lo_h(sz), acc[g][i], v[i]);
+                } else {
+                    // acc - B * sum q in one rounding (B * sum q is exact)
+                    v[i] = fmaf(lo_h(sz), BITS == 8 ? acc[g][i] : fmaf(-KB, qsum[g], acc[g][i]), v[i]);
+                    v[i] = fmaf(hi_h(sz), qsum[g], v[i]);
+                }
             }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -487,8 +531,8 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) pop[g][i] = (_Float16)(pm[i] * lo_h(vsz[4 * i + g]));
     // zero-point term sum p * v_zero, less the V operands' bias share
-    // B * P' / mult
-    {
+    // B * P' / mult (native codes: neither)
+    if constexpr (!NAT) {
         const float kb = -Code<BITS>::BIAS / st.mult;
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
@@ -509,7 +553,7 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
             const half4 pa = mine ? pop[n >> 1] : (half4){};
-            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v_operand<BITS>(vw[a], n, vb), st.o[n], 0, 0, 0);
+            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v_operand<BITS, NAT>(vw[a], n, vb), st.o[n], 0, 0, 0);
         }
     }
 
@@ -542,7 +586,7 @@ struct SplitLds {
 };
 
 // One work item (sequence, kv-head pack, run of at most E entries).
-template <int G>
+template <int G, bool NATIVE>
 __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const DecodeWs &ws,
                                   float scale2, int S, int item, const int *s_first,
                                   SplitLds<PACK(G)> &sh) {
@@ -683,11 +727,11 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
             if (kn < n_ent) issue(kn, part);
         };
         if (pool == 0)
-            attend_block<G, 8>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
+            attend_block<G, 8, NATIVE>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
         else if (pool == 1)
-            attend_block<G, 4>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
+            attend_block<G, 4, NATIVE>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
         else
-            attend_block<G, 2>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
+            attend_block<G, 2, false>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
     }
     // -- merge the waves of this workgroup and write the run's partial.  Each
     //    wave publishes its row maxima, then writes its output rows already
@@ -765,7 +809,9 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
 // items round-robin, so the dispatcher never has to refill slots and no
 // workgroup is launched for a run past a sequence's end.  The item prefix
 // (B + 1 ints) lives in dynamic LDS.
-template <int G>
+// NATIVE: the cache holds the native codec (Reasoning and Execution blocks
+// in E4M3 / E2M1; Transition blocks are integer-coded in both codecs).
+template <int G, bool NATIVE>
 __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
                                                          DecodeWs ws, float scale2, int S) {
     constexpr int P = PACK(G);
@@ -816,7 +862,7 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     }
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x)
-        split_item<G>(c, q, ws, scale2, S, item, s_first, lds);
+        split_item<G, NATIVE>(c, q, ws, scale2, S, item, s_first, lds);
 }
 
 // Finalize: FPART workgroups per (run, sequence), workgroup x taking run
@@ -1009,21 +1055,21 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
 
 }  // namespace
 
-// Workgroups of attn_split<G> that fit on the device at once, for a given
-// dynamic LDS size (cached per device and G).
-int persistent_grid(int G, const void *kernel, size_t dyn_lds) {
-    static int cache[64][KVQ_MAX_GQA + 1];
-    static size_t cache_lds[64][KVQ_MAX_GQA + 1];
+// Workgroups of attn_split<G, native> that fit on the device at once, for a
+// given dynamic LDS size (cached per device, G and codec).
+int persistent_grid(int G, bool native, const void *kernel, size_t dyn_lds) {
+    static int cache[64][2][KVQ_MAX_GQA + 1];
+    static size_t cache_lds[64][2][KVQ_MAX_GQA + 1];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int &v = cache[dev][G];
-    if (v == 0 || cache_lds[dev][G] != dyn_lds) {
+    int &v = cache[dev][native][G];
+    if (v == 0 || cache_lds[dev][native][G] != dyn_lds) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WAVES * 64, dyn_lds) != hipSuccess)
             return 0;
         v = cus * (per_cu > 0 ? per_cu : 1);
-        cache_lds[dev][G] = dyn_lds;
+        cache_lds[dev][native][G] = dyn_lds;
     }
     return v;
 }
@@ -1037,16 +1083,20 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
     const float scale2 = sm_scale * LOG2E;
     const size_t dyn = sizeof(int) * ((size_t)c.B + 1);   // item prefix of the split kernel
     switch (G) {
-#define KVQ_G(g)                                                                                   \
-    case g: {                                                                                      \
-        const int grid = persistent_grid(g, reinterpret_cast<const void *>(attn_split<g>), dyn);    \
-        if (grid <= 0) return false;                                                               \
-        hipLaunchKernelGGL(attn_split<g>, dim3(grid), dim3(WAVES * 64), dyn, s, c, qq, mass, ws, scale2, S); \
-        break;                                                                                     \
+#define KVQ_GN(g, nat)                                                                                   \
+    {                                                                                                    \
+        const int grid = persistent_grid(g, nat, reinterpret_cast<const void *>(attn_split<g, nat>), dyn); \
+        if (grid <= 0) return false;                                                                     \
+        hipLaunchKernelGGL((attn_split<g, nat>), dim3(grid), dim3(WAVES * 64), dyn, s, c, qq, mass, ws, scale2, S); \
     }
+#define KVQ_G(g)                                                    \
+    case g:                                                         \
+        if (c.codec == KVQ_CODEC_NATIVE) KVQ_GN(g, true) else KVQ_GN(g, false) \
+        break;
         KVQ_G(1) KVQ_G(2) KVQ_G(3) KVQ_G(4) KVQ_G(5) KVQ_G(6) KVQ_G(7) KVQ_G(8)
         KVQ_G(9) KVQ_G(10) KVQ_G(11) KVQ_G(12) KVQ_G(13) KVQ_G(14) KVQ_G(15) KVQ_G(16)
 #undef KVQ_G
+#undef KVQ_GN
         default: return false;
     }
     {

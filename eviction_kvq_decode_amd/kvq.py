@@ -32,7 +32,7 @@ class CacheStruct(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("n_cap", ctypes.c_int32),
-        ("pool_blocks", ctypes.c_int32 * 3),
+        ("pool_blocks", ctypes.c_int32 * 3), ("codec", ctypes.c_int32),
         ("kv", ctypes.c_void_p * 3), ("mask", ctypes.c_void_p * 3), ("pos", ctypes.c_void_p * 3),
         ("table", ctypes.c_void_p), ("n_blocks", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
         ("free_ids", ctypes.c_void_p * 3), ("free_top", ctypes.c_void_p), ("status", ctypes.c_void_p),
@@ -97,6 +97,7 @@ class Cache:
         g = geometry
         s.B, s.Hq, s.Hkv, s.head_dim = g.B, g.Hq, g.Hkv, HD
         s.max_blocks, s.n_cap = g.max_blocks, g.n_cap
+        s.codec = getattr(g, "codec", 0)
         for p in range(3):
             s.pool_blocks[p] = g.pool_blocks[p]
             s.kv[p] = self.t[f"kv{p}"].data_ptr()

@@ -60,6 +60,23 @@ enum { KVQ_HEAD_DIM = 128, KVQ_BLOCK = 16, KVQ_GROUP = 32, KVQ_MAX_GQA = 16 };
 enum { KVQ_TAG_R = 0, KVQ_TAG_E = 1, KVQ_TAG_T = 2, KVQ_TAG_NONE = 255 };
 
 /*
+ * Codecs ("ThinKV", Methodology, TBQ: precision by thought type), chosen per
+ * cache in kvq_cache.codec; both keep the same code widths and layout:
+ *   KVQ_CODEC_INT    asymmetric integer codes per group of 32 channels:
+ *                    zero = group min, scale = least fp16 >= (max-min) /
+ *                    (2^b - 1), code = rint((x - zero) / scale);
+ *   KVQ_CODEC_NATIVE ThinKV's own formats, symmetric per group of 32 with
+ *                    scale = least fp16 >= max|x| / top: Reasoning rows hold
+ *                    OCP E4M3 codes of x / scale (top 448), Execution rows
+ *                    E2M1 codes (top 6), both nearest with ties to even and
+ *                    zero = 0, dequantised as value(code) * scale; Transition
+ *                    rows hold t + 1 for t = rint(x / scale) in [-1, 1]
+ *                    (top 1) with zero = -scale, dequantised as code * scale
+ *                    + zero (ternary).
+ */
+enum { KVQ_CODEC_INT = 0, KVQ_CODEC_NATIVE = 1 };
+
+/*
  * The cache.  One pool per bit width; a block holds 16 slots of one thought
  * type.  For pool p (bits b = 8 >> p) and block id, kv head h, the region at
  *     kv[p] + (id * Hkv + h) * kvq_region_bytes(p)
@@ -76,7 +93,8 @@ enum { KVQ_TAG_R = 0, KVQ_TAG_E = 1, KVQ_TAG_T = 2, KVQ_TAG_NONE = 255 };
  *                            (u&1)*(16/b) + 2*(n mod 8/b) + (u>>1)
  *     K (scale, zero) 256 B: fp16 pair for token t, group g at (t*4 + g)*4
  *     V (scale, zero) 256 B: same layout
- * Codes are packed LSB first.  A dequantised value is code * scale + zero.
+ * Codes are packed LSB first.  A dequantised value is code * scale + zero
+ * (KVQ_CODEC_NATIVE, Reasoning and Execution rows: value(code) * scale).
  * Bytes of slots whose mask bit is clear are unspecified.
  *
  * table[b * max_blocks + e] = (pool << 30) | id, for e < n_blocks[b], in
@@ -92,6 +110,7 @@ typedef struct kvq_cache {
     int32_t max_blocks;   /* table row capacity per sequence             */
     int32_t n_cap;        /* row stride (positions) of mass / importance */
     int32_t pool_blocks[3];
+    int32_t codec;        /* KVQ_CODEC_INT or KVQ_CODEC_NATIVE           */
     uint8_t *kv[3];       /* [pool_blocks][Hkv] regions                  */
     uint16_t *mask[3];    /* [pool_blocks] valid-slot bitmask            */
     int32_t *pos[3];      /* [pool_blocks][16]                           */

@@ -75,6 +75,7 @@ def test_region_and_workspace_sizes():
     (dict(Hq=9, Hkv=2), kvq.KVQ_EINVAL),
     (dict(B=0), kvq.KVQ_EINVAL),
     (dict(table=None), kvq.KVQ_EINVAL),
+    (dict(codec=2), kvq.KVQ_EINVAL),
 ])
 def test_host_side_validation(over, code):
     L = kvq.lib()
