@@ -338,7 +338,8 @@ def ct_bench(args, w):
     out = torch.empty((B, w.Hq, 128), device="cuda")
     mass = torch.empty((B, g.n_cap), device="cuda")
     st0 = cache.state_numpy()
-    ct = ContinuousThinking(cache, w.keep, w.period, w.q_window, w.recent_window, w.decay)
+    ct = ContinuousThinking(cache, w.keep, w.period, w.q_window, w.recent_window, w.decay,
+                            policy=args.policy, tbe=TBE_PARAMS, tam=TAM_PARAMS)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(w.loop_steps)]
     pruned = np.zeros(w.loop_steps, dtype=bool)
@@ -381,11 +382,13 @@ def ct_bench(args, w):
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, {n0} cached tokens/seq, "
                                f"{w.loop_steps} generated; budget {w.keep} + windows "
-                               f"{w.q_window}/{w.recent_window}, pruned every {w.period} tokens; "
+                               f"{w.q_window}/{w.recent_window}, pruned every {w.period} tokens "
+                               f"({args.policy}); "
                                f"step = append + decode (+ evict every {w.period})",
                    "global_batch": B, "seq_len": n0 + w.loop_steps},
         "roofline": None,
-        "ct": {"us_per_step_p50": float(np.median(us)), "us_per_step_p90": float(np.quantile(us, 0.9)),
+        "ct": {"policy": args.policy,
+               "us_per_step_p50": float(np.median(us)), "us_per_step_p90": float(np.quantile(us, 0.9)),
                "us_prune_step": float(us[pr].mean()) if pr.any() else None,
                "us_other_step": float(us[~pr].mean()),
                "table_blocks_before": b0, "table_blocks_after": b1,
@@ -403,6 +406,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_evicted")
+    ap.add_argument("--policy", choices=("topk", "tbe", "tam"), default="topk",
+                    help="pruning of the continuous-thinking loop (--workload ct_loop)")
     ap.add_argument("--codec", choices=("int", "native"), default="int",
                     help="integer min/max codes, or ThinKV's E4M3 / E2M1 / ternary formats")
     ap.add_argument("--no-cpu", action="store_true")

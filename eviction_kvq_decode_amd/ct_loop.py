@@ -11,11 +11,16 @@ Pages (cited by title and section):
     between the budget t and t + P.
   - "Dynamic Thinking-Token Selection ...", section 2.3: the question and
     recent windows are kept, top-k by accumulated importance among the rest.
+  - "ThinKV", Methodology, think-before-evict: the loop can prune by thought
+    segment instead (policy "tbe": kvq_evict_tbe's annealed retention).
+  - "TAM", section 2: or by segment budgets with pivotal tokens (policy
+    "tam": kvq_evict_tam, the accumulated importance as the window score).
 
 One step appends one token per sequence, decodes (output and per-position
 mass, accumulated into the importance with the decay), and every `period`
-steps evicts down to `budget` tokens outside the windows.  All work is
-enqueued on one stream; nothing here computes or synchronises.
+steps prunes the cache outside the windows: to `budget` tokens (top-k or
+TAM budgets) or by the TBE schedule.  All work is enqueued on one stream;
+nothing here computes or synchronises.
 """
 from __future__ import annotations
 
@@ -25,12 +30,20 @@ from . import kvq
 class ContinuousThinking:
     """A decode loop with periodic windowed top-k eviction on one cache."""
 
+    POLICIES = ("topk", "tbe", "tam")
+
     def __init__(self, cache: kvq.Cache, budget: int, period: int, q_window: int = 0,
-                 recent_window: int = 0, decay: float = 0.9, importance=None):
+                 recent_window: int = 0, decay: float = 0.9, importance=None, policy: str = "topk",
+                 tbe=(64, 4, 8), tam=(8.0, 16)):
+        """tbe = (r0, r_min, t_keep) for policy "tbe"; tam = (pivot_c,
+        min_seg) for policy "tam"."""
         import torch
 
         if period < 1 or budget < 0:
             raise ValueError("period must be >= 1 and budget >= 0")
+        if policy not in self.POLICIES:
+            raise ValueError(f"policy must be one of {self.POLICIES}")
+        self.policy, self.tbe, self.tam = policy, tuple(tbe), tuple(tam)
         g = cache.g
         self.cache, self.period, self.decay = cache, period, decay
         self.q_window, self.recent_window = q_window, recent_window
@@ -47,6 +60,12 @@ class ContinuousThinking:
         self.since_evict += 1
         if self.since_evict < self.period:
             return False
-        self.cache.evict(self.importance, self.keep, self.q_window, self.recent_window, stream)
+        if self.policy == "tbe":
+            self.cache.evict_tbe(self.importance, *self.tbe, self.q_window, self.recent_window, stream)
+        elif self.policy == "tam":
+            self.cache.evict_tam(self.importance, self.keep, *self.tam, self.q_window, self.recent_window,
+                                 stream)
+        else:
+            self.cache.evict(self.importance, self.keep, self.q_window, self.recent_window, stream)
         self.since_evict = 0
         return True

@@ -1,6 +1,7 @@
 """GPU parity of the continuous-thinking loop (eviction_kvq_decode_amd.ct_loop)
 against the oracle running the same loop: a generation under a cache budget,
-pruned every P tokens ("ThinKV", Continuous Thinking; "TAM", section 2.D).
+pruned every P tokens ("ThinKV", Continuous Thinking; "TAM", section 2.D), by
+windowed top-k, by thought segment (TBE) or by segment budgets (TAM).
 
 Every step compares the output (2e-3 relative / 1e-3 absolute) and the mass
 and importance (1e-5 absolute); after every prune the whole cache state is
@@ -21,7 +22,8 @@ pytestmark = pytest.mark.gpu
 HD = 128
 
 
-def test_ct_loop_matches_oracle():
+@pytest.mark.parametrize("policy", ["topk", "tbe", "tam"])
+def test_ct_loop_matches_oracle(policy):
     import torch
 
     from eviction_kvq_decode_amd import kvq
@@ -29,7 +31,7 @@ def test_ct_loop_matches_oracle():
 
     w = wl.scaled(wl.WORKLOADS["ct_loop"], B=3, n_min=1200, n_max=1200, keep=500,
                   q_window=64, recent_window=128, period=64, loop_steps=320, extra_steps=320 + 16)
-    log(f"[gpu ct loop] B={w.B} Hq={w.Hq} Hkv={w.Hkv} cached={w.n_min} budget={w.keep} "
+    log(f"[gpu ct loop] {policy}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} cached={w.n_min} budget={w.keep} "
         f"period={w.period} steps={w.loop_steps}")
     n0 = w.n_min
     toks = wl.lockstep_tokens(w, n0 + w.extra_steps)
@@ -41,7 +43,9 @@ def test_ct_loop_matches_oracle():
         oc.append(toks.k[i], toks.v[i], toks.tags[i])
         gc.append(K[i], V[i], T[i])
     torch.cuda.synchronize()
-    ct = ContinuousThinking(gc, w.keep, w.period, w.q_window, w.recent_window, w.decay)
+    tbe, tam = (16, 2, 4), (6.0, 8)
+    ct = ContinuousThinking(gc, w.keep, w.period, w.q_window, w.recent_window, w.decay, policy=policy,
+                            tbe=tbe, tam=tam)
     imp_o = np.zeros((w.B, g.n_cap), dtype=np.float32)
     keep = np.full(w.B, w.keep, dtype=np.int32)
     tags_all = wl.loop_tags(w, n0 + w.loop_steps)
@@ -68,7 +72,12 @@ def test_ct_loop_matches_oracle():
             imp_g = ct.importance.cpu().numpy()
             ei = np.abs(imp_g - imp_o)
             assert ei.max() <= ATOL_MASS, f"step {s} importance: {ei.max():.3g}"
-            oc.evict(imp_g, keep, w.q_window, w.recent_window)
+            if policy == "tbe":
+                oc.evict_tbe(imp_g, *tbe, w.q_window, w.recent_window)
+            elif policy == "tam":
+                oc.evict_tam(imp_g, keep, *tam, w.q_window, w.recent_window)
+            else:
+                oc.evict(imp_g, keep, w.q_window, w.recent_window)
             assert_same_cache(oc, gc.state_numpy())
             prunes += 1
     assert prunes == w.loop_steps // w.period
