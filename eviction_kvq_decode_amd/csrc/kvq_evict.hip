@@ -1,8 +1,14 @@
-// kvq_evict.hip -- windowed top-k eviction with metadata-only compaction.
+// kvq_evict.hip -- eviction with metadata-only compaction, three policies:
+// windowed top-k, thought-adaptive eviction by segment, and thought-aware
+// segment budgets.
 //
 // "Dynamic Thinking-Token Selection ...", section 2.3: tokens of the
 // question window are never evicted, the local window of recent tokens is
 // kept, and inside the selection window the top-k by importance survive.
+// "ThinKV", Methodology, think-before-evict: earlier Reasoning / Execution
+// segments are pruned on an annealing schedule as Transitions follow.
+// "Thought-Aware KV Cache Compaction ... (TAM)", section 2: segment budgets
+// proportional to sqrt(mean mass) * size, pivotal tokens kept.
 // "ThinKV", Continuous Thinking: eviction only clears mask bits -- the KV
 // bytes never move; blocks that become empty leave the table and go back to
 // their pool's free list for in-place reuse.
