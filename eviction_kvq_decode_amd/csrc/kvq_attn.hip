@@ -875,6 +875,7 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
 // of each slot.
 constexpr int FT = 256;
 constexpr int FB = 4;                         // groups a wave takes per round
+constexpr int FPK = 2;                        // kv-head packs whose scores are loaded together (4: slower)
 #ifndef KVQ_FPART
 #define KVQ_FPART 2
 #endif
@@ -957,20 +958,32 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
         }
-        for (int p0 = 0; p0 < n_packs; p0 += 2) {
-            // two packs' scores of the round's groups, loads issued together
-            float4 t[FB][2];
+        // the importance of these positions, loaded before the scores so that
+        // its latency overlaps theirs (lanes lo == 0 write the slots)
+        float imp_old[FB][4];
+        if (importance && lo == 0) {
+#pragma unroll
+            for (int e = 0; e < FB; ++e) {
+                const int pp[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    imp_old[e][i] = pp[i] >= 0 && pp[i] < c.n_cap ? importance[(size_t)b * c.n_cap + pp[i]] : 0.f;
+            }
+        }
+        for (int p0 = 0; p0 < n_packs; p0 += FPK) {
+            // FPK packs' scores of the round's groups, loads issued together
+            float4 t[FB][FPK];
 #pragma unroll
             for (int e = 0; e < FB; ++e)
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
+                for (int q = 0; q < FPK; ++q) {
                     const int k = k0 + e, p = p0 + q;
                     t[e][q] = k < n_ent && p < n_packs
                                   ? reinterpret_cast<const float4 *>(ws.score + ((ek0 * n_packs + (size_t)p * E) + k) * 256)[lo * 4 + hi]
                                   : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
                 }
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            for (int q = 0; q < FPK; ++q) {
                 const int p = p0 + q;
                 const int col = p * P * G + lo;
                 const bool cv = p < n_packs && lo < min(P, c.Hkv - p * P) * G && Mh[min(col, Hq - 1)] != -INFINITY;
@@ -1000,10 +1013,7 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
                     // a position outside the row stride (a corrupt cache) is skipped
                     if (pp[i] < 0 || pp[i] >= c.n_cap) continue;
                     mass[(size_t)b * c.n_cap + pp[i]] = acc[e][i];
-                    if (importance) {
-                        float *ip = importance + (size_t)b * c.n_cap + pp[i];
-                        *ip = fmaf(decay, *ip, acc[e][i]);
-                    }
+                    if (importance) importance[(size_t)b * c.n_cap + pp[i]] = fmaf(decay, imp_old[e][i], acc[e][i]);
                 }
             }
         }
