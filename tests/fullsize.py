@@ -57,7 +57,7 @@ def subset_geometry(g: wl.Geometry, seqs: list, w: wl.Workload) -> wl.Geometry:
             counts[p] += int(math.ceil(int((s.tags == p).sum()) / BLK))
     spare = len(seqs) * (4 + int(math.ceil((w.extra_steps + w.append_steps) / BLK)))
     return wl.Geometry(len(seqs), g.Hq, g.Hkv, g.max_blocks, g.n_cap,
-                       tuple(int(c + spare) for c in counts))
+                       tuple(int(c + spare) for c in counts), g.codec)
 
 
 class FullPair:
@@ -115,6 +115,34 @@ class FullPair:
                       torch.from_numpy(np.ascontiguousarray(keep_full, dtype=np.int32)).cuda(), qw, rw)
         self.oc.evict(np.ascontiguousarray(imp_full[self.sample], dtype=np.float32),
                       np.ascontiguousarray(keep_full[self.sample], dtype=np.int32), qw, rw)
+
+    def evict_tbe(self, imp_full, r0, r_min, t_keep, qw, rw):
+        """Thought-adaptive eviction by segment on both sides."""
+        torch = self.torch
+        self.gc.evict_tbe(torch.from_numpy(np.ascontiguousarray(imp_full, dtype=np.float32)).cuda(),
+                          r0, r_min, t_keep, qw, rw)
+        self.oc.evict_tbe(np.ascontiguousarray(imp_full[self.sample], dtype=np.float32), r0, r_min, t_keep,
+                          qw, rw)
+
+    def evict_tam(self, score_full, keep_full, pivot_c, min_seg, qw, rw):
+        """Thought-aware segment budgets on both sides."""
+        torch = self.torch
+        self.gc.evict_tam(torch.from_numpy(np.ascontiguousarray(score_full, dtype=np.float32)).cuda(),
+                          torch.from_numpy(np.ascontiguousarray(keep_full, dtype=np.int32)).cuda(),
+                          pivot_c, min_seg, qw, rw)
+        self.oc.evict_tam(np.ascontiguousarray(score_full[self.sample], dtype=np.float32),
+                          np.ascontiguousarray(keep_full[self.sample], dtype=np.int32), pivot_c, min_seg, qw, rw)
+
+    def snapshot(self):
+        """Cache metadata of both sides (the KV bytes never change in eviction)."""
+        return ({k: v.clone() for k, v in self.gc.t.items() if not k.startswith("kv")},
+                {k: v.copy() for k, v in self.oc.st.items()})
+
+    def restore(self, snap):
+        gmeta, ost = snap
+        for k, v in gmeta.items():
+            self.gc.t[k].copy_(v)
+        self.oc.st = {k: v.copy() for k, v in ost.items()}
 
     def append_step(self, step):
         torch = self.torch

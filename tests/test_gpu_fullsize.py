@@ -55,6 +55,21 @@ def test_fullsize_decode(name):
     del fp
 
 
+def test_fullsize_decode_native_codec():
+    """The long evicted trace's timed step with the cache in ThinKV's own
+    formats (E4M3 / E2M1 / ternary), as `bench.py --codec native` times it."""
+    w = wl.scaled(wl.WORKLOADS["long_evicted"], codec=1)
+    log(f"[gpu fullsize] long_evicted, native codec: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.n_max}")
+    fp = FullPair(w, _sample(w))
+    fp.fill()
+    _check_sample_state(fp)
+    for step in range(w.append_steps):
+        fp.append_step(step)
+    assert fp.gc.status == 0
+    _decode_step(fp, 0)
+    del fp
+
+
 @pytest.mark.parametrize("name", ["budgeted", "ragged"])
 def test_fullsize_decode_importance_evict(name):
     """Decode with importance accumulation, then windowed top-k eviction with
@@ -85,4 +100,43 @@ def test_fullsize_decode_importance_evict(name):
         best = np.sort(cand[order[: int(keep_k[b])]])
         assert np.array_equal(np.sort(va[~np.isin(va, vb[win])]), best), f"top-k set b={b}"
     assert_pools_partitioned(after_st, fp.g)
+    del fp
+
+
+def test_fullsize_segment_eviction_and_budgets():
+    """Thought-adaptive eviction by segment and thought-aware segment budgets
+    over the whole budgeted batch (B=64, 16384 positions), from the same
+    decoded state, with the parameters the benchmark times."""
+    import bench
+
+    w = wl.WORKLOADS["budgeted"]
+    log(f"[gpu fullsize] segment eviction: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.n_max}")
+    fp = FullPair(w, _sample(w))
+    fp.fill()
+    imp0 = np.stack([wl.importance0(w, b, fp.g.n_cap) for b in range(w.B)])
+    gst, got = _decode_step(fp, 0, imp0, w.decay)
+    imp_gpu = got[2]
+    keep_k = wl.keep_counts(w)
+    before = [valid_positions(gst, fp.g, b) for b in range(w.B)]
+    snap = fp.snapshot()
+    for policy in ("tbe", "tam"):
+        log(f"[gpu fullsize] {policy}")
+        fp.restore(snap)
+        if policy == "tbe":
+            fp.evict_tbe(imp_gpu, *bench.TBE_PARAMS, w.q_window, w.recent_window)
+        else:
+            fp.evict_tam(imp_gpu, keep_k, *bench.TAM_PARAMS, w.q_window, w.recent_window)
+        assert fp.gc.status == 0
+        after_st = _check_sample_state(fp)
+        for b in range(w.B):
+            n = int(after_st["seq_len"][b])
+            vb = before[b]
+            win = (vb < w.q_window) | (vb >= n - w.recent_window)
+            va = valid_positions(after_st, fp.g, b)
+            assert np.all(np.isin(vb[win], va)), f"{policy}: window evicted b={b}"
+            assert np.all(np.isin(va, vb)), f"{policy}: a slot appeared b={b}"
+            if policy == "tam":
+                kept = int((~np.isin(va, vb[win])).sum())
+                assert kept >= min(int(keep_k[b]), int((~win).sum())), f"tam: budget not used b={b}"
+        assert_pools_partitioned(after_st, fp.g)
     del fp
