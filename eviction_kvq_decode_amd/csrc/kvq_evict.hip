@@ -746,12 +746,15 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
 
     // B. weights from running sums over the candidates: psum[k] = sum of s
     //    before candidate k, pcnt[k] = droppable candidates before it, packed
-    //    in one word (s in the low 48 bits, the count above).  Each wave takes
+    //    within a pass in one word (s in the low 48 bits, the count above).  Each wave takes
     //    TBE_RUN coalesced chunks of 64 candidates: its total, one scan of the
     //    wave totals, then a wave scan per chunk.  Then a thread per segment.
     {
+        // packed words stay inside one pass (16384 candidates: sums below
+        // 2^46); the totals carried across passes are kept apart
         constexpr uint64_t LOW = (1ull << 48) - 1;
-        uint64_t carry = 0;
+        uint64_t carry_s = 0;
+        int carry_c = 0;
         for (int k0 = 0; k0 < n; k0 += SEL_THREADS * TBE_RUN) {
             const int wb = k0 + wv * 64 * TBE_RUN;
             uint64_t mine = 0;
@@ -764,7 +767,7 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
             for (int d = 32; d > 0; d >>= 1) mine += __shfl_xor(mine, d);
             if (lane == 0) wave_u64[wv] = mine;
             __syncthreads();
-            uint64_t run = carry, tot = 0;
+            uint64_t run = 0, tot = 0;
             for (int w = 0; w < SEL_WAVES; ++w) {
                 const uint64_t v = wave_u64[w];
                 run += w < wv ? v : 0ull;
@@ -783,16 +786,17 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
                 }
                 if (k < n) {
                     const uint64_t ex = run + incl - v;
-                    psum[k] = ex & LOW;
-                    pcnt[k] = (int32_t)(ex >> 48);
+                    psum[k] = carry_s + (ex & LOW);
+                    pcnt[k] = carry_c + (int32_t)(ex >> 48);
                 }
                 run += __shfl(incl, 63);
             }
-            carry += tot;
+            carry_s += tot & LOW;
+            carry_c += (int32_t)(tot >> 48);
         }
         if (tid == 0) {
-            psum[n] = carry & LOW;
-            pcnt[n] = (int32_t)(carry >> 48);
+            psum[n] = carry_s;
+            pcnt[n] = carry_c;
         }
     }
     __syncthreads();

@@ -141,3 +141,19 @@ def test_workload_tam_bit_exact(pair):
     ref, got = pair.decode(wl.queries(w, 3))
     assert_attention_close(ref, got)
     assert_mass_close(pair.oc.st["seq_len"], ref, got)
+
+
+def test_running_sums_past_48_bits():
+    """70,000 candidates scoring near the 2^16 clamp: the fixed-point running
+    sum passes 2^48 (the packed word's field), which the budgets must not
+    notice."""
+    rng = np.random.default_rng(41)
+    n = 70_000
+    row = list(np.repeat(rng.integers(0, 3, n // 10), rng.integers(10, 40, n // 10)))[:n]
+    log(f"[gpu tam] running sums past 2^48: {len(row)} tokens")
+    oc, gc, g = _pair_from_tags([row])
+    sc = np.zeros((1, g.n_cap), dtype=np.float32)
+    sc[0, :n] = rng.uniform(60000.0, 65535.0, n).astype(np.float32)
+    assert float(np.floor(sc.astype(np.float64) * 65536).sum()) > 2.0 ** 48
+    _run_both(oc, gc, g, sc, 5000, INF, 1, 16, 32)
+    assert_same_cache(oc, gc.state_numpy())
