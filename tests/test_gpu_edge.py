@@ -93,13 +93,15 @@ def test_pool_exhaustion_and_bad_tag():
     assert_same_cache(oc3, gc3.state_numpy())
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (16, 1), (24, 2)])
-def test_gqa_group_sizes(Hq, Hkv):
-    log(f"[edge] Hq={Hq} Hkv={Hkv}")
-    g = small_geometry(2, Hq, Hkv, 700)
+@pytest.mark.parametrize("codec", [0, 1], ids=["int", "native"])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (16, 1), (24, 2), (6, 2)])
+def test_gqa_group_sizes(Hq, Hkv, codec):
+    log(f"[edge] Hq={Hq} Hkv={Hkv} codec={codec}")
+    g = small_geometry(2, Hq, Hkv, 700, codec=codec)
     oc, gc = _mk(g, identity=False)
     rng = np.random.default_rng(Hq)
     _fill(oc, gc, rng, 700)
+    assert_same_cache(oc, gc.state_numpy())
     q = rng.standard_normal((2, Hq, HD)).astype(np.float16)
     imp = rng.exponential(0.1, (2, g.n_cap)).astype(np.float32)
     ref, got = _decode(oc, gc, q, imp, 0.9)
