@@ -7,14 +7,17 @@
 // accumulated H2O-style with a decay.  "ThinKV", Continuous Thinking: the
 // kernel walks a block table whose blocks carry an eviction mask.
 //
-// attn_split: one workgroup per (sequence, kv head, run of table entries).
-//   Online softmax in base 2; writes the split's (max, sum, unnormalised
+// attn_split: persistent workgroups over (sequence, kv-head pack, run of
+//   table entries) items, the run length chosen per call so that the items
+//   fill whole rounds of the grid.  Online softmax in base 2; writes the split's (max, sum, unnormalised
 //   output) and every score it computed (needed later for the mass, whose
 //   normaliser is only known once all splits are done).
 // attn_finalize: one workgroup per (sequence, run of table entries): merges
 //   the splits (log-sum-exp), writes the output rows, and turns the stored
 //   scores into mass / importance in a fixed head order (no float atomics).
 #include <math.h>
+
+#include <algorithm>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -25,8 +28,30 @@ namespace {
 
 constexpr int E = ENTRIES_PER_SPLIT;
 constexpr int MAX_HQ = 256;
-constexpr int MAX_B = 1024;       // sequences per call handled by the split kernel's item prefix
 constexpr float LOG2E = 1.4426950408889634f;
+
+// Table entries of a sequence, as the kernels read them (a count outside
+// [0, max_blocks] in a corrupt cache is clamped).
+__device__ inline int table_entries(const kvq_cache &c, int b) {
+    return min(max(c.n_blocks[b], 0), c.max_blocks);
+}
+
+// Runs of a sequence with nb table entries when a run holds at most ew of
+// them: never fewer than E-entry runs need, never more than S (the partials
+// held per sequence; S * MIN_RUN >= max_blocks >= nb).
+__device__ inline int seq_runs(int nb, int ew, int S) {
+    if (nb <= 0) return 0;
+    const int lo = (nb + E - 1) / E, nr = (nb + ew - 1) / ew;
+    return nr < lo ? lo : (nr > S ? S : nr);
+}
+
+// Run j holds entries j, j + nr, ...: at most ceil(nb / nr) of them.  Its
+// scores start at group j * run_stride: E-entry runs keep E-aligned areas
+// (nr E <= max_blocks rounded up to E); shorter runs are packed at their
+// longest length (nr ceil(nb / nr) < nb + nr <= max_blocks + S).
+__device__ inline int run_stride(int nb, int nr, int ew) {
+    return ew == E ? E : (nb + nr - 1) / nr;
+}
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -588,7 +613,7 @@ struct SplitLds {
 // One work item (sequence, kv-head pack, run of at most E entries).
 template <int G, bool NATIVE>
 __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const DecodeWs &ws,
-                                  float scale2, int S, int item, const int *s_first,
+                                  float scale2, int S, int span, int ew, int item, const int *s_first,
                                   SplitLds<PACK(G)> &sh) {
     constexpr int P = PACK(G);
     const int n_packs = (c.Hkv + P - 1) / P;
@@ -611,8 +636,8 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     //    a sequence with nr runs holds table entries j, j + nr, j + 2 nr, ...
     //    (at most E): every run samples the whole sequence, so the runs of a
     //    sequence cost about the same whatever the order of its block widths.
-    const int nb = c.n_blocks[b];
-    const int nr = (nb + E - 1) / E;
+    const int nb = table_entries(c, b);
+    const int nr = __builtin_amdgcn_readfirstlane((s_first[b + 1] - s_first[b]) / n_packs);
     if (wave == 0) {
         int n = 0, slots = 0;
         for (int base = 0; base < E; base += 64) {
@@ -712,8 +737,10 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         issue(wv, PART_K);
     }
     // the run's compacted scores of this pack, and its slot positions
-    float *score = ws.score + ((size_t)(b * S + split) * n_packs + pack) * E * 256;
-    int *spos = ws.spos + (size_t)(b * S + split) * E * 16;
+    const int rst = __builtin_amdgcn_readfirstlane(run_stride(nb, nr, ew));
+    const size_t roff = (size_t)b * span + (size_t)split * rst;
+    float *score = ws.score + (roff * n_packs + (size_t)pack * rst) * 256;
+    int *spos = ws.spos + roff * 16;
     for (int k = wv; k < n_ent; k += WAVES) {
         // entry k is in the stage once its wave's memory operations are done
         // (the last ones issued are its K part)
@@ -803,17 +830,22 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
     }
 }
 
-// Work items are (sequence, kv-head pack, run of at most E table entries),
+// Work items are (sequence, kv-head pack, run of at most ew table entries),
 // ordered by sequence, run, pack, for the runs that hold entries.  The kernel is
 // persistent: gridDim.x workgroups (what fits on the GPU at once) take the
 // items round-robin, so the dispatcher never has to refill slots and no
 // workgroup is launched for a run past a sequence's end.  The item prefix
 // (B + 1 ints) lives in dynamic LDS.
+// The run length ew is E, unless E-entry runs give fewer items than there
+// are workgroups: then it is the shortest length whose items still fit in
+// the grid, so that a small batch is spread over every workgroup in one
+// round.  (Shortening runs to fill a partly idle last round of a larger
+// batch was measured slower than E-entry runs.)
 // NATIVE: the cache holds the native codec (Reasoning and Execution blocks
 // in E4M3 / E2M1; Transition blocks are integer-coded in both codecs).
 template <int G, bool NATIVE>
 __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
-                                                         DecodeWs ws, float scale2, int S) {
+                                                         DecodeWs ws, float scale2, int S, int span) {
     constexpr int P = PACK(G);
     const int n_packs = (c.Hkv + P - 1) / P;
     const int tid = threadIdx.x;
@@ -821,6 +853,34 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     extern __shared__ int s_first[];
     __shared__ SplitLds<P> lds;
     __shared__ int s_carry;
+    __shared__ int s_red[WAVES];
+
+    // -- run length (the same in every workgroup; workgroup 0 publishes it
+    //    for the finalize).  s_first holds the table entries until the prefix.
+    for (int bb = tid; bb < c.B; bb += NT) s_first[bb] = table_entries(c, bb);
+    __syncthreads();
+    auto items_for = [&](int ew) {
+        int n = 0;
+        for (int bb = tid; bb < c.B; bb += NT) n += seq_runs(s_first[bb], ew, S);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d);
+        if ((tid & 63) == 0) s_red[tid >> 6] = n;
+        __syncthreads();
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) t += s_red[w];
+        __syncthreads();   // s_red is reused by the next call
+        return t * n_packs;
+    };
+    int ew = E;
+    if (items_for(E) < (int)gridDim.x) {
+        for (int lo_e = 1; lo_e < ew;) {
+            const int mid = (lo_e + ew) >> 1;
+            if (items_for(mid) <= (int)gridDim.x) ew = mid;
+            else lo_e = mid + 1;
+        }
+    }
+    if (blockIdx.x == 0 && tid == 0) *ws.run_len = ew;
 
     // -- item prefix: s_first[b] = first item of sequence b (items per
     //    sequence = active runs * packs)
@@ -829,7 +889,7 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     int *s_scan = lds.u.scan;
     for (int b0 = 0; b0 < c.B; b0 += NT) {
         const int bb = b0 + tid;
-        const int cnt = bb < c.B ? ((c.n_blocks[bb] + E - 1) / E) * n_packs : 0;
+        const int cnt = bb < c.B ? seq_runs(s_first[bb], ew, S) * n_packs : 0;
         // inclusive scan of cnt over the workgroup (Hillis-Steele in LDS)
         s_scan[tid] = cnt;
         __syncthreads();
@@ -862,12 +922,12 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     }
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x)
-        split_item<G, NATIVE>(c, q, ws, scale2, S, item, s_first, lds);
+        split_item<G, NATIVE>(c, q, ws, scale2, S, span, ew, item, s_first, lds);
 }
 
-// Finalize: FPART workgroups per (run, sequence), workgroup x taking run
-// x / FPART; workgroup x also writes the output rows of heads x, x +
-// gridDim.x, ...  A run's valid slots were stored compacted, in groups of
+// Finalize: gridDim.x workgroups per sequence, FPART of them per run:
+// workgroup x takes runs x / FPART + k gridDim.x / FPART, and writes the
+// output rows of heads x, x + gridDim.x, ...  A run's valid slots were stored compacted, in groups of
 // 16; the run's workgroups and their waves take whole groups in turn:
 // a group's scores (one 1 KB block [head][16 slots] per kv-head pack) are
 // read with 1 KB loads, each lane summing exp2(s - M_h) / L_h over its head
@@ -880,22 +940,23 @@ constexpr int FPK = 2;                        // kv-head packs whose scores are 
 #define KVQ_FPART 2
 #endif
 constexpr int FPART = KVQ_FPART;              // workgroups sharing one run's groups
+constexpr int FIN_RUNS = 32;
 
 __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
-                                                    float decay, DecodeWs ws, int S, int G, int P, int n_packs) {
-    const int x = blockIdx.x, b = blockIdx.y, X = gridDim.x;
-    const int split = x / FPART, part = x % FPART;
+                                                    float decay, DecodeWs ws, int S, int span, int G, int P,
+                                                    int n_packs) {
+    const int x = blockIdx.x, b = blockIdx.y, X = gridDim.x, XS = X / FPART;
+    const int part = x % FPART;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lo = lane & 15, hi = lane >> 4;
-    const int nb = c.n_blocks[b];
-    const int s_act = (nb + E - 1) / E;
+    const int nb = table_entries(c, b);
+    const int ew = *ws.run_len;
+    const int s_act = seq_runs(nb, ew, S);
     const int Hq = c.Hq;
-    if (split >= s_act && x >= Hq) return;   // no slots and no output head
+    const int split0 = x < XS * FPART ? x / FPART : s_act;   // first run of this workgroup
+    if (split0 >= s_act && x >= Hq) return;   // no slots and no output head
     __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
     __shared__ float4 red[FT];
-    // valid slots of this run, and the groups of 16 they fill
-    const int n_slots = split < s_act ? ws.ents[(size_t)b * S + split] : 0;
-    const int n_ent = (n_slots + 15) >> 4;
 
     // -- global max / sum per head: tpg lanes of one wave per head, each over
     //    a stride of splits with its loads issued together, then a butterfly
@@ -940,84 +1001,93 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
 
     // -- mass (and importance) of the valid slots of this run, 16 at a time
     //    (a group k: lane (head lo, hi) takes slots 16 k + 4 hi .. + 3)
-    const size_t ek0 = (size_t)(b * S + split) * E;
-    for (int k0 = (part * (FT / 64) + wave) * FB; k0 < n_ent; k0 += FPART * (FT / 64) * FB) {
-        int4 pos[FB];
-        float acc[FB][4];
-#pragma unroll
-        for (int e = 0; e < FB; ++e) {
-            const int k = k0 + e;
-            pos[e] = k < n_ent ? reinterpret_cast<const int4 *>(ws.spos + (ek0 + k) * 16)[hi]
-                               : make_int4(-1, -1, -1, -1);
-            // slots past the run's last are stale
-            const int c0 = 16 * k + 4 * hi;
-            if (c0 + 0 >= n_slots) pos[e].x = -1;
-            if (c0 + 1 >= n_slots) pos[e].y = -1;
-            if (c0 + 2 >= n_slots) pos[e].z = -1;
-            if (c0 + 3 >= n_slots) pos[e].w = -1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
-        }
-        // the importance of these positions, loaded before the scores so that
-        // its latency overlaps theirs (lanes lo == 0 write the slots)
-        float imp_old[FB][4];
-        if (importance && lo == 0) {
+    auto run_mass = [&](int split) {
+        const int n_slots = ws.ents[(size_t)b * S + split];
+        const int n_ent = (n_slots + 15) >> 4;
+        const int rst = run_stride(nb, s_act, ew);
+        const size_t off = (size_t)b * span + (size_t)split * rst;
+        for (int k0 = (part * (FT / 64) + wave) * FB; k0 < n_ent; k0 += FPART * (FT / 64) * FB) {
+            int4 pos[FB];
+            float acc[FB][4];
 #pragma unroll
             for (int e = 0; e < FB; ++e) {
-                const int pp[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
+                const int k = k0 + e;
+                pos[e] = k < n_ent ? reinterpret_cast<const int4 *>(ws.spos + (off + k) * 16)[hi]
+                                   : make_int4(-1, -1, -1, -1);
+                // slots past the run's last are stale
+                const int c0 = 16 * k + 4 * hi;
+                if (c0 + 0 >= n_slots) pos[e].x = -1;
+                if (c0 + 1 >= n_slots) pos[e].y = -1;
+                if (c0 + 2 >= n_slots) pos[e].z = -1;
+                if (c0 + 3 >= n_slots) pos[e].w = -1;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    imp_old[e][i] = pp[i] >= 0 && pp[i] < c.n_cap ? importance[(size_t)b * c.n_cap + pp[i]] : 0.f;
+                for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
             }
-        }
-        for (int p0 = 0; p0 < n_packs; p0 += FPK) {
-            // FPK packs' scores of the round's groups, loads issued together
-            float4 t[FB][FPK];
+            // the importance of these positions, loaded before the scores so that
+            // its latency overlaps theirs (lanes lo == 0 write the slots)
+            float imp_old[FB][4];
+            if (importance && lo == 0) {
+#pragma unroll
+                for (int e = 0; e < FB; ++e) {
+                    const int pp[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        imp_old[e][i] = pp[i] >= 0 && pp[i] < c.n_cap ? importance[(size_t)b * c.n_cap + pp[i]] : 0.f;
+                }
+            }
+            for (int p0 = 0; p0 < n_packs; p0 += FPK) {
+                // FPK packs' scores of the round's groups, loads issued together
+                float4 t[FB][FPK];
+#pragma unroll
+                for (int e = 0; e < FB; ++e)
+#pragma unroll
+                    for (int q = 0; q < FPK; ++q) {
+                        const int k = k0 + e, p = p0 + q;
+                        t[e][q] = k < n_ent && p < n_packs
+                                      ? reinterpret_cast<const float4 *>(ws.score + (off * n_packs + (size_t)p * rst + k) * 256)[lo * 4 + hi]
+                                      : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                    }
+#pragma unroll
+                for (int q = 0; q < FPK; ++q) {
+                    const int p = p0 + q;
+                    const int col = p * P * G + lo;
+                    const bool cv = p < n_packs && lo < min(P, c.Hkv - p * P) * G && Mh[min(col, Hq - 1)] != -INFINITY;
+                    if (!cv) continue;
+                    const float Mx = Mh[col], Rx = Rh[col];
+#pragma unroll
+                    for (int e = 0; e < FB; ++e) {
+                        acc[e][0] = fmaf(exp2_fast(t[e][q].x - Mx), Rx, acc[e][0]);
+                        acc[e][1] = fmaf(exp2_fast(t[e][q].y - Mx), Rx, acc[e][1]);
+                        acc[e][2] = fmaf(exp2_fast(t[e][q].z - Mx), Rx, acc[e][2]);
+                        acc[e][3] = fmaf(exp2_fast(t[e][q].w - Mx), Rx, acc[e][3]);
+                    }
+                }
+            }
 #pragma unroll
             for (int e = 0; e < FB; ++e)
 #pragma unroll
-                for (int q = 0; q < FPK; ++q) {
-                    const int k = k0 + e, p = p0 + q;
-                    t[e][q] = k < n_ent && p < n_packs
-                                  ? reinterpret_cast<const float4 *>(ws.score + ((ek0 * n_packs + (size_t)p * E) + k) * 256)[lo * 4 + hi]
-                                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                }
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int q = 0; q < FPK; ++q) {
-                const int p = p0 + q;
-                const int col = p * P * G + lo;
-                const bool cv = p < n_packs && lo < min(P, c.Hkv - p * P) * G && Mh[min(col, Hq - 1)] != -INFINITY;
-                if (!cv) continue;
-                const float Mx = Mh[col], Rx = Rh[col];
+                    for (int w = 1; w < 16; w <<= 1) acc[e][i] += __shfl_xor(acc[e][i], w);
+            if (lo == 0) {
 #pragma unroll
                 for (int e = 0; e < FB; ++e) {
-                    acc[e][0] = fmaf(exp2_fast(t[e][q].x - Mx), Rx, acc[e][0]);
-                    acc[e][1] = fmaf(exp2_fast(t[e][q].y - Mx), Rx, acc[e][1]);
-                    acc[e][2] = fmaf(exp2_fast(t[e][q].z - Mx), Rx, acc[e][2]);
-                    acc[e][3] = fmaf(exp2_fast(t[e][q].w - Mx), Rx, acc[e][3]);
+                    const int pp[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // a position outside the row stride (a corrupt cache) is skipped
+                        if (pp[i] < 0 || pp[i] >= c.n_cap) continue;
+                        mass[(size_t)b * c.n_cap + pp[i]] = acc[e][i];
+                        if (importance) importance[(size_t)b * c.n_cap + pp[i]] = fmaf(decay, imp_old[e][i], acc[e][i]);
+                    }
                 }
             }
         }
-#pragma unroll
-        for (int e = 0; e < FB; ++e)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int w = 1; w < 16; w <<= 1) acc[e][i] += __shfl_xor(acc[e][i], w);
-        if (lo == 0) {
-#pragma unroll
-            for (int e = 0; e < FB; ++e) {
-                const int pp[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // a position outside the row stride (a corrupt cache) is skipped
-                    if (pp[i] < 0 || pp[i] >= c.n_cap) continue;
-                    mass[(size_t)b * c.n_cap + pp[i]] = acc[e][i];
-                    if (importance) importance[(size_t)b * c.n_cap + pp[i]] = fmaf(decay, imp_old[e][i], acc[e][i]);
-                }
-            }
-        }
-    }
+    };
+    // (the first run straight, further ones in a loop: a loop around the
+    // only run of the usual case was measured slower)
+    if (split0 < s_act) run_mass(split0);
+    for (int split = split0 + XS; split < s_act; split += XS) run_mass(split);
 
     // -- output rows of the heads this workgroup owns: 32 channel quads x
     //    8 split groups, merged in a fixed order
@@ -1087,7 +1157,7 @@ int persistent_grid(int G, bool native, const void *kernel, size_t dyn_lds) {
 bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, float *importance,
                    float decay, float sm_scale, void *ws_ptr, hipStream_t s) {
     DecodeWs ws(ws_ptr, c);
-    const int S = n_splits(c);
+    const int S = n_splits(c), span = score_span(c);
     const int G = c.Hq / c.Hkv;
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     const float scale2 = sm_scale * LOG2E;
@@ -1097,7 +1167,7 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
     {                                                                                                    \
         const int grid = persistent_grid(g, nat, reinterpret_cast<const void *>(attn_split<g, nat>), dyn); \
         if (grid <= 0) return false;                                                                     \
-        hipLaunchKernelGGL((attn_split<g, nat>), dim3(grid), dim3(WAVES * 64), dyn, s, c, qq, mass, ws, scale2, S); \
+        hipLaunchKernelGGL((attn_split<g, nat>), dim3(grid), dim3(WAVES * 64), dyn, s, c, qq, mass, ws, scale2, S, span); \
     }
 #define KVQ_G(g)                                                    \
     case g:                                                         \
@@ -1111,8 +1181,13 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
     }
     {
         const int P = decode_pack(G);
-        hipLaunchKernelGGL(attn_finalize, dim3(S * FPART > c.Hq ? S * FPART : c.Hq, c.B), dim3(FT), 0, s, c, out, mass, importance,
-                           decay, ws, S, G, P, decode_n_packs(c));
+        // FIN_RUNS runs per sequence at a time (more are taken in turn), and
+        // a workgroup per output head.  An odd run count per row keeps the
+        // rows' busy workgroups from landing on the same compute units (with
+        // 64 or 128 workgroups per row the finalize was measured 27% slower).
+        const int X = FPART * (std::max(std::min(S, FIN_RUNS), (c.Hq + FPART - 1) / FPART) | 1);
+        hipLaunchKernelGGL(attn_finalize, dim3(X, c.B), dim3(FT), 0, s, c, out, mass, importance, decay, ws, S, span, G, P,
+                           decode_n_packs(c));
     }
     return hipGetLastError() == hipSuccess;
 }

@@ -7,16 +7,25 @@
 
 namespace kvq {
 
-// Decode split-K: a split covers at most this many table entries of one
-// sequence and kv-head pack (a sequence with nr splits gives split j the
-// entries j, j + nr, j + 2 nr, ...).
+// Decode split-K: a run (split) covers at most this many table entries of
+// one sequence and kv-head pack (a sequence with nr runs gives run j the
+// entries j, j + nr, j + 2 nr, ...).  The decode shortens the runs when the
+// batch leaves workgroups idle, down to MIN_RUN entries for a sequence that
+// fills its table, so a sequence has at most n_splits runs.
 #ifndef KVQ_ENTRIES_PER_SPLIT
 #define KVQ_ENTRIES_PER_SPLIT 64
 #endif
 constexpr int ENTRIES_PER_SPLIT = KVQ_ENTRIES_PER_SPLIT;
+constexpr int MIN_RUN = 16;
 
-inline int n_splits(const kvq_cache &c) {
-    return (c.max_blocks + ENTRIES_PER_SPLIT - 1) / ENTRIES_PER_SPLIT;
+inline int n_splits(const kvq_cache &c) { return (c.max_blocks + MIN_RUN - 1) / MIN_RUN; }
+
+// Score groups (of 16 slots) reserved per sequence and kv-head pack: runs
+// of E entries each take E groups at E-group offsets, like any run layout
+// up to max_blocks + n_splits groups (see run_stride); rounded up to E.
+inline int score_span(const kvq_cache &c) {
+    const int e64 = (c.max_blocks + ENTRIES_PER_SPLIT - 1) / ENTRIES_PER_SPLIT * ENTRIES_PER_SPLIT;
+    return (e64 + n_splits(c) + ENTRIES_PER_SPLIT - 1) / ENTRIES_PER_SPLIT * ENTRIES_PER_SPLIT;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -47,24 +56,29 @@ inline int decode_n_packs(const kvq_cache &c) {
 struct DecodeWs {
     float *ml;         // [B][Hq][S][2]  split max (base-2 units), split sum
     float *o;          // [B][Hq][S][128] split output, unnormalised
-    // The valid slots of a split, in table and slot order, are numbered
-    // 0 .. n-1 (n <= 16 E); their scores and positions are stored compacted.
-    int32_t *ents;     // [B][S] valid slots n of the split
-    int32_t *spos;     // [B][S][16 E] position of valid slot c
-    float *score;      // [B][S][n_packs][E][16 heads][16] base-2 scaled score of
-                       // valid slot c at [c / 16][head][c % 16]
+    // The valid slots of a run, in table and slot order, are numbered
+    // 0 .. n-1 (n <= 16 x its entries); their scores and positions are
+    // stored compacted in groups of 16, run j of a sequence from group
+    // j * st (st: the run stride, at least the entries of any of its runs).
+    int32_t *ents;     // [B][S] valid slots n of the run
+    int32_t *run_len;  // [1] most entries per run, chosen by the split kernel
+    int32_t *spos;     // [B][span][16] position of valid slot c at [j st + c / 16][c % 16]
+    float *score;      // [B][span][n_packs][16 heads][16]: the base-2 scaled score
+                       // of valid slot c of pack p at group (j st) n_packs + p st +
+                       // c / 16, [head][c % 16] (a run's packs adjacent)
     static size_t bytes(const kvq_cache &c) {
-        const size_t S = n_splits(c), E = ENTRIES_PER_SPLIT;
+        const size_t S = n_splits(c), SP = score_span(c);
         return align256(8L * c.B * c.Hq * S) + align256(512L * c.B * c.Hq * S) + align256(4L * c.B * S) +
-               align256(64L * c.B * S * E) + align256(1024L * c.B * S * E * decode_n_packs(c));
+               align256(4) + align256(64L * c.B * SP) + align256(1024L * c.B * SP * decode_n_packs(c));
     }
     DecodeWs(void *ws, const kvq_cache &c) {
-        const size_t S = n_splits(c), E = ENTRIES_PER_SPLIT;
+        const size_t S = n_splits(c), SP = score_span(c);
         char *p = (char *)ws;
-        ml = (float *)p;    p += align256(8L * c.B * c.Hq * S);
-        o = (float *)p;     p += align256(512L * c.B * c.Hq * S);
-        ents = (int32_t *)p; p += align256(4L * c.B * S);
-        spos = (int32_t *)p; p += align256(64L * c.B * S * E);
+        ml = (float *)p;      p += align256(8L * c.B * c.Hq * S);
+        o = (float *)p;       p += align256(512L * c.B * c.Hq * S);
+        ents = (int32_t *)p;  p += align256(4L * c.B * S);
+        run_len = (int32_t *)p; p += align256(4);
+        spos = (int32_t *)p;  p += align256(64L * c.B * SP);
         score = (float *)p;
     }
 };

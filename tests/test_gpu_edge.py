@@ -132,6 +132,25 @@ def test_empty_blocks_left_in_table():
     assert_mass_close(oc.st["seq_len"], ref, got)
 
 
+@pytest.mark.parametrize("B,n", [(1, 1000), (2, 1040), (40, 300)])
+def test_full_tables_and_short_runs(B, n):
+    """Tables filled to max_blocks (Reasoning tokens only, 16 to a block).
+    A small batch is cut into short runs to spread over the workgroups, and
+    a full table caps a sequence's run count at the partials it holds."""
+    log(f"[edge] full tables B={B} n={n}")
+    nbk = math.ceil(n / 16)
+    g = small_geometry(B, 8, 2, n, max_blocks=nbk, n_cap=n + 16)
+    oc, gc = _mk(g, identity=False)
+    rng = np.random.default_rng(n)
+    _fill(oc, gc, rng, n, lambda i: np.zeros(B, np.uint8))
+    assert (gc.state_numpy()["n_blocks"] == nbk).all()
+    q = rng.standard_normal((B, 8, HD)).astype(np.float16)
+    imp = rng.exponential(0.1, (B, g.n_cap)).astype(np.float32)
+    ref, got = _decode(oc, gc, q, imp, 0.9)
+    assert_attention_close(ref, got)
+    assert_mass_close(oc.st["seq_len"], ref, got)
+
+
 @pytest.mark.parametrize("keep,qw,rw", [(0, 0, 0), (0, 10, 10), (10 ** 6, 0, 0), (5, 400, 400), (1, 0, 1)])
 def test_degenerate_eviction(keep, qw, rw):
     log(f"[edge] evict keep={keep} qw={qw} rw={rw}")
