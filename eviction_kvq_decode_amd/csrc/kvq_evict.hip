@@ -13,9 +13,10 @@
 // bytes never move; blocks that become empty leave the table and go back to
 // their pool's free list for in-place reuse.
 //
-// evict_select: one 1024-thread workgroup per sequence, one thread per slot
-//   in each pass.  Candidate keys (order-preserving importance bits, then
-//   inverted position, so ties go to the lower position) are radix-selected
+// evict_keys + evict_select: eight workgroups per sequence build one key
+//   word per slot; then one 1024-thread workgroup per sequence, one thread
+//   per slot in each pass.  Candidate keys (order-preserving importance bits,
+//   then inverted position, so ties go to the lower position) are radix-selected
 //   for the k-th largest; losers' mask bits are cleared; the table row is
 //   compacted in order with a ballot prefix scan; freed entries are listed
 //   in table order.
@@ -44,6 +45,10 @@ constexpr int DROP_THREADS = 256;
 constexpr int DROP_WGS = 16;
 constexpr int DROP_WAVES = DROP_WGS * DROP_THREADS / 64;
 constexpr int TBE_RUN = 16;  // chunks of 64 positions / candidates a wave takes per pass
+// top-k's slot keys: KEY_WGS workgroups of KEY_THREADS per sequence
+constexpr int KEY_WGS = EVICT_KEY_WGS;
+constexpr int KEY_THREADS = 256;
+constexpr int KEY_UNROLL = 8;
 
 __device__ inline uint32_t order_bits(float f) {
     uint32_t u = __float_as_uint(f);
@@ -139,35 +144,36 @@ __device__ inline void clear_and_compact(const kvq_cache &c, int b, uint64_t *ke
     if (tid < 4) ws.nfreed[b * 4 + tid] = tid < 3 ? pool_cnt[tid] : freed_base;
 }
 
-// One word per slot (slot s of entry e at 16 e + s), thread per slot:
-// 0 for a cleared slot, 1 for a valid slot outside [lo, hi), else the
-// candidate's key (a finite importance gives a key >= 2^55).  SEL_UNROLL
-// slots per thread and batch; the entry, then its mask and positions, then
-// the importance, each level's loads issued together.  Without an
-// importance a candidate's word is 3.  pmap, if given, receives
-// (pool << 30) | slot for each candidate position.  Returns this thread's
-// candidate count.
-__device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const float *imp, int nslot, int lo,
-                                int hi, uint64_t *key, uint32_t *pmap) {
+// One word per slot (slot s of entry e at 16 e + s), thread per slot, for
+// the slots [i_begin, i_end) of a row: 0 for a cleared slot, 1 for a valid
+// slot outside [lo, hi), else the candidate's key (a finite importance gives
+// a key >= 2^55).  UNROLL slots per thread and batch of NT threads; the
+// entry, then its mask and positions, then the importance, each level's
+// loads issued together.  Without an importance a candidate's word is 3.
+// pmap, if given, receives (pool << 30) | slot for each candidate position.
+// Returns this thread's candidate count.
+template <int NT, int UNROLL>
+__device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const float *imp, int i_begin,
+                                int i_end, int lo, int hi, uint64_t *key, uint32_t *pmap) {
     const int tid = threadIdx.x;
     int my_cand = 0;
-    for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
-        uint32_t ent[SEL_UNROLL], m[SEL_UNROLL];
-        int p[SEL_UNROLL];
+    for (int i0 = i_begin; i0 < i_end; i0 += NT * UNROLL) {
+        uint32_t ent[UNROLL], m[UNROLL];
+        int p[UNROLL];
 #pragma unroll
-        for (int u = 0; u < SEL_UNROLL; ++u) {
-            const int i = i0 + u * SEL_THREADS + tid;
-            ent[u] = i < nslot ? row[i >> 4] : 0u;
+        for (int u = 0; u < UNROLL; ++u) {
+            const int i = i0 + u * NT + tid;
+            ent[u] = i < i_end ? row[i >> 4] : 0u;
         }
 #pragma unroll
-        for (int u = 0; u < SEL_UNROLL; ++u) {
-            const int i = i0 + u * SEL_THREADS + tid;
-            m[u] = i < nslot ? c.mask[ent[u] >> 30][ent[u] & 0x3fffffffu] : 0u;
-            p[u] = i < nslot ? c.pos[ent[u] >> 30][(size_t)(ent[u] & 0x3fffffffu) * BLK + (i & 15)] : -1;
+        for (int u = 0; u < UNROLL; ++u) {
+            const int i = i0 + u * NT + tid;
+            m[u] = i < i_end ? c.mask[ent[u] >> 30][ent[u] & 0x3fffffffu] : 0u;
+            p[u] = i < i_end ? c.pos[ent[u] >> 30][(size_t)(ent[u] & 0x3fffffffu) * BLK + (i & 15)] : -1;
         }
 #pragma unroll
-        for (int u = 0; u < SEL_UNROLL; ++u) {
-            const int i = i0 + u * SEL_THREADS + tid;
+        for (int u = 0; u < UNROLL; ++u) {
+            const int i = i0 + u * NT + tid;
             uint64_t kk = 0;
             if ((m[u] >> (i & 15)) & 1u) {
                 kk = 1;
@@ -177,40 +183,60 @@ __device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const f
                     if (pmap) pmap[p[u]] = (uint32_t)i | (ent[u] & 0xc0000000u);
                 }
             }
-            if (i < nslot) key[i] = kk;
+            if (i < i_end) key[i] = kk;
         }
     }
     return my_cand;
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const float *importance,
-                                                            const int32_t *keep_k, int q_window,
-                                                            int recent_window, EvictWs ws) {
+// Top-k, step 1: one word per slot (slot_keys), a sequence's row shared by
+// KEY_WGS workgroups (grid KEY_WGS x B) in contiguous parts; each part's
+// candidate count goes to ws.kcnt.
+__global__ __launch_bounds__(KEY_THREADS) void evict_keys(kvq_cache c, const float *importance, int q_window,
+                                                          int recent_window, EvictWs ws) {
+    const int part = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int nslot = c.n_blocks[b] * BLK;
+    const int share = (nslot + KEY_WGS - 1) / KEY_WGS;
+    const int i0 = min(nslot, part * share), i1 = min(nslot, i0 + share);
+    const int lo = q_window, hi = c.seq_len[b] - recent_window;
+    int my_cand = slot_keys<KEY_THREADS, KEY_UNROLL>(c, c.table + (size_t)b * c.max_blocks,
+                                                     importance + (size_t)b * c.n_cap, i0, i1, lo, hi,
+                                                     ws.cand + (size_t)b * c.max_blocks * BLK, nullptr);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) my_cand += __shfl_xor(my_cand, off);
+    __shared__ int wsum[KEY_THREADS / 64];
+    if ((tid & 63) == 0) wsum[tid >> 6] = my_cand;
+    __syncthreads();
+    if (tid == 0) {
+        int n = 0;
+#pragma unroll
+        for (int w = 0; w < KEY_THREADS / 64; ++w) n += wsum[w];
+        ws.kcnt[b * KEY_WGS + part] = n;
+    }
+}
+
+// Top-k, step 2 (one workgroup per sequence): the k-th largest key, then
+// the losers cleared and the row compacted.
+__global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const int32_t *keep_k, EvictWs ws) {
     const int b = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
     const int nb = c.n_blocks[b];
     const int nslot = nb * BLK;
-    const int lo = q_window, hi = c.seq_len[b] - recent_window;
     uint32_t *row = c.table + (size_t)b * c.max_blocks;
-    const float *imp = importance + (size_t)b * c.n_cap;
     uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
 
     __shared__ uint32_t hist[RADIX];
-    __shared__ int s_digit, s_cum, s_ncand;
+    __shared__ int s_digit, s_cum;
     __shared__ int wave_tot[SEL_WAVES];
     __shared__ int pool_cnt[4];
-    if (tid == 0) s_ncand = 0;
     if (tid < 4) pool_cnt[tid] = 0;
     __syncthreads();
 
-    // 1. one word per slot: the candidate keys
-    int my_cand = slot_keys(c, row, imp, nslot, lo, hi, key, nullptr);
+    // 1. the candidates counted by evict_keys
+    int n = 0;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) my_cand += __shfl_xor(my_cand, off);
-    if (lane == 0) atomicAdd(&s_ncand, my_cand);
-    __syncthreads();
-    const int n = s_ncand;
+    for (int j = 0; j < KEY_WGS; ++j) n += ws.kcnt[b * KEY_WGS + j];
     const int k = max(keep_k[b], 0);
     const bool evicting = n > k;
 
@@ -545,7 +571,7 @@ __device__ inline SegOrder seg_order(const kvq_cache &c, int b, const float *val
     __syncthreads();
 
     // 1.
-    slot_keys(c, row, nullptr, nslot, lo, hi, key, pmap);
+    slot_keys<SEL_THREADS, SEL_UNROLL>(c, row, nullptr, 0, nslot, lo, hi, key, pmap);
     __syncthreads();
 
     // 2.
@@ -964,8 +990,9 @@ __global__ __launch_bounds__(256) void evict_push(kvq_cache c, EvictWs ws) {
 bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *keep_k, int q_window,
                   int recent_window, void *ws_ptr, hipStream_t s) {
     EvictWs ws(ws_ptr, c);
-    hipLaunchKernelGGL(evict_select, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, keep_k,
-                       q_window, recent_window, ws);
+    hipLaunchKernelGGL(evict_keys, dim3(KEY_WGS, c.B), dim3(KEY_THREADS), 0, s, c, importance, q_window,
+                       recent_window, ws);
+    hipLaunchKernelGGL(evict_select, dim3(c.B), dim3(SEL_THREADS), 0, s, c, keep_k, ws);
     hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);
     return hipGetLastError() == hipSuccess;
 }

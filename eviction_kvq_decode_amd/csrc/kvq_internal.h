@@ -83,8 +83,11 @@ struct DecodeWs {
     }
 };
 
+constexpr int EVICT_KEY_WGS = 8;   // workgroups per sequence building top-k's slot keys
+
 struct EvictWs {
     uint64_t *cand;    // [B][max_blocks*16] selection keys, one word per slot
+    int32_t *kcnt;     // [B][EVICT_KEY_WGS] candidates per part of a row (top-k)
     uint32_t *freed;   // [B][max_blocks] freed table entries, table order
     int32_t *nfreed;   // [B][4] freed per pool
     int32_t *top;      // [4] free_top before the call
@@ -103,7 +106,8 @@ struct EvictWs {
     int32_t *segn;     // [B][2] segments, Transition segments
     static size_t bytes(const kvq_cache &c) {
         const size_t ms = (size_t)c.max_blocks * 16, slot4 = align256(4L * c.B * ms);
-        return align256(8L * c.B * ms) + align256(4L * c.B * c.max_blocks) + align256(16L * c.B) +
+        return align256(8L * c.B * ms) + align256(4L * EVICT_KEY_WGS * c.B) + align256(4L * c.B * c.max_blocks) +
+               align256(16L * c.B) +
                align256(16) + align256(4L * c.B * c.n_cap) + 3 * slot4 + align256(4L * c.B * (ms + 1)) +
                2 * slot4 + align256(8L * c.B * ms) + slot4 + align256(8L * c.B * (ms + 1)) +
                align256(4L * c.B * (ms + 1)) + align256(8L * c.B);
@@ -112,6 +116,7 @@ struct EvictWs {
         const size_t ms = (size_t)c.max_blocks * 16, slot4 = align256(4L * c.B * ms);
         char *p = (char *)ws;
         cand = (uint64_t *)p;     p += align256(8L * c.B * ms);
+        kcnt = (int32_t *)p;      p += align256(4L * EVICT_KEY_WGS * c.B);
         freed = (uint32_t *)p;    p += align256(4L * c.B * c.max_blocks);
         nfreed = (int32_t *)p;    p += align256(16L * c.B);
         top = (int32_t *)p;       p += align256(16);
