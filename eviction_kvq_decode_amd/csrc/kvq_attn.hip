@@ -8,12 +8,12 @@
 // kernel walks a block table whose blocks carry an eviction mask.
 //
 // attn_split: persistent workgroups over (sequence, kv-head pack, run of
-//   table entries) items, the run length chosen per call so that the items
-//   fill whole rounds of the grid.  Online softmax in base 2; writes the split's (max, sum, unnormalised
-//   output) and every score it computed (needed later for the mass, whose
-//   normaliser is only known once all splits are done).
-// attn_finalize: one workgroup per (sequence, run of table entries): merges
-//   the splits (log-sum-exp), writes the output rows, and turns the stored
+//   table entries) items; runs are shortened when a small batch would leave
+//   workgroups idle.  Online softmax in base 2; writes the run's (max, sum,
+//   unnormalised output) and every score it computed (needed later for the
+//   mass, whose normaliser is only known once all runs are done).
+// attn_finalize: two workgroups per (sequence, run of table entries): merges
+//   the runs (log-sum-exp), writes the output rows, and turns the stored
 //   scores into mass / importance in a fixed head order (no float atomics).
 #include <math.h>
 
