@@ -46,9 +46,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_plan(kvq_cache c, const u
     const uint32_t *row = c.table + (size_t)b * c.max_blocks;
     const uint16_t *mask = c.mask[tag];
     // Scan the table in rounds; each thread issues PLAN_UNROLL independent
-    // loads per round so the dependent table -> mask chain overlaps.
+    // loads per round so the dependent table -> mask chain overlaps.  The
+    // thread holding the first entry with a free slot writes the plan from
+    // its registers.
     for (int base = 0; base < nb; base += PLAN_THREADS * PLAN_UNROLL) {
         uint32_t ent[PLAN_UNROLL];
+        uint32_t m[PLAN_UNROLL];
 #pragma unroll
         for (int u = 0; u < PLAN_UNROLL; ++u) {
             const int e = base + u * PLAN_THREADS + tid;
@@ -58,21 +61,28 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_plan(kvq_cache c, const u
 #pragma unroll
         for (int u = 0; u < PLAN_UNROLL; ++u) {
             const int e = base + u * PLAN_THREADS + tid;
-            if (e < nb && (int)(ent[u] >> 30) == tag && mask[ent[u] & 0x3fffffffu] != 0xffff)
-                mine = min(mine, e);
+            m[u] = 0xffffu;
+            if (e < nb && (int)(ent[u] >> 30) == tag) {
+                m[u] = mask[ent[u] & 0x3fffffffu];
+                if (m[u] != 0xffffu) mine = min(mine, e);
+            }
         }
         if (mine != INT_MAX) atomicMin(&first, mine);
         __syncthreads();
-        if (first != INT_MAX) break;
+        const int f = first;   // the same in every thread
+        if (f != INT_MAX) {
+#pragma unroll
+            for (int u = 0; u < PLAN_UNROLL; ++u)
+                if (base + u * PLAN_THREADS + tid == f) {
+                    ws.need[b] = -1;
+                    ws.entry[b] = (int32_t)ent[u];
+                    ws.slot[b] = __builtin_ctz(~m[u]);
+                }
+            return;
+        }
     }
     if (tid == 0) {
-        if (first != INT_MAX) {
-            const uint32_t ent = row[first];
-            const uint16_t m = mask[ent & 0x3fffffffu];
-            ws.need[b] = -1;
-            ws.entry[b] = (int32_t)ent;
-            ws.slot[b] = __builtin_ctz(~(uint32_t)m);
-        } else if (nb >= c.max_blocks) {
+        if (nb >= c.max_blocks) {
             ws.need[b] = -2;
             *c.status = KVQ_ENOSPC;
         } else {
