@@ -64,6 +64,12 @@ def test_identical_keys_give_mean_of_values():
     for h in range(8):
         _, V, pos = dense_kv(c, 0, h // 4)
         assert np.allclose(out[0, h], V.mean(axis=0), rtol=1e-12, atol=1e-14)
+        # and the mean of the fp16 inputs, within half a 4-bit step per
+        # group (bounded from the inputs: (max - min) / 15 rounded up to fp16)
+        vin = v[:, 0, h // 4].astype(np.float64).reshape(n, 4, 32)
+        half_step = (vin.max(axis=2) - vin.min(axis=2)) / 15 * (1 + 2.0 ** -10) * (0.5 + 2.0 ** -18)
+        bound = np.repeat(half_step.mean(axis=0), 32)
+        assert np.all(np.abs(out[0, h] - vin.reshape(n, 128).mean(axis=0)) <= bound + 1e-12)
     assert np.allclose(mass[0, :n], 8.0 / n, rtol=1e-12)
 
 
