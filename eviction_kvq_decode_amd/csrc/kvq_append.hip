@@ -80,6 +80,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_plan(kvq_cache c, const u
                 }
             return;
         }
+        // every thread has read `first` before any thread of the next round
+        // may lower it (f is uniform, so the barrier is too)
+        __syncthreads();
     }
     if (tid == 0) {
         if (nb >= c.max_blocks) {

@@ -176,16 +176,25 @@ def test_identical_keys_closed_form():
     oc, gc = _mk(g)
     rng = np.random.default_rng(5)
     kvec = rng.standard_normal((1, 2, HD)).astype(np.float16)
+    vin = []
     for i in range(300):
         v = rng.standard_normal((1, 2, HD)).astype(np.float16)
+        vin.append(v[0])
         _append(oc, gc, kvec, v, np.array([1], np.uint8))
     q = rng.standard_normal((1, 8, HD)).astype(np.float16)
     ref, got = _decode(oc, gc, q)
     assert np.all(np.abs(got[1][0, :300] - 8 / 300) <= 1e-5)
     vmean = np.stack([np.mean([oc.dequant_slot(p, b, kh, s)[1] for p, b, s, _ in oc.valid_slots(0)], axis=0)
                       for kh in range(2)])
+    # the mean of the fp16 inputs themselves, within half a 4-bit step per
+    # group (bounded from the inputs) plus the output tolerance
+    vin = np.stack(vin).astype(np.float64).reshape(300, 2, 4, 32)
+    half = (vin.max(axis=3) - vin.min(axis=3)) / 15 * (1 + 2.0 ** -10) * (0.5 + 2.0 ** -18)
+    in_bound = np.repeat(half.mean(axis=0), 32, axis=1)          # [kv head][128]
+    in_mean = vin.reshape(300, 2, HD).mean(axis=0)
     for h in range(8):
         assert np.all(np.abs(got[0][0, h] - vmean[h // 4]) <= 1e-3 + 2e-3 * np.abs(vmean[h // 4]))
+        assert np.all(np.abs(got[0][0, h] - in_mean[h // 4]) <= in_bound[h // 4] + 1e-3 + 2e-3 * np.abs(in_mean[h // 4]))
 
 
 def test_dominant_key_closed_form():
@@ -207,3 +216,57 @@ def test_dominant_key_closed_form():
     vj = [oc.dequant_slot(p, b, 0, s)[1] for p, b, s, ps in oc.valid_slots(0) if ps == 77][0]
     for h in range(4):
         assert np.all(np.abs(got[0][0, h] - vj) <= 1e-3 + 2e-3 * np.abs(vj))
+
+
+def test_append_first_free_slot_past_a_scan_round():
+    """Long tables whose first free slot of the token's type lies past the
+    first 1024 table entries (one scan round of the slot search) and past
+    2048 (two rounds): the append must still take the first free slot in
+    table order, and then the next ones, bit-exact with the oracle."""
+    log("[edge] append: first free slot past a scan round")
+    B, nent = 3, 2300
+    g = small_geometry(B, 4, 1, 16 * nent, max_blocks=nent + 8, n_cap=16 * nent + 64,
+                       pool_blocks=(B * nent, B * nent, B * nent))
+    st = wl.empty_state(g, identity_ids=True)
+    rng = np.random.default_rng(11)
+    nxt = [0, 0, 0]
+    # sequence b: full blocks of every type, and E blocks with one free slot
+    # at these table entries (all later than the first scan round for b > 0)
+    free_at = {0: [1100, 1500], 1: [2100, 2200], 2: [700, 1030]}
+    for b in range(B):
+        pos = 0
+        for e in range(nent):
+            p = 1 if e in free_at[b] else int(rng.integers(0, 3))
+            if p == 1 and e not in free_at[b] and e % 7 == 0:
+                p = 0
+            bid = nxt[p]
+            nxt[p] += 1
+            st["table"][b * g.max_blocks + e] = (p << 30) | bid
+            m = 0xFFFF
+            if e in free_at[b]:
+                m &= ~(1 << int(rng.integers(0, 16))) & 0xFFFF
+            st[f"mask{p}"][bid] = m
+            for s in range(16):
+                if (m >> s) & 1:
+                    st[f"pos{p}"][bid * 16 + s] = pos
+                    pos += 1
+        st["n_blocks"][b] = nent
+        st["seq_len"][b] = pos
+    for p in range(3):
+        # pops hand out the ids above the ones in use
+        free = np.zeros(g.pool_blocks[p], dtype=np.uint32)
+        free[: g.pool_blocks[p] - nxt[p]] = np.arange(g.pool_blocks[p] - 1, nxt[p] - 1, -1)
+        st[f"free{p}"] = free
+        st["free_top"][p] = g.pool_blocks[p] - nxt[p]
+    oc, gc = _mk(g, state=st)
+    for i in range(4):
+        k = rng.standard_normal((B, 1, HD)).astype(np.float16)
+        v = rng.standard_normal((B, 1, HD)).astype(np.float16)
+        _append(oc, gc, k, v, np.ones(B, np.uint8))
+        gst = gc.state_numpy()
+        assert_same_cache(oc, gst)
+    # the first two appends filled the two holes of every sequence in order
+    for b in range(B):
+        for e in free_at[b]:
+            ent = int(oc.table_row(b)[e])
+            assert ent >> 30 == 1 and oc.st["mask1"][ent & 0x3FFFFFFF] == 0xFFFF
