@@ -46,6 +46,12 @@ TBE_PARAMS = (64, 4, 8)
 # the importance as the window score, pivotal above 8x the mean, runs
 # shorter than 16 candidates merged ("TAM", section 2)
 TAM_PARAMS = (8.0, 16)
+# the arithmetic of the path: codes widened to exact fp16 MFMA operands
+# against fp16 q / P', accumulated in fp32; softmax, mass and the merge in fp32
+DTYPE = "fp16-mfma/fp32-acc"
+# rotate cache copies until they hold at least this many bytes (2x the MALL)
+MALL_ROTATE_BYTES = 512e6
+DECODE_KERNEL = "kvq_decode_attention (split + finalize)"
 ROW_BYTES = (288, 160, 96)   # K+V codes + (scale, zero) per token per kv head, R/E/T
 
 
@@ -116,6 +122,27 @@ def committed_traffic(workload: str):
     return d["hbm_bytes_per_call"] if h.hexdigest() == d["sources_sha256"] else None
 
 
+def host_cpu(units: int) -> dict:
+    """The host the oracle runs on: cores this process may use, the CPU
+    model, and the OpenMP threads the oracle's decode can keep busy (it runs
+    over (sequence, kv head) pairs, `units` of them)."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    omp = int(os.environ.get("OMP_NUM_THREADS", nproc))
+    return {"nproc": nproc, "model": model, "threads": max(1, min(omp, units))}
+
+
 def cpu_baseline(w, toks, n_seq: int, seconds: float):
     """Time the CPU oracle on the first n_seq sequences of the workload."""
     from eviction_kvq_decode_amd import workloads as wl
@@ -140,11 +167,11 @@ def cpu_baseline(w, toks, n_seq: int, seconds: float):
         reps += 1
         step += 1
     dt = time.time() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": n_seq * reps / dt, "unit": "tokens/s", "cores": min(n_seq, threads),
-            "kind": "oracle",
+    hc = host_cpu(n_seq * w.Hkv)
+    return {"value": n_seq * reps / dt, "unit": "tokens/s", "cores": hc["threads"],
+            "kind": "oracle", "nproc": hc["nproc"], "cpu_model": hc["model"],
             "sample": f"{n_seq} of {w.B} sequences at full length, {reps} append+decode steps "
-                      f"in {dt:.1f}s (fp64 C, OpenMP over sequences)"}
+                      f"in {dt:.1f}s (fp64 C, OpenMP over (sequence, kv head) pairs)"}
 
 
 def cpu_baseline_evict(w, toks, n_seq: int, seconds: float):
@@ -171,11 +198,12 @@ def cpu_baseline_evict(w, toks, n_seq: int, seconds: float):
         oc.evict(imp, keep_k, w.q_window, w.recent_window)
         busy += time.time() - t0
         reps += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": n_seq * reps / busy, "unit": "tokens/s", "cores": min(n_seq, threads),
-            "kind": "oracle",
+    hc = host_cpu(n_seq * w.Hkv)
+    return {"value": n_seq * reps / busy, "unit": "tokens/s", "cores": hc["threads"],
+            "kind": "oracle", "nproc": hc["nproc"], "cpu_model": hc["model"],
             "sample": f"{n_seq} of {w.B} sequences at full length, {reps} decode+evict steps "
-                      f"in {busy:.1f}s (fp64 C, OpenMP over sequences)"}
+                      f"in {busy:.1f}s (fp64 C, decode OpenMP over (sequence, kv head) pairs, "
+                      f"eviction over sequences)"}
 
 
 def evict_bench(args, w):
@@ -277,7 +305,7 @@ def evict_bench(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, "
                                f"{int(n.min())}-{int(n.max())} positions/seq; step = decode with "
@@ -287,8 +315,9 @@ def evict_bench(args, w):
                    "compressed_kv_mb_per_step": round(kvb / 1e6, 1)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": committed_traffic(args.workload),
-                     "kernel": "kvq_decode_attention (split + finalize)",
-                     "avg_us": float(dec_ms.mean() * 1e3)},
+                     "kernel": DECODE_KERNEL, "avg_us": float(dec_ms.mean() * 1e3),
+                     "us": {"mean": float(dec_ms.mean() * 1e3), "p10": float(np.quantile(dec_ms, 0.1) * 1e3),
+                            "p50": float(np.median(dec_ms) * 1e3), "p90": float(np.quantile(dec_ms, 0.9) * 1e3)}},
         "evict": {"kernel": "kvq_evict_topk (select + push)", "avg_us": float(evi_ms.mean() * 1e3),
                   "bytes": evb, "achieved_gbs": ev_gbs, "frac": ev_gbs / HBM_PEAK_GBS},
         "evict_tbe": {"kernel": "kvq_evict_tbe (prep + drop + compact + push)", "avg_us": float(tbe_ms.mean() * 1e3),
@@ -378,7 +407,7 @@ def ct_bench(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, {n0} cached tokens/seq, "
                                f"{w.loop_steps} generated; budget {w.keep} + windows "
@@ -446,22 +475,24 @@ def main():
     toks = wl.lockstep_tokens(w, n_cap, threads=min(16, os.cpu_count() or 1))
     g = wl.geometry_for(w, toks.seq_tags)
     log(f"[gen] {w.name}: tokens generated in {time.time() - t0:.1f}s; geometry {g}")
-    t0 = time.time()
-    cache = build_gpu_cache(w, toks, g)
-    log(f"[gpu] cache built in {time.time() - t0:.1f}s")
-
     # compressed-KV bytes the decode must read at each step
     valid = toks.keep[:, : toks.tags.shape[0]].T & (toks.tags != wl.TAG_SKIP)
     base_bytes = kv_bytes(toks.tags[valid], w.Hkv)
+    # a cache that fits in the 256 MB Infinity Cache (MALL) would be served
+    # from it on the next step: rotate copies whose total exceeds it twice over
+    n_copies = max(1, math.ceil(MALL_ROTATE_BYTES / base_bytes))
+    t0 = time.time()
+    caches = [build_gpu_cache(w, toks, g) for _ in range(n_copies)]
+    log(f"[gpu] {n_copies} cache cop{'y' if n_copies == 1 else 'ies'} built in {time.time() - t0:.1f}s")
     B = w.B
     steps_k, steps_v, steps_t, steps_q, step_bytes = [], [], [], [], []
-    acc = base_bytes
+    acc = [base_bytes] * n_copies
     for s in range(total_steps):
         k, v, tags = wl.step_tokens(w, s)
         steps_k.append(k), steps_v.append(v), steps_t.append(tags)
         steps_q.append(wl.queries(w, s))
-        acc += kv_bytes(tags, w.Hkv)
-        step_bytes.append(acc)
+        acc[s % n_copies] += kv_bytes(tags, w.Hkv)
+        step_bytes.append(acc[s % n_copies])
     K = torch.from_numpy(np.stack(steps_k)).cuda()
     V = torch.from_numpy(np.stack(steps_v)).cuda()
     T = torch.from_numpy(np.stack(steps_t)).cuda()
@@ -472,6 +503,7 @@ def main():
           for _ in range(total_steps)]
 
     def step(s):
+        cache = caches[s % n_copies]
         cache.append(K[s], V[s], T[s])
         ev[s][0].record()
         cache.decode(Q[s], out, mass)
@@ -493,15 +525,18 @@ def main():
         step(s)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    if cache.status != 0:
-        raise RuntimeError(f"status {cache.status} after timed steps")
-    dec_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, total_steps)]
+    for cache in caches:
+        if cache.status != 0:
+            raise RuntimeError(f"status {cache.status} after timed steps")
+    dec_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, total_steps)])
     dec_bytes = step_bytes[args.warmup:]
-    achieved = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
+    achieved = sum(dec_bytes) / (dec_ms.sum() * 1e-3) / 1e9
     ms_per_step = dt * 1e3 / args.steps
-    log(f"[gpu] step {ms_per_step * 1e3:.1f} us, decode call {np.mean(dec_ms) * 1e3:.1f} us "
-        f"(min {np.min(dec_ms) * 1e3:.1f}), {dec_bytes[-1] / 1e6:.1f} MB compressed KV, "
-        f"{achieved:.0f} GB/s")
+    dec_us = {"mean": float(dec_ms.mean() * 1e3), "p10": float(np.quantile(dec_ms, 0.1) * 1e3),
+              "p50": float(np.median(dec_ms) * 1e3), "p90": float(np.quantile(dec_ms, 0.9) * 1e3)}
+    log(f"[gpu] step {ms_per_step * 1e3:.1f} us, decode call {dec_us['mean']:.1f} us "
+        f"(p10 {dec_us['p10']:.1f}, p50 {dec_us['p50']:.1f}, p90 {dec_us['p90']:.1f}), "
+        f"{dec_bytes[-1] / 1e6:.1f} MB compressed KV, {achieved:.0f} GB/s")
 
     result = {
         "metric": METRIC,
@@ -514,7 +549,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, "
                                f"{int(n.max())} logical positions/seq, "
@@ -526,8 +561,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": committed_traffic(args.workload) if not w.codec else None,
-                     "kernel": "kvq_decode_attention (split + finalize)",
-                     "avg_us": float(np.mean(dec_ms) * 1e3)},
+                     "kernel": DECODE_KERNEL, "avg_us": dec_us["mean"], "us": dec_us,
+                     "cache_copies": n_copies},
         "cpu_baseline": None,
     }
     del K, V, Q

@@ -225,9 +225,11 @@ kvq_status kvq_evict_tbe(const kvq_cache *cache, const float *importance, int32_
  * recent_window are the candidates; the others are kept.  A candidate is
  * pivotal if s * N > pivot_c * S (in doubles; N candidates, S the sum of
  * their s) and is kept; the budget left, T = max(0, keep_k - pivotal), goes
- * to the others.  In position order the candidates form segments: a change
- * of thought type opens a new segment once the open one holds min_seg
- * candidates.  Segment i (n_i candidates, m_i not pivotal, S_i the sum of
+ * to the others.  In position order the candidates form runs of one thought
+ * type; a run of at least min_seg candidates opens a new segment and a
+ * shorter run joins the segment before it (the first run always opens one;
+ * the pages merge short segments, and the cache's only segment structure is
+ * the thought type).  Segment i (n_i candidates, m_i not pivotal, S_i the sum of
  * their s) has weight a_i = isqrt(floor(S_i / n_i) * 2^16) * m_i, that is
  * sqrt(mean score) * m_i.  A segment whose share T' a_i / A reaches m_i
  * (T' the budget left after such segments, A the sum of the others'

@@ -517,28 +517,42 @@ static int list_valid(const orc_cache *c, int b, valid_slot *out)
  * position).  If imp_in is non-null, imp_out[b][pos] =
  * float(decay*imp_in + mass) at valid positions and imp_in elsewhere.
  * want: optional [B] flags; sequences with want[b]==0 are skipped.
+ *
+ * Each (sequence, kv head) is independent, so OpenMP runs over those
+ * pairs.  A pair sums the probabilities its G query heads give each valid
+ * slot (heads in order); the mass of a position is then the sum of those
+ * per-kv-head sums in kv-head order, i.e. the sum over all Hq heads.
  */
 void orc_decode(const orc_cache *c, const uint16_t *q, double sm_scale,
                 double *out, double *mass, const float *imp_in, float *imp_out,
                 double decay, const uint8_t *want)
 {
-    const int G = c->Hq / c->Hkv;
+    const int G = c->Hq / c->Hkv, B = c->B, Hkv = c->Hkv;
+    valid_slot **vs = calloc((size_t)B, sizeof(valid_slot *));
+    int *nv = calloc((size_t)B, sizeof(int));
+    double **mslot = calloc((size_t)B, sizeof(double *));   /* [Hkv][n] per sequence */
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int b = 0; b < c->B; ++b) {
+    for (int b = 0; b < B; ++b) {
         if (want && !want[b])
             continue;
-        double *mrow = mass + (long)b * c->n_cap;
-        for (int p = 0; p < c->seq_len[b]; ++p)
-            mrow[p] = 0.0;
         long cap = (long)c->n_blocks[b] * BLK + 1;
-        valid_slot *vs = malloc(sizeof(valid_slot) * cap);
-        int n = list_valid(c, b, vs);
-        double *K = malloc(sizeof(double) * HD * (n + 1));
-        double *V = malloc(sizeof(double) * HD * (n + 1));
-        double *s = malloc(sizeof(double) * (n + 1));
-        for (int kh = 0; kh < c->Hkv; ++kh) {
+        vs[b] = malloc(sizeof(valid_slot) * cap);
+        nv[b] = list_valid(c, b, vs[b]);
+        mslot[b] = calloc((size_t)Hkv * (nv[b] + 1), sizeof(double));
+    }
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        for (int kh = 0; kh < Hkv; ++kh) {
+            if (want && !want[b])
+                continue;
+            const int n = nv[b];
+            const valid_slot *sl = vs[b];
+            double *K = malloc(sizeof(double) * HD * (n + 1));
+            double *V = malloc(sizeof(double) * HD * (n + 1));
+            double *s = malloc(sizeof(double) * (n + 1));
+            double *ms = mslot[b] + (long)kh * (n + 1);
             for (int t = 0; t < n; ++t)
-                orc_dequant_slot(c, vs[t].pool, vs[t].id, kh, vs[t].slot, K + (long)t * HD,
+                orc_dequant_slot(c, sl[t].pool, sl[t].id, kh, sl[t].slot, K + (long)t * HD,
                                  V + (long)t * HD);
             for (int h = kh * G; h < (kh + 1) * G; ++h) {
                 const uint16_t *qh = q + ((long)b * c->Hq + h) * HD;
@@ -565,9 +579,27 @@ void orc_decode(const orc_cache *c, const uint16_t *q, double sm_scale,
                     double p = s[t] / L;
                     for (int d = 0; d < HD; ++d)
                         oh[d] += p * V[(long)t * HD + d];
-                    mrow[vs[t].pos] += p;
+                    ms[t] += p;
                 }
             }
+            free(K);
+            free(V);
+            free(s);
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        if (want && !want[b])
+            continue;
+        const int n = nv[b];
+        double *mrow = mass + (long)b * c->n_cap;
+        for (int p = 0; p < c->seq_len[b]; ++p)
+            mrow[p] = 0.0;
+        for (int t = 0; t < n; ++t) {
+            double m = 0.0;
+            for (int kh = 0; kh < Hkv; ++kh)
+                m += mslot[b][(long)kh * (n + 1) + t];
+            mrow[vs[b][t].pos] = m;
         }
         if (imp_in && imp_out) {
             const float *ii = imp_in + (long)b * c->n_cap;
@@ -575,13 +607,14 @@ void orc_decode(const orc_cache *c, const uint16_t *q, double sm_scale,
             for (int p = 0; p < c->n_cap; ++p)
                 io[p] = ii[p];
             for (int t = 0; t < n; ++t)
-                io[vs[t].pos] = (float)(decay * (double)ii[vs[t].pos] + mrow[vs[t].pos]);
+                io[vs[b][t].pos] = (float)(decay * (double)ii[vs[b][t].pos] + mrow[vs[b][t].pos]);
         }
-        free(vs);
-        free(K);
-        free(V);
-        free(s);
+        free(vs[b]);
+        free(mslot[b]);
     }
+    free(vs);
+    free(nv);
+    free(mslot);
 }
 
 /* ------------------------------------------------------------------ */
