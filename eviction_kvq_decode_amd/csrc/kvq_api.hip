@@ -52,6 +52,18 @@ extern "C" kvq_status kvq_append_quantize(const kvq_cache *c, const void *k_new,
     return kvq::launch_append(*c, k_new, v_new, tags, ws, stream) ? KVQ_OK : KVQ_EHIP;
 }
 
+extern "C" kvq_status kvq_append_quantize_noalloc(const kvq_cache *c, const void *k_new,
+                                                  const void *v_new, const uint8_t *tags,
+                                                  hipStream_t stream) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (!k_new || !v_new || !tags) return KVQ_EINVAL;
+    if (kvq::AppendWs::bytes(*c) > kvq::APPEND_SCRATCH_BYTES) return KVQ_EUNSUPPORTED;
+    void *ws = kvq::append_scratch();
+    if (!ws) return KVQ_EHIP;
+    return kvq::launch_append(*c, k_new, v_new, tags, ws, stream) ? KVQ_OK : KVQ_EHIP;
+}
+
 extern "C" kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, float *out,
                                            float *mass, float *importance, float decay,
                                            float sm_scale, void *ws, size_t ws_bytes,

@@ -16,6 +16,8 @@
 // synchronisation is needed.
 #include <limits.h>
 
+#include <mutex>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -290,6 +292,29 @@ __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *
 }
 
 }  // namespace
+
+// Scratch of the no-allocation append: the plan buffers (AppendWs) for up to
+// APPEND_SCRATCH_BYTES, in a file-scope device array.  Each GPU holds its own
+// copy for the life of the process; its device address is looked up once per
+// device (the array's name is only a host-side stand-in).  Every plan buffer
+// is written by append_plan before append_write reads it, so nothing needs
+// clearing between calls; calls that overlap on one GPU share the array and
+// race.
+__device__ __align__(256) uint8_t scratch[APPEND_SCRATCH_BYTES];
+
+void *append_scratch() {
+    static std::mutex mu;
+    static void *ptr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
 
 bool launch_append(const kvq_cache &c, const void *k_new, const void *v_new, const uint8_t *tags,
                    void *ws_ptr, hipStream_t s) {

@@ -46,6 +46,13 @@ struct AppendWs {
     }
 };
 
+// The no-allocation append keeps AppendWs in a static device array of this
+// size: enough for every batch the library accepts (B <= 1024).
+constexpr size_t APPEND_SCRATCH_BYTES = 16384;
+// Its device address on the current device (looked up once per device), or
+// null if the lookup failed.
+void *append_scratch();
+
 // kv heads whose query heads share one 16-column MFMA tile in decode
 inline int decode_pack(int G) { return 16 / G < 4 ? 16 / G : 4; }
 inline int decode_n_packs(const kvq_cache &c) {

@@ -19,8 +19,8 @@ KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EHIP, KVQ_ENOSPC = 0, -1, -2, -3, -4
 TAG_R, TAG_E, TAG_T, TAG_NONE = 0, 1, 2, 255
 
 EXPORTS = ("kvq_region_bytes", "kvq_workspace_bytes", "kvq_append_quantize",
-           "kvq_decode_attention", "kvq_evict_topk", "kvq_evict_tbe",
-           "kvq_evict_tam")
+           "kvq_append_quantize_noalloc", "kvq_decode_attention", "kvq_evict_topk",
+           "kvq_evict_tbe", "kvq_evict_tam")
 
 
 class KvqError(RuntimeError):
@@ -56,6 +56,8 @@ def lib():
         L.kvq_workspace_bytes.argtypes = [CS]
         L.kvq_append_quantize.restype = ctypes.c_int
         L.kvq_append_quantize.argtypes = [CS, P, P, P, P, ctypes.c_size_t, P]
+        L.kvq_append_quantize_noalloc.restype = ctypes.c_int
+        L.kvq_append_quantize_noalloc.argtypes = [CS, P, P, P, P]
         L.kvq_decode_attention.restype = ctypes.c_int
         L.kvq_decode_attention.argtypes = [CS, P, P, P, P, ctypes.c_float, ctypes.c_float, P,
                                            ctypes.c_size_t, P]
@@ -128,6 +130,13 @@ class Cache:
         _check(lib().kvq_append_quantize(ctypes.byref(self.struct), _ptr(k_new), _ptr(v_new),
                                          _ptr(tags), self.ws_ptr, self.ws_bytes,
                                          self._stream(stream)), "kvq_append_quantize")
+
+    def append_noalloc(self, k_new, v_new, tags, stream=None):
+        """kvq_append_quantize_noalloc: as append, with the library's static
+        scratch instead of this cache's workspace."""
+        _check(lib().kvq_append_quantize_noalloc(ctypes.byref(self.struct), _ptr(k_new), _ptr(v_new),
+                                                 _ptr(tags), self._stream(stream)),
+               "kvq_append_quantize_noalloc")
 
     def decode(self, q, out, mass, importance=None, decay=0.0, sm_scale=None, stream=None):
         """q fp16 [B][Hq][128]; out fp32 [B][Hq][128]; mass (and importance) fp32 [B][n_cap]."""

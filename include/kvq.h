@@ -148,6 +148,20 @@ kvq_status kvq_append_quantize(const kvq_cache *cache, const void *k_new, const 
                                hipStream_t stream);
 
 /*
+ * kvq_append_quantize without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same semantics and kernels; the plan
+ * buffers live in a static device array of the library (16 KiB per GPU, held
+ * until the process ends), enough for every B the library accepts (<= 1024).
+ * A cache whose plan buffers would not fit returns KVQ_EUNSUPPORTED.  Nothing
+ * is allocated or freed.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (concurrent streams) race and must not be
+ * issued; calls ordered on one stream are safe.
+ */
+kvq_status kvq_append_quantize_noalloc(const kvq_cache *cache, const void *k_new, const void *v_new,
+                                       const uint8_t *tags, hipStream_t stream);
+
+/*
  * Decode attention for one query token per sequence ("Back from the
  * Future", Problem Statement: scaled dot-product attention over the cache),
  * plus the per-position attention mass ("TAM", sections 1 and 2.B).

@@ -82,6 +82,7 @@ def test_host_side_validation(over, code):
     s = _dummy_struct(**over)
     buf = 0x100000
     assert L.kvq_append_quantize(ctypes.byref(s), buf, buf, buf, buf, 1 << 40, None) == code
+    assert L.kvq_append_quantize_noalloc(ctypes.byref(s), buf, buf, buf, None) == code
     assert L.kvq_decode_attention(ctypes.byref(s), buf, buf, buf, None, 0.9, 0.1, buf, 1 << 40, None) == code
     assert L.kvq_evict_topk(ctypes.byref(s), buf, buf, 0, 0, buf, 1 << 40, None) == code
     assert L.kvq_evict_tbe(ctypes.byref(s), buf, 64, 1, 4, 0, 0, buf, 1 << 40, None) == code
@@ -96,6 +97,10 @@ def test_bad_arguments_rejected_before_launch():
     assert L.kvq_append_quantize(ctypes.byref(s), None, ok, ok, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_append_quantize(ctypes.byref(s), ok, ok, ok, ok, need - 1, None) == kvq.KVQ_EINVAL
     assert L.kvq_append_quantize(ctypes.byref(s), ok, ok, ok, ok + 8, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_append_quantize_noalloc(ctypes.byref(s), None, ok, ok, None) == kvq.KVQ_EINVAL
+    assert L.kvq_append_quantize_noalloc(ctypes.byref(s), ok, ok, None, None) == kvq.KVQ_EINVAL
+    assert L.kvq_append_quantize_noalloc(ctypes.byref(_dummy_struct(B=1025)), ok, ok, ok, None) == \
+        kvq.KVQ_EUNSUPPORTED
     assert L.kvq_decode_attention(ctypes.byref(s), ok, None, ok, None, 0.9, 0.1, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_topk(ctypes.byref(s), ok, ok, -1, 0, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_topk(ctypes.byref(s), None, ok, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
