@@ -26,7 +26,7 @@ namespace kvq {
 
 namespace {
 
-constexpr int E = ENTRIES_PER_SPLIT;
+constexpr int E = 64;   // table entries a segment walks at a time
 constexpr int MAX_HQ = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -34,23 +34,6 @@ constexpr float LOG2E = 1.4426950408889634f;
 // [0, max_blocks] in a corrupt cache is clamped).
 __device__ inline int table_entries(const kvq_cache &c, int b) {
     return min(max(c.n_blocks[b], 0), c.max_blocks);
-}
-
-// Runs of a sequence with nb table entries when a run holds at most ew of
-// them: never fewer than E-entry runs need, never more than S (the partials
-// held per sequence; S * MIN_RUN >= max_blocks >= nb).
-__device__ inline int seq_runs(int nb, int ew, int S) {
-    if (nb <= 0) return 0;
-    const int lo = (nb + E - 1) / E, nr = (nb + ew - 1) / ew;
-    return nr < lo ? lo : (nr > S ? S : nr);
-}
-
-// Run j holds entries j, j + nr, ...: at most ceil(nb / nr) of them.  Its
-// scores start at group j * run_stride: E-entry runs keep E-aligned areas
-// (nr E <= max_blocks rounded up to E); shorter runs are packed at their
-// longest length (nr ceil(nb / nr) < nb + nr <= max_blocks + S).
-__device__ inline int run_stride(int nb, int nr, int ew) {
-    return ew == E ? E : (nb + nr - 1) / nr;
 }
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -211,14 +194,14 @@ struct WaveState {
     float m;         // running max of head rho (base-2 scaled scores)
     float l;         // this lane's share of the running sum
     float z[NGRP];   // this lane's share of sum p * v_zero - B * P' / mult per group
-    floatx4 o[8];    // sum P' * (B + code), P' = p * v_scale * mult, per 16-channel tile
+    floatx4 o[8];    // sum P' * (B + code), P' = p * v_scale * mult: head rho, channels
+                     // 16 n + 4 r .. + 3 of tile n
     float mult;      // power-of-two headroom factor applied to P'
 };
 
 // ---------------------------------------------------------------------------
 // Block staging.  Each wave owns an LDS stage that holds one block-pack: the
-// (scale, zero) areas of its kv heads at a * 512, the block's 16 slot
-// positions at P * 512 (first pack of a sequence only), kv head a's K codes
+// (scale, zero) areas of its kv heads at a * 512, kv head a's K codes
 // at kcode0(P) + 2048 a and its V codes at vcode0(P) + 2048 a, whatever the
 // bit width (an 8-bit block fills them; 4- and 2-bit blocks use the first
 // half or quarter).  The areas of one part sit at the same place for every
@@ -230,8 +213,8 @@ struct WaveState {
 // cleared slot (p = 0) turns into exact zeros.
 constexpr int STAGE_REGION = 4096 + 512;                        // 8-bit region
 constexpr int CODE_AREA = 2048;                                 // per part and kv head
-__host__ __device__ constexpr int stage_bytes(int P) { return P * STAGE_REGION + 64; }
-__host__ __device__ constexpr int kcode0(int P) { return P * 512 + 64; }
+__host__ __device__ constexpr int stage_bytes(int P) { return P * STAGE_REGION; }
+__host__ __device__ constexpr int kcode0(int P) { return P * 512; }
 __host__ __device__ constexpr int vcode0(int P) { return kcode0(P) + P * CODE_AREA; }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -254,12 +237,11 @@ __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Issue the loads of one block-pack into `stage`, in two parts: PART_V
-// (V codes and both (scale, zero) areas) and PART_K (K codes and the
-// positions).  blk = the pack's first region (kv head kh0) in HBM; np kv heads
-// are real; posb = the block's positions or null.
+// (V codes and both (scale, zero) areas) and PART_K (K codes).  blk = the
+// pack's first region (kv head kh0) in HBM; np kv heads are real.
 constexpr int PART_V = 1, PART_K = 2;
 template <int BITS, int P, int PART>
-__device__ inline void issue_block(uint8_t *stage, const uint8_t *blk, int np, uint32_t m16, const int *posb) {
+__device__ inline void issue_block(uint8_t *stage, const uint8_t *blk, int np, uint32_t m16) {
     constexpr uint32_t CB = 512u * BITS, RB = CB + 512u;
     const int lane = threadIdx.x & 63;
     const uint32_t live4 = ((m16 & 0x000fu) ? 1u : 0u) | ((m16 & 0x00f0u) ? 2u : 0u) |
@@ -338,10 +320,24 @@ __device__ inline void issue_block(uint8_t *stage, const uint8_t *blk, int np, u
                 if (2 * a2 + (lane >> 5) < np) lds_load16(blk + (2u * a2 * RB + soff), stage + a2 * 1024);
         }
     }
-    if constexpr (PART == PART_K) {
-        if (posb != nullptr && lane < 4 && ((m16 >> (4 * lane)) & 15u))
-            lds_load16(reinterpret_cast<const uint8_t *>(posb) + loff, stage + P * 512);
-    }
+}
+
+// 4x4 transpose across the four lanes of a group (lane bits 0-1 = i):
+// lane i's element k becomes lane k's element i.  Two exchange stages, over
+// lane bit 0 / element bit 0, then lane bit 1 / element bit 1 (DPP quad
+// permutations: swap neighbours, swap pairs).
+template <int CTRL>
+__device__ inline float quad_perm(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ inline float4 quad_transpose(float4 r, int lane) {
+    const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
+    // lane bit 0: even lanes send elements 1, 3 and receive the odd lane's 0, 2
+    const float y0 = quad_perm<0xB1>(b0 ? r.x : r.y), y1 = quad_perm<0xB1>(b0 ? r.z : r.w);
+    r = b0 ? make_float4(y0, r.y, y1, r.w) : make_float4(r.x, y0, r.z, y1);
+    // lane bit 1: lanes 0, 1 send elements 2, 3 and receive lanes 2, 3's 0, 1
+    const float z0 = quad_perm<0x4E>(b1 ? r.x : r.z), z1 = quad_perm<0x4E>(b1 ? r.y : r.w);
+    return b1 ? make_float4(z0, z1, r.z, r.w) : make_float4(r.x, r.y, z0, z1);
 }
 
 // The next block-pack's loads, issued by attend_block in two parts: the V
@@ -353,9 +349,9 @@ struct NoNext {
 
 // NAT: the block holds native E4M3 / E2M1 codes (symmetric, zero 0).
 template <int G, int BITS, bool NAT, class Next>
-__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, float *score, int *spos,
-                                    int off, bool has_pos, const uint4 *const *qa, const float *qsum, float scale2,
-                                    WaveState &st, const Next &next) {
+__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, float *tile,
+                                    const uint4 *const *qa, const float *qsum, float scale2, WaveState &st,
+                                    const Next &next) {
     constexpr int P = PACK(G);
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
     const int a_rho = min(lo / G, np - 1);
@@ -472,55 +468,42 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
             s[i] = row_ok && tv[i] ? v[i] * scale2 : -INFINITY;
         }
     }
-    // -- the valid slots' scores, and from the first pack their positions,
-    //    in the split's compacted numbering: valid slot t of this block is
-    //    number off + (valid slots of the block before t)
+    // -- the block's scores: the entry's 1 KB tile is [slot][head] (cleared
+    //    slots -inf; heads past the pack unspecified).  Lane (head lo = 4a +
+    //    i, hi) holds head lo's slots 4hi..4hi+3; a 4x4 transpose inside each
+    //    group of four lanes gives it slot 4hi + i's heads 4a..4a+3, stored
+    //    with one 16-byte write, so the wave writes the whole tile at once.
     {
-        int4 pos4 = make_int4(0, 0, 0, 0);
-        if (has_pos && lo == 0) pos4 = reinterpret_cast<const int4 *>(stage + P * 512)[hi];
-        const int pp[4] = {pos4.x, pos4.y, pos4.z, pos4.w};
-        int cn = off + __popc(m16 & ((1u << (4 * hi)) - 1u));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (tv[i]) {
-                if (row_ok) score[(cn >> 4) * 256 + lo * 16 + (cn & 15)] = s[i];
-                if (has_pos && lo == 0) spos[cn] = pp[i];
-                ++cn;
-            }
-        }
+        const float4 v = quad_transpose(make_float4(s[0], s[1], s[2], s[3]), lo);
+        *reinterpret_cast<float4 *>(tile + (4 * hi + (lo & 3)) * 16 + 4 * (lo >> 2)) = v;
     }
 
-    // -- the K and position reads have landed: the next block-pack's K part.
-    //    No LDS read follows in this block, and the stores above were issued
-    //    before it, so the next block waits for all of its wave's memory
-    //    operations.
+    // -- the K reads have landed: the next block-pack's K part.  No LDS read
+    //    follows in this block, and the stores above were issued before it,
+    //    so the next block waits for all of its wave's memory operations.
     wait_lgkm0();
     next(PART_K);
-    // -- online softmax; the max only moves when some score exceeds it
+    // -- online softmax.  The PV accumulators hold this lane's own head (lo),
+    //    so a rescale is a multiply by the lane's own factor; it is done on
+    //    every block (a branch around it makes the compiler copy the
+    //    accumulators at the join).
     float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    if (__ballot(bm > st.m)) {
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(st.m, bm);
-        const float alpha = st.m == -INFINITY ? 0.f : exp2_fast(st.m - mn);
-        st.m = mn;
-        st.l *= alpha;
-#pragma unroll
-        for (int g = 0; g < NGRP; ++g) st.z[g] *= alpha;
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * hi + i);
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st.o[n][i] *= al[i];
-    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(st.m, bm);
+    const float am = mn == st.m ? 1.f : (st.m == -INFINITY ? 0.f : exp2_fast(st.m - mn));
+    st.m = mn;
     float p[4];
+    float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        p[i] = s[i] == -INFINITY ? 0.f : exp2_fast(s[i] - st.m);
-        st.l += p[i];
+        p[i] = s[i] == -INFINITY ? 0.f : exp2_fast(s[i] - mn);
+        psum += p[i];
     }
+    st.l = fmaf(st.l, am, psum);
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) st.z[g] *= am;
+    float ao = am;   // the accumulators' factor: am, and the headroom change
 
     // -- headroom: P' = p * v_scale * mult must stay inside fp16, and p <= 1,
     //    so the largest v_scale in the stage bounds it.  Scales are
@@ -536,14 +519,14 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
             for (int off = 1; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
             float nm = st.mult;
             while (vmax * nm > P_HEADROOM) nm *= 0.5f;
-            const float f = nm / st.mult;
+            ao *= nm / st.mult;
             st.mult = nm;
-#pragma unroll
-            for (int n = 0; n < 8; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) st.o[n][i] *= f;
         }
     }
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o[n][i] *= ao;
     // -- P' per group in the PV A-operand layout (lane = head, 4 tokens), one
     //    rounding to fp16.  A cleared token has p = 0 and finite stale pairs,
     //    so it contributes exact zeros.
@@ -578,31 +561,34 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
             const half4 pa = mine ? pop[n >> 1] : (half4){};
-            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, v_operand<BITS, NAT>(vw[a], n, vb), st.o[n], 0, 0, 0);
+            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(v_operand<BITS, NAT>(vw[a], n, vb), pa, st.o[n], 0, 0, 0);
         }
     }
 
 }
 
 // Workgroup LDS of the split kernel.  A wave's merged output rows reuse its
-// stage's code area once every wave has left its loop; the prologue's scan
-// buffer shares the stage area too.
+// stage's code area once every wave has left its loop; the prologue's
+// prefix sums share the stage area too.
 template <int P>
 struct SplitLds {
-    uint32_t ent[E];
-    int off[E];              // valid slots before entry k (compacted numbering)
-    uint32_t msk[E];
+    uint32_t ent[E];         // non-empty table entries of the chunk, in order
+    uint32_t msk[E];         // their masks
+    int eix[E];              // their table indices
     int n;
     uint4 qb[NGRP][65];      // [g][lane]: q of column head lane % 16, channel
                              // slice lane / 16 of group g; [g][64] is zero
-    // wave merge: row maxima, scaled row sums and zero-point sums per wave
-    float mm[WAVES][16], lw[WAVES][16], zz[WAVES][16][NGRP];
+    // wave merge: row maxima and scaled row sums per wave
+    float mm[WAVES][16], lw[WAVES][16];
+    // merged rows: padded by 4 floats where the stage has room, so the 16
+    // head rows written at once meet different banks
+    static constexpr int MRS = P >= 3 ? HD + 4 : HD;
     // the stages; a wave's merged output rows go to its own stage's code
     // area (whose stale bytes are harmless), or after the stages when a
     // one-kv-head stage is too small for 16 rows
     union alignas(16) {
         uint8_t stage[WAVES * stage_bytes(P) + (P == 1 ? WAVES * 16 * HD * 4 : 0)];
-        int scan[WAVES * 64];
+        int scan[WAVES * 64 + 1025];
     } u;
     __device__ float *merge_rows(int w) {
         return reinterpret_cast<float *>(u.stage + (P == 1 ? WAVES * stage_bytes(P) + w * 16 * HD * 4
@@ -610,65 +596,18 @@ struct SplitLds {
     }
 };
 
-// One work item (sequence, kv-head pack, run of at most E entries).
+// One segment: table entries [e_begin, e_end) of sequence b for kv-head pack
+// `pack`, taken E entries at a time; writes its partial (max, sum, output)
+// for the pack's heads to segment slot `seg`.
 template <int G, bool NATIVE>
-__device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const DecodeWs &ws,
-                                  float scale2, int S, int span, int ew, int item, const int *s_first,
-                                  SplitLds<PACK(G)> &sh) {
+__device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, const DecodeWs &ws, float scale2,
+                                     int b, int pack, int e_begin, int e_end, int seg, SplitLds<PACK(G)> &sh) {
     constexpr int P = PACK(G);
     const int n_packs = (c.Hkv + P - 1) / P;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lo = lane & 15, hi = lane >> 4;
-    // decode the item: sequence by binary search over the item prefix
-    int lo_b = 0, hi_b = c.B - 1;
-    while (lo_b < hi_b) {
-        const int mid = (lo_b + hi_b + 1) >> 1;
-        if (s_first[mid] <= item) lo_b = mid; else hi_b = mid - 1;
-    }
-    // (item values read from LDS are uniform: keep them in scalar registers)
-    const int b = __builtin_amdgcn_readfirstlane(lo_b);
-    const int r = __builtin_amdgcn_readfirstlane(item - s_first[b]);
-    const int pack = r % n_packs, split = r / n_packs;
     const int kh0 = pack * P, np = min(P, c.Hkv - kh0);
     const bool row_ok = lo < np * G;
-
-    // -- non-empty table entries of this run, compacted (wave 0).  Run j of
-    //    a sequence with nr runs holds table entries j, j + nr, j + 2 nr, ...
-    //    (at most E): every run samples the whole sequence, so the runs of a
-    //    sequence cost about the same whatever the order of its block widths.
-    const int nb = table_entries(c, b);
-    const int nr = __builtin_amdgcn_readfirstlane((s_first[b + 1] - s_first[b]) / n_packs);
-    if (wave == 0) {
-        int n = 0, slots = 0;
-        for (int base = 0; base < E; base += 64) {
-            const int e = split + nr * (base + lane);
-            uint32_t ent = 0, m = 0;
-            if (base + lane < E && e < nb) {
-                ent = c.table[(size_t)b * c.max_blocks + e];
-                m = c.mask[ent >> 30][ent & 0x3fffffffu];
-            }
-            const uint64_t bal = __ballot(m != 0);
-            const int at = n + __popcll(bal & ((1ull << lane) - 1));
-            // valid slots of the entries before this one: a wave prefix sum
-            int cnt = __popc(m), incl = cnt;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int y = __shfl_up(incl, d);
-                if (lane >= d) incl += y;
-            }
-            if (m != 0) {
-                sh.ent[at] = ent;
-                sh.msk[at] = m;
-                sh.off[at] = slots + incl - cnt;
-            }
-            n += __popcll(bal);
-            slots += __shfl(incl, 63);
-        }
-        if (lane == 0) {
-            sh.n = n;
-            if (pack == 0) ws.ents[(size_t)b * S + split] = slots;
-        }
-    }
 
     // -- q of the pack's heads into LDS (zero past the pack), and the
     //    per-group q sums of head lo in registers
@@ -707,63 +646,90 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
 #pragma unroll
     for (int n = 0; n < 8; ++n) st.o[n] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    // -- this wave's entries k = wave, wave + WAVES, ...: the loads of entry
-    //    k + WAVES run while entry k is computed
-    const int n_ent = __builtin_amdgcn_readfirstlane(sh.n);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     uint8_t *stg = sh.u.stage + wv * stage_bytes(P);
-    auto issue = [&](int k, int part) {
-        // block metadata is wave-uniform: keep it in scalar registers
-        const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
-        const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
-        const int pool = (int)(ent >> 30);
-        const uint32_t id = ent & 0x3fffffffu;
-        const int *pb = pack == 0 ? c.pos[pool] + (size_t)id * BLK : nullptr;
-        const uint8_t *blk0 = c.kv[0] + ((size_t)id * c.Hkv + kh0) * (512u * 8 + 512u);
-        const uint8_t *blk1 = c.kv[1] + ((size_t)id * c.Hkv + kh0) * (512u * 4 + 512u);
-        const uint8_t *blk2 = c.kv[2] + ((size_t)id * c.Hkv + kh0) * (512u * 2 + 512u);
-        if (part == PART_V) {
-            if (pool == 0) issue_block<8, P, PART_V>(stg, blk0, np, msk, pb);
-            else if (pool == 1) issue_block<4, P, PART_V>(stg, blk1, np, msk, pb);
-            else issue_block<2, P, PART_V>(stg, blk2, np, msk, pb);
-        } else {
-            if (pool == 0) issue_block<8, P, PART_K>(stg, blk0, np, msk, pb);
-            else if (pool == 1) issue_block<4, P, PART_K>(stg, blk1, np, msk, pb);
-            else issue_block<2, P, PART_K>(stg, blk2, np, msk, pb);
+    float *const score_u = ws.score + ((size_t)b * n_packs + pack) * c.max_blocks * 256;
+    for (int base = e_begin; base < e_end; base += E) {
+        // -- the chunk's non-empty table entries, compacted in table order (wave 0)
+        if (wave == 0) {
+            const int cnt = min(E, e_end - base);
+            int n = 0;
+            for (int k0 = 0; k0 < cnt; k0 += 64) {
+                const int k = k0 + lane;
+                uint32_t ent = 0, m = 0;
+                if (k < cnt) {
+                    ent = c.table[(size_t)b * c.max_blocks + base + k];
+                    m = c.mask[ent >> 30][ent & 0x3fffffffu];
+                }
+                const uint64_t bal = __ballot(m != 0);
+                const int at = n + __popcll(bal & ((1ull << lane) - 1));
+                if (m != 0) {
+                    sh.ent[at] = ent;
+                    sh.msk[at] = m;
+                    sh.eix[at] = base + k;
+                }
+                n += __popcll(bal);
+            }
+            if (lane == 0) sh.n = n;
         }
-    };
-    if (wv < n_ent) {
-        issue(wv, PART_V);
-        issue(wv, PART_K);
-    }
-    // the run's compacted scores of this pack, and its slot positions
-    const int rst = __builtin_amdgcn_readfirstlane(run_stride(nb, nr, ew));
-    const size_t roff = (size_t)b * span + (size_t)split * rst;
-    float *score = ws.score + (roff * n_packs + (size_t)pack * rst) * 256;
-    int *spos = ws.spos + roff * 16;
-    for (int k = wv; k < n_ent; k += WAVES) {
-        // entry k is in the stage once its wave's memory operations are done
-        // (the last ones issued are its K part)
-        wait_vm0();
-        const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
-        const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
-        const int off = __builtin_amdgcn_readfirstlane(sh.off[k]);
-        const int pool = (int)(ent >> 30);
-        const int kn = k + WAVES;
-        auto next = [&](int part) {
-            if (kn < n_ent) issue(kn, part);
+        __syncthreads();
+
+        // -- this wave's entries k = wave, wave + WAVES, ...: the loads of entry
+        //    k + WAVES run while entry k is computed
+        const int n_ent = __builtin_amdgcn_readfirstlane(sh.n);
+        auto issue = [&](int k, int part) {
+            // block metadata is wave-uniform: keep it in scalar registers
+            const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
+            const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
+            const int pool = (int)(ent >> 30);
+            const uint32_t id = ent & 0x3fffffffu;
+            const uint8_t *blk0 = c.kv[0] + ((size_t)id * c.Hkv + kh0) * (512u * 8 + 512u);
+            const uint8_t *blk1 = c.kv[1] + ((size_t)id * c.Hkv + kh0) * (512u * 4 + 512u);
+            const uint8_t *blk2 = c.kv[2] + ((size_t)id * c.Hkv + kh0) * (512u * 2 + 512u);
+            if (part == PART_V) {
+                if (pool == 0) issue_block<8, P, PART_V>(stg, blk0, np, msk);
+                else if (pool == 1) issue_block<4, P, PART_V>(stg, blk1, np, msk);
+                else issue_block<2, P, PART_V>(stg, blk2, np, msk);
+            } else {
+                if (pool == 0) issue_block<8, P, PART_K>(stg, blk0, np, msk);
+                else if (pool == 1) issue_block<4, P, PART_K>(stg, blk1, np, msk);
+                else issue_block<2, P, PART_K>(stg, blk2, np, msk);
+            }
         };
-        if (pool == 0)
-            attend_block<G, 8, NATIVE>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
-        else if (pool == 1)
-            attend_block<G, 4, NATIVE>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
-        else
-            attend_block<G, 2, false>(stg, np, msk, score, spos, off, pack == 0, qa, qsum, scale2, st, next);
+        if (wv < n_ent) {
+            issue(wv, PART_V);
+            issue(wv, PART_K);
+        }
+        for (int k = wv; k < n_ent; k += WAVES) {
+            // entry k is in the stage once its wave's memory operations are done
+            // (the last ones issued are its K part)
+            wait_vm0();
+            const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
+            const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
+            const int e = __builtin_amdgcn_readfirstlane(sh.eix[k]);
+            const int pool = (int)(ent >> 30);
+            const int kn = k + WAVES;
+            auto next = [&](int part) {
+                if (kn < n_ent) issue(kn, part);
+            };
+            float *tile = score_u + (size_t)e * 256;
+            if (pool == 0)
+                attend_block<G, 8, NATIVE>(stg, np, msk, tile, qa, qsum, scale2, st, next);
+            else if (pool == 1)
+                attend_block<G, 4, NATIVE>(stg, np, msk, tile, qa, qsum, scale2, st, next);
+            else
+                attend_block<G, 2, false>(stg, np, msk, tile, qa, qsum, scale2, st, next);
+        }
+        // every wave is done with the chunk's entries before the next chunk's
+        // walk overwrites them
+        __syncthreads();
     }
-    // -- merge the waves of this workgroup and write the run's partial.  Each
-    //    wave publishes its row maxima, then writes its output rows already
-    //    rescaled to the workgroup maximum (zero-point term included) into its
-    //    own stage; the rows are then summed over the waves in a fixed order.
+
+    // -- merge the waves of this workgroup and write the segment's partial.
+    //    Each wave publishes its row maxima, then writes its output rows
+    //    already rescaled to the workgroup maximum (zero-point term included)
+    //    into its own stage; the rows are then summed over the waves in a
+    //    fixed order.
     float lsum = st.l;
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
@@ -774,39 +740,24 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         zs[g] += __shfl_xor(zs[g], 16);
         zs[g] += __shfl_xor(zs[g], 32);
     }
-    if (hi == 0) {
-        sh.mm[wave][lo] = st.m;
-#pragma unroll
-        for (int g = 0; g < NGRP; ++g) sh.zz[wave][lo][g] = zs[g];
-    }
-    __syncthreads();   // maxima and zero-point sums of every wave
+    if (hi == 0) sh.mm[wave][lo] = st.m;
+    __syncthreads();   // maxima of every wave
     {
-        // this lane's output rows are 4hi..4hi+3
+        // this lane's output row is head lo, channels 16 n + 4 hi .. + 3
         const float inv_mult = 1.0f / st.mult;
-        float f[4];
+        float M = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * hi + i;
-            float M = -INFINITY;
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.mm[w][lo]);
+        const float f = st.m == -INFINITY ? 0.f : exp2_fast(st.m - M);
+        if (hi == 0) sh.lw[wave][lo] = f * lsum;
+        float *rows_out = sh.merge_rows(wave) + lo * SplitLds<P>::MRS + 4 * hi;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.mm[w][r]);
-            const float mw = sh.mm[wave][r];
-            f[i] = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
+        for (int n = 0; n < 8; ++n) {
+            const float zg = zs[n >> 1];
+            *reinterpret_cast<float4 *>(rows_out + 16 * n) =
+                make_float4(f * fmaf(st.o[n][0], inv_mult, zg), f * fmaf(st.o[n][1], inv_mult, zg),
+                            f * fmaf(st.o[n][2], inv_mult, zg), f * fmaf(st.o[n][3], inv_mult, zg));
         }
-        if (hi == 0) {
-            float M = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.mm[w][lo]);
-            sh.lw[wave][lo] = st.m == -INFINITY ? 0.f : lsum * exp2_fast(st.m - M);
-        }
-        float *rows_out = sh.merge_rows(wave);
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * hi + i;
-                rows_out[r * HD + 16 * n + lo] = f[i] * fmaf(st.o[n][i], inv_mult, sh.zz[wave][r][n >> 1]);
-            }
     }
     __syncthreads();
 
@@ -815,82 +766,53 @@ __device__ inline void split_item(const kvq_cache &c, const uint16_t *q, const D
         const int rr = idx / HD, d = idx % HD;
         float o = 0.f;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) o += sh.merge_rows(w)[rr * HD + d];
-        const size_t hrow = (size_t)b * c.Hq + (size_t)kh0 * G + rr;
-        ws.o[(hrow * S + split) * HD + d] = o;
+        for (int w = 0; w < WAVES; ++w) o += sh.merge_rows(w)[rr * SplitLds<P>::MRS + d];
+        ws.o[((size_t)seg * 16 + rr) * HD + d] = o;
         if (d == 0) {
             float M = -INFINITY, L = 0.f;
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.mm[w][rr]);
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) L += sh.lw[w][rr];
-            ws.ml[(hrow * S + split) * 2 + 0] = M;
-            ws.ml[(hrow * S + split) * 2 + 1] = L;
+            ws.ml[((size_t)seg * 16 + rr) * 2 + 0] = M;
+            ws.ml[((size_t)seg * 16 + rr) * 2 + 1] = L;
         }
     }
+    // the merge rows live in the stages: every wave has read them before the
+    // next segment's loads land there
+    __syncthreads();
 }
 
-// Work items are (sequence, kv-head pack, run of at most ew table entries),
-// ordered by sequence, run, pack, for the runs that hold entries.  The kernel is
-// persistent: gridDim.x workgroups (what fits on the GPU at once) take the
-// items round-robin, so the dispatcher never has to refill slots and no
-// workgroup is launched for a run past a sequence's end.  The item prefix
-// (B + 1 ints) lives in dynamic LDS.
-// The run length ew is E, unless E-entry runs give fewer items than there
-// are workgroups: then it is the shortest length whose items still fit in
-// the grid, so that a small batch is spread over every workgroup in one
-// round.  (Shortening runs to fill a partly idle last round of a larger
-// batch was measured slower than E-entry runs.)
+// The work is the flat list of (sequence b, kv-head pack p, table entry e),
+// in that order: sequence b's entries for pack p sit at
+// pre(b) + p nb(b) + e, where nb(b) is its table length and pre(b) =
+// n_packs * (table entries of the sequences before it).  Workgroup j of the
+// NW in the grid (what fits on the GPU at once) takes the contiguous range
+// [N j / NW, N (j + 1) / NW) of the N entries: every workgroup streams the
+// same number of block-packs, with no scheduling traffic.  Where its range
+// crosses a (sequence, pack) boundary it writes one partial per side; the
+// partial of workgroup j for unit u = b n_packs + p sits in slot j + u
+// (unique, since both j and u grow along the list).
 // NATIVE: the cache holds the native codec (Reasoning and Execution blocks
 // in E4M3 / E2M1; Transition blocks are integer-coded in both codecs).
 template <int G, bool NATIVE>
-__global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split(kvq_cache c, const uint16_t *q, float *mass,
-                                                         DecodeWs ws, float scale2, int S, int span) {
+__global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split(kvq_cache c, const uint16_t *q,
+                                                                                 float *mass, DecodeWs ws, float scale2) {
     constexpr int P = PACK(G);
     const int n_packs = (c.Hkv + P - 1) / P;
     const int tid = threadIdx.x;
     constexpr int NT = WAVES * 64;
-    extern __shared__ int s_first[];
     __shared__ SplitLds<P> lds;
-    __shared__ int s_carry;
-    __shared__ int s_red[WAVES];
+    __shared__ int s_carry, s_loc[2];
 
-    // -- run length (the same in every workgroup; workgroup 0 publishes it
-    //    for the finalize).  s_first holds the table entries until the prefix.
-    for (int bb = tid; bb < c.B; bb += NT) s_first[bb] = table_entries(c, bb);
-    __syncthreads();
-    auto items_for = [&](int ew) {
-        int n = 0;
-        for (int bb = tid; bb < c.B; bb += NT) n += seq_runs(s_first[bb], ew, S);
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d);
-        if ((tid & 63) == 0) s_red[tid >> 6] = n;
-        __syncthreads();
-        int t = 0;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) t += s_red[w];
-        __syncthreads();   // s_red is reused by the next call
-        return t * n_packs;
-    };
-    int ew = E;
-    if (items_for(E) < (int)gridDim.x) {
-        for (int lo_e = 1; lo_e < ew;) {
-            const int mid = (lo_e + ew) >> 1;
-            if (items_for(mid) <= (int)gridDim.x) ew = mid;
-            else lo_e = mid + 1;
-        }
-    }
-    if (blockIdx.x == 0 && tid == 0) *ws.run_len = ew;
-
-    // -- item prefix: s_first[b] = first item of sequence b (items per
-    //    sequence = active runs * packs)
+    // -- pre(b) for every sequence (a scan over table lengths in the stage
+    //    area), the total N, and where this workgroup's range starts
+    int *s_scan = lds.u.scan, *s_pre = lds.u.scan + NT;
     if (tid == 0) s_carry = 0;
     __syncthreads();
-    int *s_scan = lds.u.scan;
     for (int b0 = 0; b0 < c.B; b0 += NT) {
         const int bb = b0 + tid;
-        const int cnt = bb < c.B ? seq_runs(s_first[bb], ew, S) * n_packs : 0;
-        // inclusive scan of cnt over the workgroup (Hillis-Steele in LDS)
+        const int cnt = bb < c.B ? table_entries(c, bb) * n_packs : 0;
         s_scan[tid] = cnt;
         __syncthreads();
         for (int off = 1; off < NT; off <<= 1) {
@@ -899,14 +821,32 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
             s_scan[tid] += v;
             __syncthreads();
         }
-        if (bb < c.B) s_first[bb] = s_carry + s_scan[tid] - cnt;
+        if (bb < c.B) s_pre[bb] = s_carry + s_scan[tid] - cnt;
         __syncthreads();
         if (tid == NT - 1) s_carry += s_scan[NT - 1];
         __syncthreads();
     }
-    if (tid == 0) s_first[c.B] = s_carry;
+    const long N = s_carry;
+    const int NW = gridDim.x, j = blockIdx.x;
+    if (j == 0) {
+        // for the finalize: where each sequence's entries start, and N
+        for (int bb = tid; bb < c.B; bb += NT) ws.pre[bb] = s_pre[bb];
+        if (tid == 0) ws.pre[c.B] = (int)N;
+    }
+    const int f0 = (int)(N * j / NW), f1 = (int)(N * (j + 1) / NW);
+    if (tid == 0) {
+        // the sequence holding entry f0: the last b with pre(b) <= f0
+        int lo_b = 0, hi_b = c.B - 1;
+        while (lo_b < hi_b) {
+            const int mid = (lo_b + hi_b + 1) >> 1;
+            if (s_pre[mid] <= f0) lo_b = mid; else hi_b = mid - 1;
+        }
+        s_loc[0] = lo_b;
+        s_loc[1] = f0 - s_pre[lo_b];
+    }
     __syncthreads();
-    const int n_items = s_first[c.B];
+    int b = __builtin_amdgcn_readfirstlane(s_loc[0]), r = __builtin_amdgcn_readfirstlane(s_loc[1]);
+    __syncthreads();   // s_loc read before the stage area is cleared
 
     // -- stage bytes start finite: zero the shared area once (the scan used it;
     //    later only loaded pairs and merged rows in the code areas land there)
@@ -921,67 +861,95 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
         for (int p = blockIdx.x * NT + tid; p < len; p += gridDim.x * NT) mass[(size_t)bb * c.n_cap + p] = 0.f;
     }
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x)
-        split_item<G, NATIVE>(c, q, ws, scale2, S, span, ew, item, s_first, lds);
+    // -- the range's segments
+    for (int f = f0; f < f1 && b < c.B;) {
+        const int nb = table_entries(c, b);
+        if (nb == 0) {   // an empty sequence holds no entries of the list
+            ++b;
+            continue;
+        }
+        const int pack = r / nb, e = r % nb;
+        const int cnt = min(nb - e, f1 - f);
+        split_segment<G, NATIVE>(c, q, ws, scale2, b, pack, e, e + cnt, j + b * n_packs + pack, lds);
+        f += cnt;
+        r += cnt;
+        if (r == nb * n_packs) {
+            r = 0;
+            ++b;
+        }
+    }
 }
 
-// Finalize: gridDim.x workgroups per sequence, FPART of them per run:
-// workgroup x takes runs x / FPART + k gridDim.x / FPART, and writes the
-// output rows of heads x, x + gridDim.x, ...  A run's valid slots were stored compacted, in groups of
-// 16; the run's workgroups and their waves take whole groups in turn:
-// a group's scores (one 1 KB block [head][16 slots] per kv-head pack) are
-// read with 1 KB loads, each lane summing exp2(s - M_h) / L_h over its head
-// of every pack for 4 slots, and a fixed 16-lane butterfly totals the heads
-// of each slot.
+// Sum of x over the 16 lanes of this lane's row, in lane 15 of the row
+// (other lanes hold partial sums): four DPP row shifts, in a fixed order.
+__device__ inline float row_sum16(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
+    return x;
+}
+
+// Start of workgroup j's range of the flat entry list, and the workgroup
+// whose range holds entry f: the last j with start(j) <= f (a workgroup
+// with an empty range is never the answer).
+__device__ inline int range_start(long N, int NW, int j) { return (int)(N * j / NW); }
+__device__ inline int range_owner(long N, int NW, int f) {
+    int j = (int)(((long)f * NW) / N);
+    while (j + 1 < NW && range_start(N, NW, j + 1) <= f) ++j;
+    return j;
+}
+
+// Finalize: grid (X, B); workgroup x of row b
+//  - merges, per head of sequence b, the partials of its unit's segments
+//    (the workgroups whose ranges met the unit, in order) into M_h, 1 / L_h;
+//  - takes b's table entries FB per wave, workgroups and waves in turn: lanes
+//    4t .. 4t + 3 load slot t's row of every pack's tile (16 B each, four
+//    heads), sum exp2(s - M_h) / L_h over their heads, and a fixed two-step
+//    butterfly totals the slot; mass and importance are written at the slot's
+//    position;
+//  - writes the output rows of heads x, x + X, ...
 constexpr int FT = 256;
-constexpr int FB = 4;                         // groups a wave takes per round
-constexpr int FPK = 2;                        // kv-head packs whose scores are loaded together (4: slower)
-#ifndef KVQ_FPART
-#define KVQ_FPART 2
-#endif
-constexpr int FPART = KVQ_FPART;              // workgroups sharing one run's groups
-constexpr int FIN_RUNS = 32;
+constexpr int FB = 4;   // entries a wave takes per round
 
 __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
-                                                    float decay, DecodeWs ws, int S, int span, int G, int P,
-                                                    int n_packs) {
-    const int x = blockIdx.x, b = blockIdx.y, X = gridDim.x, XS = X / FPART;
-    const int part = x % FPART;
+                                                    float decay, DecodeWs ws, int NW, int G, int P, int n_packs) {
+    const int x = blockIdx.x, b = blockIdx.y, X = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lo = lane & 15, hi = lane >> 4;
     const int nb = table_entries(c, b);
-    const int ew = *ws.run_len;
-    const int s_act = seq_runs(nb, ew, S);
-    const int Hq = c.Hq;
-    const int split0 = x < XS * FPART ? x / FPART : s_act;   // first run of this workgroup
-    if (split0 >= s_act && x >= Hq) return;   // no slots and no output head
+    const int Hq = c.Hq, PG = P * G;
     __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
     __shared__ float4 red[FT];
+    const long pre = nb > 0 ? ws.pre[b] : 0, N = ws.pre[c.B];
 
     // -- global max / sum per head: tpg lanes of one wave per head, each over
-    //    a stride of splits with its loads issued together, then a butterfly
+    //    a stride of its unit's segments, then a butterfly
     int tpg = 64;
     while (tpg > 1 && tpg * Hq > FT) tpg >>= 1;
     for (int h0 = 0; h0 < Hq; h0 += FT / tpg) {
         const int h = h0 + tid / tpg, jj = tid % tpg;
         float M = -INFINITY, L = 0.f;
-        if (h < Hq) {
-            const float2 *ml = reinterpret_cast<const float2 *>(ws.ml + ((size_t)b * Hq + h) * S * 2);
-            for (int s0 = jj; s0 < s_act; s0 += 8 * tpg) {
-                float2 v[8];
+        if (h < Hq && nb > 0) {
+            const int p = h / PG, hh = h % PG, u = b * n_packs + p;
+            const long U0 = pre + (long)p * nb;
+            const int j0 = range_owner(N, NW, (int)U0), j1 = range_owner(N, NW, (int)(U0 + nb - 1));
+            for (int jb = j0 + jj; jb <= j1; jb += 4 * tpg) {
+                float2 v[4];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int s = s0 + u * tpg;
-                    v[u] = s < s_act ? ml[s] : make_float2(-INFINITY, 0.f);
+                for (int q = 0; q < 4; ++q) {
+                    const int jx = jb + q * tpg;
+                    const bool live = jx <= j1 && range_start(N, NW, jx) < range_start(N, NW, jx + 1);
+                    v[q] = live ? reinterpret_cast<const float2 *>(ws.ml)[((size_t)jx + u) * 16 + hh]
+                                : make_float2(-INFINITY, 0.f);
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    if (v[u].x == -INFINITY) continue;
-                    if (v[u].x > M) {
-                        L = L * exp2f(M - v[u].x) + v[u].y;
-                        M = v[u].x;
+                for (int q = 0; q < 4; ++q) {
+                    if (v[q].x == -INFINITY) continue;
+                    if (v[q].x > M) {
+                        L = L * exp2f(M - v[q].x) + v[q].y;
+                        M = v[q].x;
                     } else {
-                        L += v[u].y * exp2f(v[u].x - M);
+                        L += v[q].y * exp2f(v[q].x - M);
                     }
                 }
             }
@@ -999,121 +967,105 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
     }
     __syncthreads();
 
-    // -- mass (and importance) of the valid slots of this run, 16 at a time
-    //    (a group k: lane (head lo, hi) takes slots 16 k + 4 hi .. + 3)
-    auto run_mass = [&](int split) {
-        const int n_slots = ws.ents[(size_t)b * S + split];
-        const int n_ent = (n_slots + 15) >> 4;
-        const int rst = run_stride(nb, s_act, ew);
-        const size_t off = (size_t)b * span + (size_t)split * rst;
-        for (int k0 = (part * (FT / 64) + wave) * FB; k0 < n_ent; k0 += FPART * (FT / 64) * FB) {
-            int4 pos[FB];
-            float acc[FB][4];
+    // -- mass (and importance) of the valid slots of b's entries
+    {
+        const int t = lane >> 2, hq = lane & 3;
+        const float *const score_b = ws.score + (size_t)b * n_packs * c.max_blocks * 256;
+        for (int e0 = (x * (FT / 64) + wave) * FB; e0 < nb; e0 += X * (FT / 64) * FB) {
+            bool valid[FB];
+            int pos[FB];
 #pragma unroll
-            for (int e = 0; e < FB; ++e) {
-                const int k = k0 + e;
-                pos[e] = k < n_ent ? reinterpret_cast<const int4 *>(ws.spos + (off + k) * 16)[hi]
-                                   : make_int4(-1, -1, -1, -1);
-                // slots past the run's last are stale
-                const int c0 = 16 * k + 4 * hi;
-                if (c0 + 0 >= n_slots) pos[e].x = -1;
-                if (c0 + 1 >= n_slots) pos[e].y = -1;
-                if (c0 + 2 >= n_slots) pos[e].z = -1;
-                if (c0 + 3 >= n_slots) pos[e].w = -1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
-            }
-            // the importance of these positions, loaded before the scores so that
-            // its latency overlaps theirs (lanes lo == 0 write the slots)
-            float imp_old[FB][4];
-            if (importance && lo == 0) {
-#pragma unroll
-                for (int e = 0; e < FB; ++e) {
-                    const int pp[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        imp_old[e][i] = pp[i] >= 0 && pp[i] < c.n_cap ? importance[(size_t)b * c.n_cap + pp[i]] : 0.f;
+            for (int q = 0; q < FB; ++q) {
+                valid[q] = false;
+                pos[q] = -1;
+                if (e0 + q < nb) {
+                    const uint32_t ent = c.table[(size_t)b * c.max_blocks + e0 + q];
+                    const int pool = (int)(ent >> 30);
+                    const uint32_t id = ent & 0x3fffffffu;
+                    valid[q] = (c.mask[pool][id] >> t) & 1u;
+                    pos[q] = c.pos[pool][(size_t)id * BLK + t];
                 }
+                // a position outside the row stride (a corrupt cache) is skipped
+                if (pos[q] < 0 || pos[q] >= c.n_cap) valid[q] = false;
             }
-            for (int p0 = 0; p0 < n_packs; p0 += FPK) {
-                // FPK packs' scores of the round's groups, loads issued together
-                float4 t[FB][FPK];
+            // the importance of these positions, loaded with the scores so
+            // that its latency overlaps theirs
+            float imp_old[FB];
+            if (importance && hq == 0) {
 #pragma unroll
-                for (int e = 0; e < FB; ++e)
+                for (int q = 0; q < FB; ++q) imp_old[q] = valid[q] ? importance[(size_t)b * c.n_cap + pos[q]] : 0.f;
+            }
+            float acc[FB];
 #pragma unroll
-                    for (int q = 0; q < FPK; ++q) {
-                        const int k = k0 + e, p = p0 + q;
-                        t[e][q] = k < n_ent && p < n_packs
-                                      ? reinterpret_cast<const float4 *>(ws.score + (off * n_packs + (size_t)p * rst + k) * 256)[lo * 4 + hi]
-                                      : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                    }
+            for (int q = 0; q < FB; ++q) acc[q] = 0.f;
+            for (int p = 0; p < n_packs; ++p) {
+                float4 sv[FB];
 #pragma unroll
-                for (int q = 0; q < FPK; ++q) {
-                    const int p = p0 + q;
-                    const int col = p * P * G + lo;
-                    const bool cv = p < n_packs && lo < min(P, c.Hkv - p * P) * G && Mh[min(col, Hq - 1)] != -INFINITY;
-                    if (!cv) continue;
-                    const float Mx = Mh[col], Rx = Rh[col];
+                for (int q = 0; q < FB; ++q)
+                    sv[q] = valid[q] ? reinterpret_cast<const float4 *>(
+                                           score_b + ((size_t)p * c.max_blocks + e0 + q) * 256)[t * 4 + hq]
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int np = min(P, c.Hkv - p * P);
 #pragma unroll
-                    for (int e = 0; e < FB; ++e) {
-                        acc[e][0] = fmaf(exp2_fast(t[e][q].x - Mx), Rx, acc[e][0]);
-                        acc[e][1] = fmaf(exp2_fast(t[e][q].y - Mx), Rx, acc[e][1]);
-                        acc[e][2] = fmaf(exp2_fast(t[e][q].z - Mx), Rx, acc[e][2]);
-                        acc[e][3] = fmaf(exp2_fast(t[e][q].w - Mx), Rx, acc[e][3]);
+                for (int i = 0; i < 4; ++i) {
+                    const int hh = 4 * hq + i;
+                    if (hh >= np * G) continue;
+                    const int h = p * PG + hh;
+                    const float Mx = Mh[h], Rx = Rh[h];
+                    if (Mx == -INFINITY) continue;
+#pragma unroll
+                    for (int q = 0; q < FB; ++q) {
+                        const float sx = i == 0 ? sv[q].x : i == 1 ? sv[q].y : i == 2 ? sv[q].z : sv[q].w;
+                        if (valid[q]) acc[q] = fmaf(exp2_fast(sx - Mx), Rx, acc[q]);
                     }
                 }
             }
 #pragma unroll
-            for (int e = 0; e < FB; ++e)
+            for (int q = 0; q < FB; ++q) {
+                acc[q] += __shfl_xor(acc[q], 1);
+                acc[q] += __shfl_xor(acc[q], 2);
+            }
+            if (hq == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int w = 1; w < 16; w <<= 1) acc[e][i] += __shfl_xor(acc[e][i], w);
-            if (lo == 0) {
-#pragma unroll
-                for (int e = 0; e < FB; ++e) {
-                    const int pp[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        // a position outside the row stride (a corrupt cache) is skipped
-                        if (pp[i] < 0 || pp[i] >= c.n_cap) continue;
-                        mass[(size_t)b * c.n_cap + pp[i]] = acc[e][i];
-                        if (importance) importance[(size_t)b * c.n_cap + pp[i]] = fmaf(decay, imp_old[e][i], acc[e][i]);
-                    }
+                for (int q = 0; q < FB; ++q) {
+                    if (!valid[q]) continue;
+                    mass[(size_t)b * c.n_cap + pos[q]] = acc[q];
+                    if (importance) importance[(size_t)b * c.n_cap + pos[q]] = fmaf(decay, imp_old[q], acc[q]);
                 }
             }
         }
-    };
-    // (the first run straight, further ones in a loop: a loop around the
-    // only run of the usual case was measured slower)
-    if (split0 < s_act) run_mass(split0);
-    for (int split = split0 + XS; split < s_act; split += XS) run_mass(split);
+    }
 
     // -- output rows of the heads this workgroup owns: 32 channel quads x
-    //    8 split groups, merged in a fixed order
+    //    8 segment groups, merged in a fixed order
     for (int h = x; h < Hq; h += X) {
         const int c4 = tid & 31, sg = tid >> 5;
-        const float *ml = ws.ml + ((size_t)b * Hq + h) * S * 2;
-        const float4 *o = reinterpret_cast<const float4 *>(ws.o + ((size_t)b * Hq + h) * S * HD);
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         const float Mx = Mh[h];
-        for (int s0 = sg; s0 < s_act; s0 += 4 * 8) {
-            float mv[4];
-            float4 ov[4];
+        if (nb > 0 && Mx != -INFINITY) {
+            const int p = h / PG, hh = h % PG, u = b * n_packs + p;
+            const long U0 = pre + (long)p * nb;
+            const int j0 = range_owner(N, NW, (int)U0), j1 = range_owner(N, NW, (int)(U0 + nb - 1));
+            for (int jb = j0 + sg; jb <= j1; jb += 4 * 8) {
+                float mv[4];
+                float4 ov[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int s = s0 + 8 * u;
-                mv[u] = s < s_act ? ml[2 * s] : -INFINITY;
-                ov[u] = s < s_act ? o[(size_t)s * (HD / 4) + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+                for (int q = 0; q < 4; ++q) {
+                    const int jx = jb + 8 * q;
+                    const bool live = jx <= j1 && range_start(N, NW, jx) < range_start(N, NW, jx + 1);
+                    const size_t row = ((size_t)jx + u) * 16 + hh;
+                    mv[q] = live ? ws.ml[row * 2] : -INFINITY;
+                    ov[q] = live ? reinterpret_cast<const float4 *>(ws.o + row * HD)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (mv[u] == -INFINITY) continue;
-                const float f = exp2f(mv[u] - Mx);
-                acc.x = fmaf(ov[u].x, f, acc.x);
-                acc.y = fmaf(ov[u].y, f, acc.y);
-                acc.z = fmaf(ov[u].z, f, acc.z);
-                acc.w = fmaf(ov[u].w, f, acc.w);
+                for (int q = 0; q < 4; ++q) {
+                    if (mv[q] == -INFINITY) continue;
+                    const float f = exp2f(mv[q] - Mx);
+                    acc.x = fmaf(ov[q].x, f, acc.x);
+                    acc.y = fmaf(ov[q].y, f, acc.y);
+                    acc.z = fmaf(ov[q].z, f, acc.z);
+                    acc.w = fmaf(ov[q].w, f, acc.w);
+                }
             }
         }
         red[tid] = acc;
@@ -1121,9 +1073,9 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
         if (tid < 32) {
             float4 sum = red[tid];
 #pragma unroll
-            for (int k = 1; k < 8; ++k) {
-                const float4 r = red[k * 32 + tid];
-                sum.x += r.x; sum.y += r.y; sum.z += r.z; sum.w += r.w;
+            for (int q = 1; q < 8; ++q) {
+                const float4 rr = red[q * 32 + tid];
+                sum.x += rr.x; sum.y += rr.y; sum.z += rr.z; sum.w += rr.w;
             }
             const float R = Rh[h];
             reinterpret_cast<float4 *>(out + ((size_t)b * Hq + h) * HD)[tid] =
@@ -1157,17 +1109,16 @@ int persistent_grid(int G, bool native, const void *kernel, size_t dyn_lds) {
 bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, float *importance,
                    float decay, float sm_scale, void *ws_ptr, hipStream_t s) {
     DecodeWs ws(ws_ptr, c);
-    const int S = n_splits(c), span = score_span(c);
     const int G = c.Hq / c.Hkv;
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     const float scale2 = sm_scale * LOG2E;
-    const size_t dyn = sizeof(int) * ((size_t)c.B + 1);   // item prefix of the split kernel
+    int NW = 0;
     switch (G) {
 #define KVQ_GN(g, nat)                                                                                   \
     {                                                                                                    \
-        const int grid = persistent_grid(g, nat, reinterpret_cast<const void *>(attn_split<g, nat>), dyn); \
-        if (grid <= 0) return false;                                                                     \
-        hipLaunchKernelGGL((attn_split<g, nat>), dim3(grid), dim3(WAVES * 64), dyn, s, c, qq, mass, ws, scale2, S, span); \
+        NW = std::min(persistent_grid(g, nat, reinterpret_cast<const void *>(attn_split<g, nat>), 0), MAX_SPLIT_WGS); \
+        if (NW <= 0) return false;                                                                       \
+        hipLaunchKernelGGL((attn_split<g, nat>), dim3(NW), dim3(WAVES * 64), 0, s, c, qq, mass, ws, scale2); \
     }
 #define KVQ_G(g)                                                    \
     case g:                                                         \
@@ -1180,14 +1131,14 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
         default: return false;
     }
     {
-        const int P = decode_pack(G);
-        // FIN_RUNS runs per sequence at a time (more are taken in turn), and
-        // a workgroup per output head.  An odd run count per row keeps the
-        // rows' busy workgroups from landing on the same compute units (with
-        // 64 or 128 workgroups per row the finalize was measured 27% slower).
-        const int X = FPART * (std::max(std::min(S, FIN_RUNS), (c.Hq + FPART - 1) / FPART) | 1);
-        hipLaunchKernelGGL(attn_finalize, dim3(X, c.B), dim3(FT), 0, s, c, out, mass, importance, decay, ws, S, span, G, P,
-                           decode_n_packs(c));
+        // enough workgroups per sequence that a full table takes two rounds
+        // of FB entries per wave, and at least one per output head (up to
+        // 64); an odd row keeps the rows' busy workgroups off the same
+        // compute units
+        const int per_round = FB * (FT / 64);
+        const int X = std::max((c.max_blocks + 2 * per_round - 1) / (2 * per_round), std::min(c.Hq, 64)) | 1;
+        hipLaunchKernelGGL(attn_finalize, dim3(X, c.B), dim3(FT), 0, s, c, out, mass, importance, decay, ws, NW, G,
+                           decode_pack(G), decode_n_packs(c));
     }
     return hipGetLastError() == hipSuccess;
 }

@@ -7,27 +7,6 @@
 
 namespace kvq {
 
-// Decode split-K: a run (split) covers at most this many table entries of
-// one sequence and kv-head pack (a sequence with nr runs gives run j the
-// entries j, j + nr, j + 2 nr, ...).  The decode shortens the runs when the
-// batch leaves workgroups idle, down to MIN_RUN entries for a sequence that
-// fills its table, so a sequence has at most n_splits runs.
-#ifndef KVQ_ENTRIES_PER_SPLIT
-#define KVQ_ENTRIES_PER_SPLIT 64
-#endif
-constexpr int ENTRIES_PER_SPLIT = KVQ_ENTRIES_PER_SPLIT;
-constexpr int MIN_RUN = 16;
-
-inline int n_splits(const kvq_cache &c) { return (c.max_blocks + MIN_RUN - 1) / MIN_RUN; }
-
-// Score groups (of 16 slots) reserved per sequence and kv-head pack: runs
-// of E entries each take E groups at E-group offsets, like any run layout
-// up to max_blocks + n_splits groups (see run_stride); rounded up to E.
-inline int score_span(const kvq_cache &c) {
-    const int e64 = (c.max_blocks + ENTRIES_PER_SPLIT - 1) / ENTRIES_PER_SPLIT * ENTRIES_PER_SPLIT;
-    return (e64 + n_splits(c) + ENTRIES_PER_SPLIT - 1) / ENTRIES_PER_SPLIT * ENTRIES_PER_SPLIT;
-}
-
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace carve-up.  Calls are stream-ordered, so they share one buffer.
@@ -60,32 +39,32 @@ inline int decode_n_packs(const kvq_cache &c) {
     return (c.Hkv + P - 1) / P;
 }
 
+// The decode split kernel's grid holds at most this many workgroups.  Each
+// takes a contiguous range of the flat (sequence, kv-head pack, table entry)
+// list and writes one partial per (sequence, pack) unit its range touches,
+// in slot (workgroup + unit): fewer than MAX_SPLIT_WGS + B * n_packs slots.
+constexpr int MAX_SPLIT_WGS = 2048;
+
 struct DecodeWs {
-    float *ml;         // [B][Hq][S][2]  split max (base-2 units), split sum
-    float *o;          // [B][Hq][S][128] split output, unnormalised
-    // The valid slots of a run, in table and slot order, are numbered
-    // 0 .. n-1 (n <= 16 x its entries); their scores and positions are
-    // stored compacted in groups of 16, run j of a sequence from group
-    // j * st (st: the run stride, at least the entries of any of its runs).
-    int32_t *ents;     // [B][S] valid slots n of the run
-    int32_t *run_len;  // [1] most entries per run, chosen by the split kernel
-    int32_t *spos;     // [B][span][16] position of valid slot c at [j st + c / 16][c % 16]
-    float *score;      // [B][span][n_packs][16 heads][16]: the base-2 scaled score
-                       // of valid slot c of pack p at group (j st) n_packs + p st +
-                       // c / 16, [head][c % 16] (a run's packs adjacent)
+    float *ml;         // [slots][16 heads][2] segment max (base-2 units) and sum
+    float *o;          // [slots][16 heads][128] segment output, unnormalised
+    float *score;      // [B][n_packs][max_blocks][16 slots][16 heads]: the base-2
+                       // scaled scores of table entry e (-inf at cleared slots),
+                       // written by the split kernel, read by the finalize
+    int32_t *pre;      // [B + 1] where each sequence's entries start in the split
+                       // kernel's flat list (n_packs x the entries before it); [B]: N
+    static size_t slots(const kvq_cache &c) { return MAX_SPLIT_WGS + (size_t)c.B * decode_n_packs(c); }
     static size_t bytes(const kvq_cache &c) {
-        const size_t S = n_splits(c), SP = score_span(c);
-        return align256(8L * c.B * c.Hq * S) + align256(512L * c.B * c.Hq * S) + align256(4L * c.B * S) +
-               align256(4) + align256(64L * c.B * SP) + align256(1024L * c.B * SP * decode_n_packs(c));
+        const size_t S = slots(c);
+        return align256(4L * (c.B + 1)) + align256(128L * S) + align256(8192L * S) +
+               align256(1024L * c.B * c.max_blocks * decode_n_packs(c));
     }
     DecodeWs(void *ws, const kvq_cache &c) {
-        const size_t S = n_splits(c), SP = score_span(c);
+        const size_t S = slots(c);
         char *p = (char *)ws;
-        ml = (float *)p;      p += align256(8L * c.B * c.Hq * S);
-        o = (float *)p;       p += align256(512L * c.B * c.Hq * S);
-        ents = (int32_t *)p;  p += align256(4L * c.B * S);
-        run_len = (int32_t *)p; p += align256(4);
-        spos = (int32_t *)p;  p += align256(64L * c.B * SP);
+        pre = (int32_t *)p;   p += align256(4L * (c.B + 1));
+        ml = (float *)p;      p += align256(128L * S);
+        o = (float *)p;       p += align256(8192L * S);
         score = (float *)p;
     }
 };
