@@ -26,7 +26,7 @@ namespace kvq {
 
 namespace {
 
-constexpr int E = 64;   // table entries a segment walks at a time
+constexpr int E = 256;  // table entries a segment walks at a time (64 per wave)
 constexpr int MAX_HQ = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -577,9 +577,9 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
 template <int P>
 struct SplitLds {
     uint32_t ent[E];         // non-empty table entries of the chunk, in order
-    uint32_t msk[E];         // their masks
     int eix[E];              // their table indices
-    int n;
+    uint16_t msk[E];         // their masks
+    int wcnt[WAVES];         // non-empty entries each wave found
     uint4 qb[NGRP][65];      // [g][lane]: q of column head lane % 16, channel
                              // slice lane / 16 of group g; [g][64] is zero
     // wave merge: row maxima and scaled row sums per wave
@@ -604,8 +604,9 @@ struct SplitLds {
 // `pack`, taken E entries at a time; writes its partial (max, sum, output)
 // for the pack's heads to segment slot `seg`.
 template <int G, bool NATIVE>
-__device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, const DecodeWs &ws, float scale2,
-                                     int b, int pack, int e_begin, int e_end, int seg, SplitLds<PACK(G)> &sh) {
+__device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, float *mass, const DecodeWs &ws,
+                                     float scale2, int b, int nb, int pack, int e_begin, int e_end, int seg,
+                                     SplitLds<PACK(G)> &sh) {
     constexpr int P = PACK(G);
     const int n_packs = (c.Hkv + P - 1) / P;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -654,33 +655,34 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, cons
     uint8_t *stg = sh.u.stage + wv * stage_bytes(P);
     float *const score_u = ws.score + ((size_t)b * n_packs + pack) * c.max_blocks * 256;
     for (int base = e_begin; base < e_end; base += E) {
-        // -- the chunk's non-empty table entries, compacted in table order (wave 0)
-        if (wave == 0) {
+        // -- the chunk's non-empty table entries, compacted in table order:
+        //    wave w walks entries [64 w, 64 w + 64) of the chunk and places its
+        //    non-empty ones after those of the waves before it
+        {
             const int cnt = min(E, e_end - base);
-            int n = 0;
-            for (int k0 = 0; k0 < cnt; k0 += 64) {
-                const int k = k0 + lane;
-                uint32_t ent = 0, m = 0;
-                if (k < cnt) {
-                    ent = c.table[(size_t)b * c.max_blocks + base + k];
-                    m = c.mask[ent >> 30][ent & 0x3fffffffu];
-                }
-                const uint64_t bal = __ballot(m != 0);
-                const int at = n + __popcll(bal & ((1ull << lane) - 1));
-                if (m != 0) {
-                    sh.ent[at] = ent;
-                    sh.msk[at] = m;
-                    sh.eix[at] = base + k;
-                }
-                n += __popcll(bal);
+            const int k = 64 * wave + lane;
+            uint32_t ent = 0, m = 0;
+            if (k < cnt) {
+                ent = c.table[(size_t)b * c.max_blocks + base + k];
+                m = c.mask[ent >> 30][ent & 0x3fffffffu];
             }
-            if (lane == 0) sh.n = n;
+            const uint64_t bal = __ballot(m != 0);
+            if (lane == 0) sh.wcnt[wave] = __popcll(bal);
+            __syncthreads();
+            int at = __popcll(bal & ((1ull << lane) - 1));
+            for (int w = 0; w < wave; ++w) at += sh.wcnt[w];
+            if (m != 0) {
+                sh.ent[at] = ent;
+                sh.msk[at] = (uint16_t)m;
+                sh.eix[at] = base + k;
+            }
         }
+        int n_ent = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) n_ent += sh.wcnt[w];
+        n_ent = __builtin_amdgcn_readfirstlane(n_ent);
         __syncthreads();
 
-        // -- this wave's entries k = wave, wave + WAVES, ...: the loads of entry
-        //    k + WAVES run while entry k is computed
-        const int n_ent = __builtin_amdgcn_readfirstlane(sh.n);
         auto issue = [&](int k, int part) {
             // block metadata is wave-uniform: keep it in scalar registers
             const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
@@ -782,6 +784,14 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, cons
             ws.ml[((size_t)seg * 16 + rr) * 2 + 1] = L;
         }
     }
+    // -- pack 0's segments partition the sequence's table, so their shares of
+    //    the positions below seq_len partition those: each starts its share
+    //    at mass 0 (the finalize then writes the valid positions)
+    if (pack == 0) {
+        const int len = min(c.seq_len[b], c.n_cap);
+        const int p0 = (int)((long)len * e_begin / nb), p1 = (int)((long)len * e_end / nb);
+        for (int p = p0 + tid; p < p1; p += WAVES * 64) mass[(size_t)b * c.n_cap + p] = 0.f;
+    }
     // the merge rows live in the stages: every wave has read them before the
     // next segment's loads land there
     __syncthreads();
@@ -815,19 +825,23 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     if (tid == 0) s_carry = 0;
     __syncthreads();
     for (int b0 = 0; b0 < c.B; b0 += NT) {
-        const int bb = b0 + tid;
+        // inclusive scan of the counts: inside each wave by shuffles, then
+        // the wave totals in LDS
+        const int bb = b0 + tid, lane = tid & 63, wave = tid >> 6;
         const int cnt = bb < c.B ? table_entries(c, bb) * n_packs : 0;
-        s_scan[tid] = cnt;
-        __syncthreads();
-        for (int off = 1; off < NT; off <<= 1) {
-            const int v = tid >= off ? s_scan[tid - off] : 0;
-            __syncthreads();
-            s_scan[tid] += v;
-            __syncthreads();
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
         }
-        if (bb < c.B) s_pre[bb] = s_carry + s_scan[tid] - cnt;
+        if (lane == 63) s_scan[wave] = incl;
         __syncthreads();
-        if (tid == NT - 1) s_carry += s_scan[NT - 1];
+        int before = s_carry;
+        for (int w = 0; w < wave; ++w) before += s_scan[w];
+        if (bb < c.B) s_pre[bb] = before + incl - cnt;
+        __syncthreads();
+        if (tid == NT - 1) s_carry = before + incl;
         __syncthreads();
     }
     const long N = s_carry;
@@ -858,12 +872,6 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
         reinterpret_cast<uint4 *>(&lds.u)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
-    // -- every position below seq_len starts at mass 0; the finalize pass
-    //    writes the valid ones.  Grid-stride over (sequence, position).
-    for (int bb = 0; bb < c.B; ++bb) {
-        const int len = min(c.seq_len[bb], c.n_cap);
-        for (int p = blockIdx.x * NT + tid; p < len; p += gridDim.x * NT) mass[(size_t)bb * c.n_cap + p] = 0.f;
-    }
 
     // -- the range's segments
     for (int f = f0; f < f1 && b < c.B;) {
@@ -874,7 +882,7 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
         }
         const int pack = r / nb, e = r % nb;
         const int cnt = min(nb - e, f1 - f);
-        split_segment<G, NATIVE>(c, q, ws, scale2, b, pack, e, e + cnt, j + b * n_packs + pack, lds);
+        split_segment<G, NATIVE>(c, q, mass, ws, scale2, b, nb, pack, e, e + cnt, j + b * n_packs + pack, lds);
         f += cnt;
         r += cnt;
         if (r == nb * n_packs) {
@@ -925,6 +933,12 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
     __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
     __shared__ float4 red[FT];
     const long pre = nb > 0 ? ws.pre[b] : 0, N = ws.pre[c.B];
+    if (nb == 0) {
+        // no table entries, so no split segment zeroed this sequence's
+        // positions: every one below seq_len has mass 0
+        const int len = min(c.seq_len[b], c.n_cap);
+        for (int p = x * FT + tid; p < len; p += X * FT) mass[(size_t)b * c.n_cap + p] = 0.f;
+    }
 
     // -- global max / sum per head: tpg lanes of one wave per head, each over
     //    a stride of its unit's segments, then a butterfly
