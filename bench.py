@@ -46,6 +46,9 @@ TBE_PARAMS = (64, 4, 8)
 # the importance as the window score, pivotal above 8x the mean, runs
 # shorter than 16 candidates merged ("TAM", section 2)
 TAM_PARAMS = (8.0, 16)
+# the continuous-thinking loop's TAM pruning: the same, on the mass of the
+# last 64 queries before each prune (the selection window, "TAM", 2.B)
+CT_TAM_PARAMS = TAM_PARAMS + (64,)
 # the arithmetic of the path: codes widened to exact fp16 MFMA operands
 # against fp16 q / P', accumulated in fp32; softmax, mass and the merge in fp32
 DTYPE = "fp16-mfma/fp32-acc"
@@ -360,22 +363,24 @@ def ct_bench(args, w):
     steps = [wl.loop_step_tokens(w, s, tags_all) for s in range(w.loop_steps)]
     K = torch.from_numpy(np.stack([x[0] for x in steps])).cuda()
     V = torch.from_numpy(np.stack([x[1] for x in steps])).cuda()
-    T = torch.from_numpy(np.stack([x[2] for x in steps])).cuda()
+    tags_host = np.stack([x[2] for x in steps])
+    T = torch.from_numpy(tags_host).cuda()
     Q = torch.from_numpy(np.stack([wl.queries(w, s) for s in range(64)])).cuda()
     del steps
     B = w.B
     out = torch.empty((B, w.Hq, 128), device="cuda")
     mass = torch.empty((B, g.n_cap), device="cuda")
     st0 = cache.state_numpy()
+    last_tags = tags_all[np.arange(w.B), n0 - 1]
     ct = ContinuousThinking(cache, w.keep, w.period, w.q_window, w.recent_window, w.decay,
-                            policy=args.policy, tbe=TBE_PARAMS, tam=TAM_PARAMS)
+                            policy=args.policy, tbe=TBE_PARAMS, tam=CT_TAM_PARAMS, last_tags=last_tags)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(w.loop_steps)]
     pruned = np.zeros(w.loop_steps, dtype=bool)
     torch.cuda.synchronize()
     for s in range(w.loop_steps):
         ev[s][0].record()
-        pruned[s] = ct.step(K[s], V[s], T[s], Q[s % 64], out, mass)
+        pruned[s] = ct.step(K[s], V[s], T[s], Q[s % 64], out, mass, tags_host=tags_host[s])
         ev[s][1].record()
     torch.cuda.synchronize()
     if cache.status != 0:
@@ -410,10 +415,13 @@ def ct_bench(args, w):
         "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} D=128, {n0} cached tokens/seq, "
-                               f"{w.loop_steps} generated; budget {w.keep} + windows "
-                               f"{w.q_window}/{w.recent_window}, pruned every {w.period} tokens "
-                               f"({args.policy}); "
-                               f"step = append + decode (+ evict every {w.period})",
+                               f"{w.loop_steps} generated; windows {w.q_window}/{w.recent_window}; "
+                               + (f"pruned by segment where a Transition starts (tbe {TBE_PARAMS})"
+                                  if args.policy == "tbe" else
+                                  f"pruned to {w.keep} every {w.period} tokens ({args.policy}"
+                                  + (f", window of {CT_TAM_PARAMS[2]} queries" if args.policy == "tam" else "")
+                                  + ")")
+                               + "; step = append + decode (+ evict)",
                    "global_batch": B, "seq_len": n0 + w.loop_steps},
         "roofline": None,
         "ct": {"policy": args.policy,

@@ -25,9 +25,10 @@ kvq_status check_cache(const kvq_cache *c) {
     return KVQ_OK;
 }
 
-kvq_status check_ws(const kvq_cache *c, const void *ws, size_t bytes) {
+// each call checks the workspace against its own need
+kvq_status check_ws(const void *ws, size_t bytes, size_t need) {
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) return KVQ_EINVAL;
-    return bytes >= kvq_workspace_bytes(c) ? KVQ_OK : KVQ_EINVAL;
+    return bytes >= need ? KVQ_OK : KVQ_EINVAL;
 }
 
 }  // namespace
@@ -42,13 +43,18 @@ extern "C" size_t kvq_workspace_bytes(const kvq_cache *c) {
     return std::max({kvq::AppendWs::bytes(*c), kvq::DecodeWs::bytes(*c), kvq::EvictWs::bytes(*c)});
 }
 
+extern "C" size_t kvq_decode_workspace_bytes(const kvq_cache *c) {
+    if (check_cache(c) != KVQ_OK) return 0;
+    return kvq::DecodeWs::bytes(*c);
+}
+
 extern "C" kvq_status kvq_append_quantize(const kvq_cache *c, const void *k_new, const void *v_new,
                                           const uint8_t *tags, void *ws, size_t ws_bytes,
                                           hipStream_t stream) {
     kvq_status st = check_cache(c);
     if (st != KVQ_OK) return st;
     if (!k_new || !v_new || !tags) return KVQ_EINVAL;
-    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, kvq::AppendWs::bytes(*c))) != KVQ_OK) return st;
     return kvq::launch_append(*c, k_new, v_new, tags, ws, stream) ? KVQ_OK : KVQ_EHIP;
 }
 
@@ -71,7 +77,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, fl
     kvq_status st = check_cache(c);
     if (st != KVQ_OK) return st;
     if (!q || !out || !mass) return KVQ_EINVAL;
-    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, kvq::DecodeWs::bytes(*c))) != KVQ_OK) return st;
     return kvq::launch_decode(*c, q, out, mass, importance, decay, sm_scale, ws, stream) ? KVQ_OK
                                                                                          : KVQ_EHIP;
 }
@@ -83,21 +89,22 @@ extern "C" kvq_status kvq_evict_topk(const kvq_cache *c, const float *importance
     kvq_status st = check_cache(c);
     if (st != KVQ_OK) return st;
     if (!importance || !keep_k || q_window < 0 || recent_window < 0) return KVQ_EINVAL;
-    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, kvq::EvictWs::bytes(*c))) != KVQ_OK) return st;
     return kvq::launch_evict(*c, importance, keep_k, q_window, recent_window, ws, stream) ? KVQ_OK
                                                                                            : KVQ_EHIP;
 }
 
-extern "C" kvq_status kvq_evict_tbe(const kvq_cache *c, const float *importance, int32_t r0,
-                                    int32_t r_min, int32_t t_keep, int32_t q_window,
+extern "C" kvq_status kvq_evict_tbe(const kvq_cache *c, const float *importance, const uint8_t *seq_mask,
+                                    int32_t r0, int32_t r_min, int32_t t_keep, int32_t q_window,
                                     int32_t recent_window, void *ws, size_t ws_bytes,
                                     hipStream_t stream) {
     kvq_status st = check_cache(c);
     if (st != KVQ_OK) return st;
     if (!importance || r0 < 0 || r_min < 0 || t_keep < 0 || q_window < 0 || recent_window < 0)
         return KVQ_EINVAL;
-    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
-    return kvq::launch_evict_tbe(*c, importance, r0, r_min, t_keep, q_window, recent_window, ws, stream)
+    if ((st = check_ws(ws, ws_bytes, kvq::EvictWs::bytes(*c))) != KVQ_OK) return st;
+    return kvq::launch_evict_tbe(*c, importance, seq_mask, r0, r_min, t_keep, q_window, recent_window, ws,
+                                  stream)
                ? KVQ_OK
                : KVQ_EHIP;
 }
@@ -110,7 +117,7 @@ extern "C" kvq_status kvq_evict_tam(const kvq_cache *c, const float *score, cons
     if (st != KVQ_OK) return st;
     if (!score || !keep_k || !(pivot_c >= 0.0f) || min_seg < 1 || q_window < 0 || recent_window < 0)
         return KVQ_EINVAL;
-    if ((st = check_ws(c, ws, ws_bytes)) != KVQ_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, kvq::EvictWs::bytes(*c))) != KVQ_OK) return st;
     return kvq::launch_evict_tam(*c, score, keep_k, pivot_c, min_seg, q_window, recent_window, ws, stream)
                ? KVQ_OK
                : KVQ_EHIP;

@@ -666,10 +666,19 @@ __device__ inline SegOrder seg_order(const kvq_cache &c, int b, const float *val
 // segment followed by k Transition segments keeps everything if k == 0,
 // else its best max(r_min, r0 >> (k - 1)) slots (Reasoning, Execution) or
 // t_keep slots (Transition), by importance.
-__global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const float *importance, int r0,
-                                                              int r_min, int t_keep, int q_window,
-                                                              int recent_window, EvictWs ws) {
+// A sequence outside seq_mask gets segn = -1: no segment to drop, and the
+// compaction leaves it as it is.
+__global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const float *importance,
+                                                              const uint8_t *seq_mask, int r0, int r_min,
+                                                              int t_keep, int q_window, int recent_window,
+                                                              EvictWs ws) {
     const int b = blockIdx.x, tid = threadIdx.x;
+    if (seq_mask && seq_mask[b] == 0) {
+        // (the free-stack tops are still taken, by sequence 0's workgroup)
+        if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
+        if (tid == 0) ws.segn[2 * b] = -1;
+        return;
+    }
     __shared__ int wave_tot[SEL_WAVES];
     __shared__ uint64_t wave_u64[SEL_WAVES];
     const SegOrder so = seg_order(c, b, importance, q_window, recent_window, ws, nullptr, wave_tot, wave_u64);
@@ -930,6 +939,10 @@ __global__ __launch_bounds__(DROP_THREADS) void evict_seg_drop(kvq_cache c, Evic
 // row as evict_select does, one workgroup per sequence.
 __global__ __launch_bounds__(SEL_THREADS) void evict_seg_compact(kvq_cache c, EvictWs ws) {
     const int b = blockIdx.x, tid = threadIdx.x;
+    if (ws.segn[2 * b] < 0) {   // a sequence left as it is frees nothing
+        if (tid < 4) ws.nfreed[b * 4 + tid] = 0;
+        return;
+    }
     const int nb = c.n_blocks[b];
     uint32_t *row = c.table + (size_t)b * c.max_blocks;
     uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
@@ -997,11 +1010,11 @@ bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *ke
     return hipGetLastError() == hipSuccess;
 }
 
-bool launch_evict_tbe(const kvq_cache &c, const float *importance, int r0, int r_min, int t_keep,
-                      int q_window, int recent_window, void *ws_ptr, hipStream_t s) {
+bool launch_evict_tbe(const kvq_cache &c, const float *importance, const uint8_t *seq_mask, int r0, int r_min,
+                      int t_keep, int q_window, int recent_window, void *ws_ptr, hipStream_t s) {
     EvictWs ws(ws_ptr, c);
-    hipLaunchKernelGGL(evict_tbe_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, r0, r_min, t_keep,
-                       q_window, recent_window, ws);
+    hipLaunchKernelGGL(evict_tbe_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, seq_mask, r0, r_min,
+                       t_keep, q_window, recent_window, ws);
     hipLaunchKernelGGL(evict_seg_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, ws);
     hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws);
     hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);

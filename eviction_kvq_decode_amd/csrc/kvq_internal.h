@@ -43,7 +43,7 @@ inline int decode_n_packs(const kvq_cache &c) {
 // takes a contiguous range of the flat (sequence, kv-head pack, table entry)
 // list and writes one partial per (sequence, pack) unit its range touches,
 // in slot (workgroup + unit): fewer than MAX_SPLIT_WGS + B * n_packs slots.
-constexpr int MAX_SPLIT_WGS = 2048;
+constexpr int MAX_SPLIT_WGS = 1024;
 
 struct DecodeWs {
     float *ml;         // [slots][16 heads][2] segment max (base-2 units) and sum
@@ -89,7 +89,7 @@ struct EvictWs {
     int32_t *segm;     // [B][max_blocks*16] droppable candidates of each segment (-m-1: capped)
     uint64_t *psum;    // [B][max_blocks*16 + 1] running sum of sfx before each candidate
     int32_t *pcnt;     // [B][max_blocks*16 + 1] droppable candidates before each candidate
-    int32_t *segn;     // [B][2] segments, Transition segments
+    int32_t *segn;     // [B][2] segments (-1: the sequence is left as it is), Transition segments
     static size_t bytes(const kvq_cache &c) {
         const size_t ms = (size_t)c.max_blocks * 16, slot4 = align256(4L * c.B * ms);
         return align256(8L * c.B * ms) + align256(4L * EVICT_KEY_WGS * c.B) + align256(4L * c.B * c.max_blocks) +
@@ -128,8 +128,8 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
                    float decay, float sm_scale, void *ws, hipStream_t s);
 bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *keep_k, int q_window,
                   int recent_window, void *ws, hipStream_t s);
-bool launch_evict_tbe(const kvq_cache &c, const float *importance, int r0, int r_min, int t_keep,
-                      int q_window, int recent_window, void *ws, hipStream_t s);
+bool launch_evict_tbe(const kvq_cache &c, const float *importance, const uint8_t *seq_mask, int r0, int r_min,
+                      int t_keep, int q_window, int recent_window, void *ws, hipStream_t s);
 bool launch_evict_tam(const kvq_cache &c, const float *score, const int32_t *keep_k, float pivot_c,
                       int min_seg, int q_window, int recent_window, void *ws, hipStream_t s);
 

@@ -18,7 +18,7 @@ HD = 128
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EHIP, KVQ_ENOSPC = 0, -1, -2, -3, -4
 TAG_R, TAG_E, TAG_T, TAG_NONE = 0, 1, 2, 255
 
-EXPORTS = ("kvq_region_bytes", "kvq_workspace_bytes", "kvq_append_quantize",
+EXPORTS = ("kvq_region_bytes", "kvq_workspace_bytes", "kvq_decode_workspace_bytes", "kvq_append_quantize",
            "kvq_append_quantize_noalloc", "kvq_decode_attention", "kvq_evict_topk",
            "kvq_evict_tbe", "kvq_evict_tam")
 
@@ -54,6 +54,8 @@ def lib():
         L.kvq_region_bytes.argtypes = [ctypes.c_int]
         L.kvq_workspace_bytes.restype = ctypes.c_size_t
         L.kvq_workspace_bytes.argtypes = [CS]
+        L.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_decode_workspace_bytes.argtypes = [CS]
         L.kvq_append_quantize.restype = ctypes.c_int
         L.kvq_append_quantize.argtypes = [CS, P, P, P, P, ctypes.c_size_t, P]
         L.kvq_append_quantize_noalloc.restype = ctypes.c_int
@@ -64,7 +66,7 @@ def lib():
         L.kvq_evict_topk.restype = ctypes.c_int
         L.kvq_evict_topk.argtypes = [CS, P, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_size_t, P]
         L.kvq_evict_tbe.restype = ctypes.c_int
-        L.kvq_evict_tbe.argtypes = [CS, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        L.kvq_evict_tbe.argtypes = [CS, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, P, ctypes.c_size_t, P]
         L.kvq_evict_tam.restype = ctypes.c_int
         L.kvq_evict_tam.argtypes = [CS, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -153,10 +155,12 @@ class Cache:
                                     int(q_window), int(recent_window), self.ws_ptr, self.ws_bytes,
                                     self._stream(stream)), "kvq_evict_topk")
 
-    def evict_tbe(self, importance, r0, r_min, t_keep, q_window, recent_window, stream=None):
-        """importance fp32 [B][n_cap]; thought-adaptive eviction by segment."""
-        _check(lib().kvq_evict_tbe(ctypes.byref(self.struct), _ptr(importance), int(r0), int(r_min),
-                                   int(t_keep), int(q_window), int(recent_window), self.ws_ptr,
+    def evict_tbe(self, importance, r0, r_min, t_keep, q_window, recent_window, stream=None, seq_mask=None):
+        """importance fp32 [B][n_cap]; thought-adaptive eviction by segment.
+        seq_mask: uint8 [B] device tensor (or None: every sequence); the
+        sequences outside it are left as they are."""
+        _check(lib().kvq_evict_tbe(ctypes.byref(self.struct), _ptr(importance), _ptr(seq_mask), int(r0),
+                                   int(r_min), int(t_keep), int(q_window), int(recent_window), self.ws_ptr,
                                    self.ws_bytes, self._stream(stream)), "kvq_evict_tbe")
 
     def evict_tam(self, score, keep_k, pivot_c, min_seg, q_window, recent_window, stream=None):

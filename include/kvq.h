@@ -125,9 +125,18 @@ typedef struct kvq_cache {
 /* Bytes of one (block, kv head) region of pool p (0, 1, 2): 512*b + 512. */
 size_t kvq_region_bytes(int pool);
 
-/* Workspace bytes that every call below needs for this cache (device
- * memory, 256-byte aligned, contents need not be initialised). */
+/* Workspace bytes that every call below needs for this cache, so that one
+ * buffer serves them all (device memory, 256-byte aligned, contents need not
+ * be initialised; calls ordered on one stream may share it).  0 if the cache
+ * description is rejected. */
 size_t kvq_workspace_bytes(const kvq_cache *cache);
+
+/* Workspace bytes kvq_decode_attention needs for this cache (a buffer this
+ * size serves the decode alone; <= kvq_workspace_bytes).  It holds the split
+ * partials (max, sum, output per head), the base-2 scores of every table
+ * entry's slots for the mass pass, and the sequence prefix of the work list.
+ * 0 if the cache description is rejected. */
+size_t kvq_decode_workspace_bytes(const kvq_cache *cache);
 
 /*
  * Append one token per sequence ("ThinKV", TBQ and Continuous Thinking).
@@ -205,6 +214,10 @@ kvq_status kvq_evict_topk(const kvq_cache *cache, const float *importance, const
  * schedule, and a small safety net of every earlier Transition segment stays.
  *   importance : fp32 [B][n_cap], read at the positions of valid slots
  *                (finite values; -0 counts as +0)
+ *   seq_mask   : uint8 [B] or NULL; a sequence with seq_mask[b] == 0 is left
+ *                exactly as it is (no eviction, no compaction): the caller
+ *                fires the eviction only for the sequences in which a
+ *                Transition thought was detected.  NULL: every sequence.
  *   r0, r_min, t_keep : >= 0
  * Per sequence, the valid slots with q_window <= pos < seq_len -
  * recent_window are the candidates; the others are kept.  In position order
@@ -214,10 +227,11 @@ kvq_status kvq_evict_topk(const kvq_cache *cache, const float *importance, const
  * Execution segment (r0, r0 / 2, r0 / 4, ... as Transitions follow) and
  * t_keep slots if it is a Transition segment.  A segment keeps its slots of
  * largest importance (ties: lower position).  The rest are evicted, and the
- * table is compacted and emptied blocks are freed as in kvq_evict_topk.
+ * table is compacted and emptied blocks are freed as in kvq_evict_topk (pushes
+ * ranked over the sequences in the mask, in batch order).
  */
-kvq_status kvq_evict_tbe(const kvq_cache *cache, const float *importance, int32_t r0,
-                         int32_t r_min, int32_t t_keep, int32_t q_window,
+kvq_status kvq_evict_tbe(const kvq_cache *cache, const float *importance, const uint8_t *seq_mask,
+                         int32_t r0, int32_t r_min, int32_t t_keep, int32_t q_window,
                          int32_t recent_window, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 

@@ -730,12 +730,18 @@ static int pos_cmp(const void *a, const void *b)
  * (r0 after the first later Transition, r0 / 2 after the second, ...) and
  * t_keep slots if it is a Transition segment.  A segment keeps its best
  * slots: larger importance first, then lower position.  Then the table is
- * compacted as in orc_evict.
+ * compacted as in orc_evict.  seq_mask (NULL: every sequence) names the
+ * sequences the eviction fires for; the others are skipped whole.
  */
-void orc_evict_tbe(orc_cache *c, const float *importance, int r0, int r_min, int t_keep,
-                   int q_window, int recent_window)
+void orc_evict_tbe(orc_cache *c, const float *importance, const uint8_t *seq_mask, int r0,
+                   int r_min, int t_keep, int q_window, int recent_window)
 {
     for (int b = 0; b < c->B; ++b) {
+        /* the eviction fires per sequence, where a Transition thought was
+         * detected ("ThinKV", Methodology, think-before-evict); the others
+         * stay exactly as they are */
+        if (seq_mask && !seq_mask[b])
+            continue;
         uint32_t *row = c->table + (long)b * c->max_blocks;
         const float *imp = importance + (long)b * c->n_cap;
         int lo = q_window, hi = c->seq_len[b] - recent_window;

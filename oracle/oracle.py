@@ -72,7 +72,7 @@ def lib():
         L.orc_decode.argtypes = [ctypes.POINTER(_Cache), P, ctypes.c_double, P, P, P, P,
                                  ctypes.c_double, P]
         L.orc_evict.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int, ctypes.c_int]
-        L.orc_evict_tbe.argtypes = [ctypes.POINTER(_Cache), P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        L.orc_evict_tbe.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int]
         L.orc_evict_tam.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_float, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int]
@@ -224,13 +224,15 @@ class OracleCache:
         lib().orc_evict(self._c(), _p(imp), _p(kk), int(q_window), int(recent_window))
 
     def evict_tbe(self, importance: np.ndarray, r0: int, r_min: int, t_keep: int, q_window: int,
-                  recent_window: int):
+                  recent_window: int, seq_mask=None):
         """Thought-adaptive eviction ("ThinKV", think-before-evict); see
-        orc_evict_tbe in kvq_oracle.c."""
+        orc_evict_tbe in kvq_oracle.c.  seq_mask: uint8 [B] (None: every
+        sequence); the sequences outside it are skipped."""
         g = self.g
         imp = np.ascontiguousarray(importance, dtype=np.float32).reshape(g.B, g.n_cap)
-        lib().orc_evict_tbe(self._c(), _p(imp), int(r0), int(r_min), int(t_keep), int(q_window),
-                            int(recent_window))
+        sm = None if seq_mask is None else np.ascontiguousarray(seq_mask, dtype=np.uint8).reshape(g.B)
+        lib().orc_evict_tbe(self._c(), _p(imp), None if sm is None else _p(sm), int(r0), int(r_min),
+                            int(t_keep), int(q_window), int(recent_window))
 
     def evict_tam(self, score: np.ndarray, keep_k, pivot_c: float, min_seg: int, q_window: int,
                   recent_window: int):

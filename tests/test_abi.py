@@ -30,6 +30,14 @@ def test_exports_every_declared_symbol():
         assert re.search(rf"\bT {n}$", nm, re.M), n
 
 
+def test_survey_boundary_calls_exported():
+    """The calls the hot path's boundary is drawn with: append + quantise,
+    the decode with its workspace size, windowed top-k eviction."""
+    L = kvq.lib()
+    for n in ("kvq_append_quantize", "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_evict_topk"):
+        assert n in _declared() and hasattr(L, n), n
+
+
 def test_struct_layout_matches_header(tmp_path):
     fields = [f[0] for f in kvq.CacheStruct._fields_]
     prog = tmp_path / "layout.c"
@@ -85,7 +93,7 @@ def test_host_side_validation(over, code):
     assert L.kvq_append_quantize_noalloc(ctypes.byref(s), buf, buf, buf, None) == code
     assert L.kvq_decode_attention(ctypes.byref(s), buf, buf, buf, None, 0.9, 0.1, buf, 1 << 40, None) == code
     assert L.kvq_evict_topk(ctypes.byref(s), buf, buf, 0, 0, buf, 1 << 40, None) == code
-    assert L.kvq_evict_tbe(ctypes.byref(s), buf, 64, 1, 4, 0, 0, buf, 1 << 40, None) == code
+    assert L.kvq_evict_tbe(ctypes.byref(s), buf, None, 64, 1, 4, 0, 0, buf, 1 << 40, None) == code
     assert L.kvq_evict_tam(ctypes.byref(s), buf, buf, 2.0, 1, 0, 0, buf, 1 << 40, None) == code
 
 
@@ -94,8 +102,13 @@ def test_bad_arguments_rejected_before_launch():
     s = _dummy_struct()
     ok = 0x100000
     need = L.kvq_workspace_bytes(ctypes.byref(s))
+    dneed = L.kvq_decode_workspace_bytes(ctypes.byref(s))
+    assert 0 < dneed <= need
+    # each call checks the workspace against its own need
+    assert L.kvq_decode_attention(ctypes.byref(s), ok, ok, ok, None, 0.9, 0.1, ok, dneed - 1, None) == \
+        kvq.KVQ_EINVAL
     assert L.kvq_append_quantize(ctypes.byref(s), None, ok, ok, ok, need, None) == kvq.KVQ_EINVAL
-    assert L.kvq_append_quantize(ctypes.byref(s), ok, ok, ok, ok, need - 1, None) == kvq.KVQ_EINVAL
+    assert L.kvq_append_quantize(ctypes.byref(s), ok, ok, ok, ok, 255, None) == kvq.KVQ_EINVAL
     assert L.kvq_append_quantize(ctypes.byref(s), ok, ok, ok, ok + 8, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_append_quantize_noalloc(ctypes.byref(s), None, ok, ok, None) == kvq.KVQ_EINVAL
     assert L.kvq_append_quantize_noalloc(ctypes.byref(s), ok, ok, None, None) == kvq.KVQ_EINVAL
@@ -104,15 +117,16 @@ def test_bad_arguments_rejected_before_launch():
     assert L.kvq_decode_attention(ctypes.byref(s), ok, None, ok, None, 0.9, 0.1, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_topk(ctypes.byref(s), ok, ok, -1, 0, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_topk(ctypes.byref(s), None, ok, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
-    assert L.kvq_evict_tbe(ctypes.byref(s), None, 64, 1, 4, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
-    assert L.kvq_evict_tbe(ctypes.byref(s), ok, -1, 1, 4, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
-    assert L.kvq_evict_tbe(ctypes.byref(s), ok, 64, 1, -4, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
-    assert L.kvq_evict_tbe(ctypes.byref(s), ok, 64, 1, 4, 0, -1, ok, need, None) == kvq.KVQ_EINVAL
-    assert L.kvq_evict_tbe(ctypes.byref(s), ok, 64, 1, 4, 0, 0, ok, need - 1, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tbe(ctypes.byref(s), None, None, 64, 1, 4, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tbe(ctypes.byref(s), ok, None, -1, 1, 4, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tbe(ctypes.byref(s), ok, None, 64, 1, -4, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tbe(ctypes.byref(s), ok, None, 64, 1, 4, 0, -1, ok, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tbe(ctypes.byref(s), ok, None, 64, 1, 4, 0, 0, ok, 255, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_tam(ctypes.byref(s), None, ok, 2.0, 1, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_tam(ctypes.byref(s), ok, None, 2.0, 1, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, -1.0, 1, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, float("nan"), 1, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, 2.0, 0, 0, 0, ok, need, None) == kvq.KVQ_EINVAL
     assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, 2.0, 1, -1, 0, ok, need, None) == kvq.KVQ_EINVAL
-    assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, 2.0, 1, 0, 0, ok, need - 1, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_tam(ctypes.byref(s), ok, ok, 2.0, 1, 0, 0, ok, 255, None) == kvq.KVQ_EINVAL
+    assert L.kvq_evict_topk(ctypes.byref(s), ok, ok, 0, 0, ok, 255, None) == kvq.KVQ_EINVAL

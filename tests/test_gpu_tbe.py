@@ -105,6 +105,39 @@ def test_mixed_sequences_against_oracle():
         assert_same_cache(oc, gc.state_numpy())
 
 
+def test_sequence_mask_against_oracle():
+    """The eviction fires per sequence (where a Transition starts): masked-out
+    sequences stay exactly as they are, including a block emptied before the
+    call that an unmasked call would drop; the others match the oracle and
+    the freed blocks are ranked over them in batch order."""
+    import torch
+
+    rng = np.random.default_rng(31)
+    rows = [list(np.repeat(rng.integers(0, 3, 30), rng.integers(1, 12, 30))) for _ in range(6)]
+    oc, gc, g = _pair_from_tags(rows)
+    imp = (np.round(rng.exponential(1.0, (g.B, g.n_cap)) * 16) / 16).astype(np.float32)
+    # sequence 2's first block emptied by hand on both sides
+    st = gc.state_numpy()
+    ent = int(st["table"][2 * g.max_blocks])
+    pool, bid = ent >> 30, ent & 0x3FFFFFFF
+    oc.st[f"mask{pool}"][bid] = 0
+    gc.t[f"mask{pool}"].view(torch.int16)[bid] = 0
+    for mask in ([1, 0, 0, 1, 1, 0], [0, 0, 0, 0, 0, 0], [0, 1, 1, 0, 0, 1]):
+        sm = np.array(mask, dtype=np.uint8)
+        log(f"[gpu tbe] sequence mask {mask}")
+        before = gc.state_numpy()
+        gc.evict_tbe(_dev(imp), 4, 1, 2, 0, 0, seq_mask=_dev(sm))
+        oc.evict_tbe(imp, 4, 1, 2, 0, 0, seq_mask=sm)
+        torch.cuda.synchronize()
+        assert gc.status == 0
+        after = gc.state_numpy()
+        assert_same_cache(oc, after)
+        for b in np.flatnonzero(sm == 0):
+            row = slice(b * g.max_blocks, (b + 1) * g.max_blocks)
+            assert np.array_equal(after["table"][row], before["table"][row])
+            assert _kept(after, g, b) == _kept(before, g, b)
+
+
 @pytest.fixture(scope="module", params=list(SMALL_WORKLOADS))
 def pair(request):
     w = SMALL_WORKLOADS[request.param]

@@ -113,3 +113,32 @@ def test_retention_never_grows_with_more_transitions():
         kept.append(sum(1 for p in _kept(oc) if p < len(base)))
     assert kept == sorted(kept, reverse=True) and kept[-1] < kept[0]
     assert kept[0] == 16 + 16 and kept[1] == 8 + 8 and kept[2] == 4 + 4
+
+
+def test_sequence_mask_fires_per_sequence():
+    # "ThinKV", think-before-evict: eviction is triggered where a Transition
+    # thought is detected, so it runs per sequence.  Two sequences with the
+    # same tokens; only sequence 1 is in the mask.  Sequence 0 keeps every
+    # slot, and also the block whose slots were all cleared before the call
+    # (an unmasked call would drop it from the table); sequence 1 ends as
+    # the hand-worked schedule.
+    oc, imp = _build(TAGS, IMP, B=2)
+    ent0 = int(oc.st["table"][0])
+    pool, bid = ent0 >> 30, ent0 & 0x3FFFFFFF
+    oc.st[f"mask{pool}"][bid] = 0          # sequence 0's first block, emptied by hand
+    before = {k: v.copy() for k, v in oc.st.items()}
+    kept0 = _kept(oc, 0)
+    oc.evict_tbe(imp, 2, 1, 1, 0, 0, seq_mask=np.array([0, 1], dtype=np.uint8))
+    assert _kept(oc, 0) == kept0
+    g = oc.g
+    row0 = slice(0, g.max_blocks)
+    assert np.array_equal(oc.st["table"][row0], before["table"][row0])
+    assert int(oc.st["n_blocks"][0]) == int(before["n_blocks"][0])
+    assert _kept(oc, 1) == [1, 5, 8, 10, 13, 14, 15, 16]
+    # a mask of ones is the unmasked call
+    oc2, imp2 = _build(TAGS, IMP, B=2)
+    oc3, _ = _build(TAGS, IMP, B=2)
+    oc2.evict_tbe(imp2, 2, 1, 1, 0, 0, seq_mask=np.ones(2, dtype=np.uint8))
+    oc3.evict_tbe(imp2, 2, 1, 1, 0, 0)
+    for k in oc2.st:
+        assert np.array_equal(oc2.st[k], oc3.st[k]), k
