@@ -8,14 +8,17 @@
 // that type in place; only when none is free does a block come from the
 // type's free list.
 //
-// Two launches: append_plan (one workgroup per sequence) finds the slot or
-// decides on a pop; append_write (one wave per (sequence, kv head))
-// quantises K and V, packs the codes into the cache layout and updates the
-// block metadata.  Pops are ranked across sequences in batch order from a
-// copy of the free-stack tops taken by the plan, so no cross-workgroup
-// synchronisation is needed.
+// One launch, one workgroup per sequence: it finds the slot or decides on a
+// pop, then quantises K and V for every kv head, packs the codes into the
+// cache layout and updates the block metadata.  Pops are served in batch
+// order: each workgroup publishes its pops per pool in a word of its own
+// (tagged with the call's epoch), and a workgroup that pops sums the words
+// of the sequences before it for its rank; the last workgroup also sums all
+// of them and lowers the free-stack tops.  Workgroups only wait on earlier
+// ones, which are dispatched first and never wait on later ones.
 #include <limits.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "kvq_device.h"
@@ -25,32 +28,30 @@ namespace kvq {
 
 namespace {
 
-constexpr int PLAN_THREADS = 256;
+constexpr int PLAN_THREADS = 512;
 constexpr int PLAN_UNROLL = 4;
 
-__global__ __launch_bounds__(PLAN_THREADS) void append_plan(kvq_cache c, const uint8_t *tags,
-                                                            AppendWs ws) {
-    const int b = blockIdx.x;
+// The plan of sequence b: -2 nothing to do (tag none, or the sequence cannot
+// be served: status set), -1 reuse (entry, slot), p >= 0 pop a block of
+// pool p.  The workgroup scans the table in rounds; each thread issues
+// PLAN_UNROLL independent loads per round so the dependent table -> mask
+// chain overlaps, and the first entry of the tag with a free slot wins.
+struct Plan {
+    int need;
+    uint32_t entry;
+    int slot;
+};
+__device__ inline Plan plan_slot(const kvq_cache &c, int b, int tag, int *first, Plan *sh_plan) {
     const int tid = threadIdx.x;
-    if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
-    const int tag = tags[b];
     if (tag == TAG_NONE || tag > 2 || c.seq_len[b] >= c.n_cap) {
-        if (tid == 0) {
-            ws.need[b] = -2;
-            if (tag != TAG_NONE) *c.status = tag > 2 ? KVQ_EINVAL : KVQ_ENOSPC;
-        }
-        return;
+        if (tid == 0 && tag != TAG_NONE) *c.status = tag > 2 ? KVQ_EINVAL : KVQ_ENOSPC;
+        return Plan{-2, 0u, 0};
     }
-    __shared__ int first;
-    if (tid == 0) first = INT_MAX;
+    if (tid == 0) *first = INT_MAX;
     __syncthreads();
     const int nb = c.n_blocks[b];
     const uint32_t *row = c.table + (size_t)b * c.max_blocks;
     const uint16_t *mask = c.mask[tag];
-    // Scan the table in rounds; each thread issues PLAN_UNROLL independent
-    // loads per round so the dependent table -> mask chain overlaps.  The
-    // thread holding the first entry with a free slot writes the plan from
-    // its registers.
     for (int base = 0; base < nb; base += PLAN_THREADS * PLAN_UNROLL) {
         uint32_t ent[PLAN_UNROLL];
         uint32_t m[PLAN_UNROLL];
@@ -69,31 +70,71 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_plan(kvq_cache c, const u
                 if (m[u] != 0xffffu) mine = min(mine, e);
             }
         }
-        if (mine != INT_MAX) atomicMin(&first, mine);
+        if (mine != INT_MAX) atomicMin(first, mine);
         __syncthreads();
-        const int f = first;   // the same in every thread
+        const int f = *first;   // the same in every thread
         if (f != INT_MAX) {
+            // the thread holding the first free entry passes it on
 #pragma unroll
             for (int u = 0; u < PLAN_UNROLL; ++u)
-                if (base + u * PLAN_THREADS + tid == f) {
-                    ws.need[b] = -1;
-                    ws.entry[b] = (int32_t)ent[u];
-                    ws.slot[b] = __builtin_ctz(~m[u]);
-                }
-            return;
+                if (base + u * PLAN_THREADS + tid == f) *sh_plan = Plan{-1, ent[u], __builtin_ctz(~m[u])};
+            __syncthreads();
+            return *sh_plan;
         }
         // every thread has read `first` before any thread of the next round
         // may lower it (f is uniform, so the barrier is too)
         __syncthreads();
     }
-    if (tid == 0) {
-        if (nb >= c.max_blocks) {
-            ws.need[b] = -2;
-            *c.status = KVQ_ENOSPC;
-        } else {
-            ws.need[b] = tag;
-        }
+    if (nb >= c.max_blocks) {
+        if (tid == 0) *c.status = KVQ_ENOSPC;
+        return Plan{-2, 0u, 0};
     }
+    return Plan{tag, 0u, 0};
+}
+
+// Pop counts of one sequence (one per pool) in a word tagged with the call's
+// epoch: bits 0-32 three 11-bit counts, 40-63 the epoch.  A word of another
+// epoch (an earlier call, or never written) is not this call's yet.
+constexpr int SYNC_SPINS = 1 << 22;
+__device__ inline unsigned long long pop_word(uint32_t epoch, int need) {
+    const unsigned long long cnt = need >= 0 ? 1ull << (11 * need) : 0ull;
+    return ((unsigned long long)(epoch & 0xffffffu) << 40) | cnt;
+}
+// Pops per pool by sequences [0, n), summed by wave 0 (n <= 1024): every
+// lane waits for its sequences' words of this epoch (bounded: false if one
+// never comes).  The words are read at device scope; they hold all that is
+// passed, so no acquire (which would invalidate the cache) is needed.
+__device__ inline bool pops_before(const unsigned long long *words, int n, uint32_t epoch, int cnt[3]) {
+    const int lane = threadIdx.x & 63;
+    int c0 = 0, c1 = 0, c2 = 0;
+    bool ok = true;
+    for (int i = lane; i < n; i += 64) {
+        unsigned long long v = 0;
+        int spins = 0;
+        for (;;) {
+            v = __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(v >> 40) == (epoch & 0xffffffu)) break;
+            if (++spins > SYNC_SPINS) {
+                ok = false;
+                v = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        c0 += (int)(v & 0x7ff);
+        c1 += (int)((v >> 11) & 0x7ff);
+        c2 += (int)((v >> 22) & 0x7ff);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        c0 += __shfl_xor(c0, off);
+        c1 += __shfl_xor(c1, off);
+        c2 += __shfl_xor(c2, off);
+    }
+    cnt[0] = c0;
+    cnt[1] = c1;
+    cnt[2] = c2;
+    return __ballot(!ok) == 0;
 }
 
 // Group-quantise one 128-channel fp16 row held two channels per lane
@@ -188,50 +229,20 @@ __device__ inline void quantise_pair_native(uint32_t two, int pool, uint32_t &c0
     scale_zero = (uint32_t)sh | ((uint32_t)zh << 16);
 }
 
-__global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *k_new,
-                                                   const uint16_t *v_new, AppendWs ws) {
-    const int b = blockIdx.x / c.Hkv, h = blockIdx.x % c.Hkv;
-    const int lane = threadIdx.x;
-    // this lane's two channels of the new K and V rows, loaded before the
-    // plan so that the loads overlap the dependent plan/table reads
-    const size_t row_off = ((size_t)b * c.Hkv + h) * HD;
-    const uint32_t k_two = reinterpret_cast<const uint32_t *>(k_new + row_off)[lane];
-    const uint32_t v_two = reinterpret_cast<const uint32_t *>(v_new + row_off)[lane];
-    if (blockIdx.x == 0 && lane < 3) {
-        int cnt = 0;
-        for (int bb = 0; bb < c.B; ++bb) cnt += ws.need[bb] == lane;
-        c.free_top[lane] = ws.top[lane] - min(cnt, ws.top[lane]);
-    }
-    const int need = ws.need[b];
-    if (need == -2) return;
-    int pool, slot;
-    uint32_t id;
-    bool fresh = false;
-    if (need == -1) {
-        const uint32_t ent = (uint32_t)ws.entry[b];
-        pool = (int)(ent >> 30);
-        id = ent & 0x3fffffffu;
-        slot = ws.slot[b];
-    } else {
-        pool = need;
-        int rank = 0;
-        for (int bb = lane; bb < b; bb += 64) rank += ws.need[bb] == pool;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) rank += __shfl_xor(rank, off);
-        const int top = ws.top[pool];
-        if (rank >= top) {
-            if (h == 0 && lane == 0) *c.status = KVQ_ENOSPC;
-            return;
-        }
-        id = c.free_ids[pool][top - 1 - rank];
-        slot = 0;
-        fresh = true;
-    }
-    const int bits = pool_bits(pool);
-    uint8_t *reg = region_ptr(c.kv[pool], id, c.Hkv, h, pool);
+// LDS written by some lanes of a wave is visible to the others after this
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-    __shared__ uint8_t kcode[HD];  // by K-row code index
-    __shared__ uint8_t vcode[HD];  // by channel
+// Quantise and pack one kv head's K and V rows of the token into slot `slot`
+// of region `reg` (one wave; lane l holds channels 2l, 2l+1 of each row).
+// kcode / vcode: the wave's own 128-byte LDS buffers.
+__device__ inline void write_head(const kvq_cache &c, uint8_t *reg, int pool, int slot, uint32_t k_two,
+                                  uint32_t v_two, uint8_t *kcode, uint8_t *vcode) {
+    const int lane = threadIdx.x & 63;
+    const int bits = pool_bits(pool);
     uint32_t k0, k1, ksz, v0, v1, vsz;
     if (c.codec == KVQ_CODEC_NATIVE) {
         quantise_pair_native(k_two, pool, k0, k1, ksz);
@@ -249,7 +260,8 @@ __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *
         reinterpret_cast<uint32_t *>(reg + 512 * bits)[slot * NGRP + g] = ksz;
         reinterpret_cast<uint32_t *>(reg + 512 * bits + 256)[slot * NGRP + g] = vsz;
     }
-    __syncthreads();
+    // the wave's code bytes are in LDS before any lane packs them
+    wave_sync();
 
     // K row: 4*bits dwords, LSB-first.
     const int per = 32 / bits;  // codes per dword
@@ -275,8 +287,91 @@ __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *
         }
         *dw = val;
     }
+    // the buffers are reused by the wave's next head
+    wave_sync();
+}
 
-    if (h == 0 && lane == 0) {
+// One workgroup per sequence: plan the slot, take a block id if the plan
+// pops (ranked in batch order over the sequences' published pop words),
+// then quantise and write the token for every kv head (wave w takes heads
+// w, w + 8, ...) and update the block metadata.
+__global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const uint16_t *k_new,
+                                                             const uint16_t *v_new, const uint8_t *tags,
+                                                             AppendWs ws, uint32_t epoch) {
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NWAVE = PLAN_THREADS / 64;
+    __shared__ int first;
+    __shared__ Plan sh_plan;
+    __shared__ int s_id;
+    __shared__ uint8_t kcode[NWAVE][HD], vcode[NWAVE][HD];
+    // this lane's two channels of the first head's new K and V rows, loaded
+    // first so that the loads overlap the plan
+    const int h0 = wave;
+    uint32_t k_two = 0, v_two = 0;
+    if (h0 < c.Hkv) {
+        const size_t row_off = ((size_t)b * c.Hkv + h0) * HD;
+        k_two = reinterpret_cast<const uint32_t *>(k_new + row_off)[lane];
+        v_two = reinterpret_cast<const uint32_t *>(v_new + row_off)[lane];
+    }
+    // the free-stack tops before the call: read before this sequence's pop
+    // word is published (only the last workgroup lowers them, once every
+    // word is in)
+    const int tops[3] = {c.free_top[0], c.free_top[1], c.free_top[2]};
+    const Plan pl = plan_slot(c, b, tags[b], &first, &sh_plan);
+    if (tid == 0) {
+        // the tops have been read (every load of the wave returned) before the
+        // word goes out; the word carries its data, so no fence is needed
+        __builtin_amdgcn_s_waitcnt(0);
+        __hip_atomic_store(ws.pops + b, pop_word(epoch, pl.need), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const bool last = b == c.B - 1;
+    if (pl.need >= 0 || last) {
+        if (wave == 0) {
+            int cnt[3];
+            const bool ok = pops_before(ws.pops, b, epoch, cnt);
+            if (lane == 0) {
+                if (!ok) *c.status = KVQ_EHIP;
+                if (last) {
+                    for (int p = 0; p < 3; ++p) {
+                        const int tot = cnt[p] + (pl.need == p ? 1 : 0);
+                        c.free_top[p] = tops[p] - min(tot, tops[p]);
+                    }
+                }
+                int id = -1;
+                if (pl.need >= 0) {
+                    const int top = tops[pl.need], rank = cnt[pl.need];
+                    if (rank >= top) *c.status = KVQ_ENOSPC;
+                    else id = (int)c.free_ids[pl.need][top - 1 - rank];
+                }
+                s_id = id;
+            }
+        }
+        __syncthreads();
+    }
+    if (pl.need == -2) return;
+    int pool, slot;
+    uint32_t id;
+    const bool fresh = pl.need >= 0;
+    if (fresh) {
+        if (s_id < 0) return;   // pool exhausted: the sequence is left unchanged
+        pool = pl.need;
+        id = (uint32_t)s_id;
+        slot = 0;
+    } else {
+        pool = (int)(pl.entry >> 30);
+        id = pl.entry & 0x3fffffffu;
+        slot = pl.slot;
+    }
+    for (int h = h0; h < c.Hkv; h += NWAVE) {
+        if (h != h0) {
+            const size_t row_off = ((size_t)b * c.Hkv + h) * HD;
+            k_two = reinterpret_cast<const uint32_t *>(k_new + row_off)[lane];
+            v_two = reinterpret_cast<const uint32_t *>(v_new + row_off)[lane];
+        }
+        write_head(c, region_ptr(c.kv[pool], id, c.Hkv, h, pool), pool, slot, k_two, v_two, kcode[wave],
+                   vcode[wave]);
+    }
+    if (tid == 0) {
         if (fresh) {
             const int nb = c.n_blocks[b];
             c.table[(size_t)b * c.max_blocks + nb] = ((uint32_t)pool << 30) | id;
@@ -297,9 +392,9 @@ __global__ __launch_bounds__(64) void append_write(kvq_cache c, const uint16_t *
 // APPEND_SCRATCH_BYTES, in a file-scope device array.  Each GPU holds its own
 // copy for the life of the process; its device address is looked up once per
 // device (the array's name is only a host-side stand-in).  Every plan buffer
-// is written by append_plan before append_write reads it, so nothing needs
-// clearing between calls; calls that overlap on one GPU share the array and
-// race.
+// is written before it is read in the same call (the pop words carry the
+// call's epoch), so nothing needs clearing between calls; calls that overlap
+// on one GPU share the array and race.
 __device__ __align__(256) uint8_t scratch[APPEND_SCRATCH_BYTES];
 
 void *append_scratch() {
@@ -318,10 +413,13 @@ void *append_scratch() {
 
 bool launch_append(const kvq_cache &c, const void *k_new, const void *v_new, const uint8_t *tags,
                    void *ws_ptr, hipStream_t s) {
+    // a fresh epoch per call for the sequences' pop words (24 bits kept,
+    // never 0, so zeroed memory never matches)
+    static std::atomic<uint32_t> epochs{0};
+    uint32_t epoch = (epochs.fetch_add(1) % 0xffffffu) + 1;
     AppendWs ws(ws_ptr, c);
-    hipLaunchKernelGGL(append_plan, dim3(c.B), dim3(PLAN_THREADS), 0, s, c, tags, ws);
-    hipLaunchKernelGGL(append_write, dim3(c.B * c.Hkv), dim3(64), 0, s, c,
-                       static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new), ws);
+    hipLaunchKernelGGL(append_token, dim3(c.B), dim3(PLAN_THREADS), 0, s, c, static_cast<const uint16_t *>(k_new),
+                       static_cast<const uint16_t *>(v_new), tags, ws, epoch);
     return hipGetLastError() == hipSuccess;
 }
 
