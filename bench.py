@@ -321,13 +321,13 @@ def evict_bench(args, w):
                      "kernel": DECODE_KERNEL, "avg_us": float(dec_ms.mean() * 1e3),
                      "us": {"mean": float(dec_ms.mean() * 1e3), "p10": float(np.quantile(dec_ms, 0.1) * 1e3),
                             "p50": float(np.median(dec_ms) * 1e3), "p90": float(np.quantile(dec_ms, 0.9) * 1e3)}},
-        "evict": {"kernel": "kvq_evict_topk (select + push)", "avg_us": float(evi_ms.mean() * 1e3),
+        "evict": {"kernel": "kvq_evict_topk (keys + select, compact and push)", "avg_us": float(evi_ms.mean() * 1e3),
                   "bytes": evb, "achieved_gbs": ev_gbs, "frac": ev_gbs / HBM_PEAK_GBS},
-        "evict_tbe": {"kernel": "kvq_evict_tbe (prep + drop + compact + push)", "avg_us": float(tbe_ms.mean() * 1e3),
+        "evict_tbe": {"kernel": "kvq_evict_tbe (prep + drop + compact and push)", "avg_us": float(tbe_ms.mean() * 1e3),
                       "r0_rmin_tkeep": list(TBE_PARAMS), "valid_before": n_valid,
                       "valid_after": tbe_kept, "bytes": evb,
                       "achieved_gbs": evb / (tbe_ms.mean() * 1e-3) / 1e9},
-        "evict_tam": {"kernel": "kvq_evict_tam (prep + drop + compact + push)",
+        "evict_tam": {"kernel": "kvq_evict_tam (prep + drop + compact and push)",
                       "avg_us": float(tam_ms.mean() * 1e3), "pivot_c_min_seg": list(TAM_PARAMS),
                       "valid_before": n_valid, "valid_after": tam_kept, "bytes": evb,
                       "achieved_gbs": evb / (tam_ms.mean() * 1e-3) / 1e9},

@@ -11,18 +11,16 @@
 // One launch, one workgroup per sequence: it finds the slot or decides on a
 // pop, then quantises K and V for every kv head, packs the codes into the
 // cache layout and updates the block metadata.  Pops are served in batch
-// order: each workgroup publishes its pops per pool in a word of its own
-// (tagged with the call's epoch), and a workgroup that pops sums the words
-// of the sequences before it for its rank; the last workgroup also sums all
-// of them and lowers the free-stack tops.  Workgroups only wait on earlier
-// ones, which are dispatched first and never wait on later ones.
+// order (kvq_sync.h): each workgroup publishes its pops per pool, and a
+// workgroup that pops sums the pops of the sequences before it for its rank;
+// the last workgroup also sums all of them and lowers the free-stack tops.
 #include <limits.h>
 
-#include <atomic>
 #include <mutex>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_sync.h"
 
 namespace kvq {
 
@@ -90,51 +88,6 @@ __device__ inline Plan plan_slot(const kvq_cache &c, int b, int tag, int *first,
         return Plan{-2, 0u, 0};
     }
     return Plan{tag, 0u, 0};
-}
-
-// Pop counts of one sequence (one per pool) in a word tagged with the call's
-// epoch: bits 0-32 three 11-bit counts, 40-63 the epoch.  A word of another
-// epoch (an earlier call, or never written) is not this call's yet.
-constexpr int SYNC_SPINS = 1 << 22;
-__device__ inline unsigned long long pop_word(uint32_t epoch, int need) {
-    const unsigned long long cnt = need >= 0 ? 1ull << (11 * need) : 0ull;
-    return ((unsigned long long)(epoch & 0xffffffu) << 40) | cnt;
-}
-// Pops per pool by sequences [0, n), summed by wave 0 (n <= 1024): every
-// lane waits for its sequences' words of this epoch (bounded: false if one
-// never comes).  The words are read at device scope; they hold all that is
-// passed, so no acquire (which would invalidate the cache) is needed.
-__device__ inline bool pops_before(const unsigned long long *words, int n, uint32_t epoch, int cnt[3]) {
-    const int lane = threadIdx.x & 63;
-    int c0 = 0, c1 = 0, c2 = 0;
-    bool ok = true;
-    for (int i = lane; i < n; i += 64) {
-        unsigned long long v = 0;
-        int spins = 0;
-        for (;;) {
-            v = __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((uint32_t)(v >> 40) == (epoch & 0xffffffu)) break;
-            if (++spins > SYNC_SPINS) {
-                ok = false;
-                v = 0;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        c0 += (int)(v & 0x7ff);
-        c1 += (int)((v >> 11) & 0x7ff);
-        c2 += (int)((v >> 22) & 0x7ff);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        c0 += __shfl_xor(c0, off);
-        c1 += __shfl_xor(c1, off);
-        c2 += __shfl_xor(c2, off);
-    }
-    cnt[0] = c0;
-    cnt[1] = c1;
-    cnt[2] = c2;
-    return __ballot(!ok) == 0;
 }
 
 // Group-quantise one 128-channel fp16 row held two channels per lane
@@ -292,12 +245,12 @@ __device__ inline void write_head(const kvq_cache &c, uint8_t *reg, int pool, in
 }
 
 // One workgroup per sequence: plan the slot, take a block id if the plan
-// pops (ranked in batch order over the sequences' published pop words),
-// then quantise and write the token for every kv head (wave w takes heads
-// w, w + 8, ...) and update the block metadata.
+// pops (ranked in batch order over the sequences' published pops), then
+// quantise and write the token for every kv head (wave w takes heads w,
+// w + 8, ...) and update the block metadata.
 __global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const uint16_t *k_new,
                                                              const uint16_t *v_new, const uint8_t *tags,
-                                                             AppendWs ws, uint32_t epoch) {
+                                                             AppendWs sync) {
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int NWAVE = PLAN_THREADS / 64;
     __shared__ int first;
@@ -313,22 +266,25 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const 
         k_two = reinterpret_cast<const uint32_t *>(k_new + row_off)[lane];
         v_two = reinterpret_cast<const uint32_t *>(v_new + row_off)[lane];
     }
-    // the free-stack tops before the call: read before this sequence's pop
-    // word is published (only the last workgroup lowers them, once every
-    // word is in)
-    const int tops[3] = {c.free_top[0], c.free_top[1], c.free_top[2]};
+    // wave 0 publishes and ranks: it reads the call's epoch and the
+    // free-stack tops before this sequence's pops go out (only the last
+    // workgroup moves the tops and the epoch, once every sequence's are in)
+    uint32_t epoch = 0;
+    int tops[3] = {0, 0, 0};
+    if (wave == 0) {
+        epoch = sync_epoch(sync);
+        for (int p = 0; p < 3; ++p) tops[p] = c.free_top[p];
+    }
     const Plan pl = plan_slot(c, b, tags[b], &first, &sh_plan);
-    if (tid == 0) {
-        // the tops have been read (every load of the wave returned) before the
-        // word goes out; the word carries its data, so no fence is needed
-        __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_store(ws.pops + b, pop_word(epoch, pl.need), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 3) {
+        wait_loads_done();
+        sync_publish(sync, c.B, b, tid, epoch, pl.need == tid ? 1u : 0u);
     }
     const bool last = b == c.B - 1;
     if (pl.need >= 0 || last) {
         if (wave == 0) {
             int cnt[3];
-            const bool ok = pops_before(ws.pops, b, epoch, cnt);
+            const bool ok = sync_counts_before(sync, c.B, b, epoch, last ? 7u : 1u << pl.need, cnt);
             if (lane == 0) {
                 if (!ok) *c.status = KVQ_EHIP;
                 if (last) {
@@ -336,6 +292,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const 
                         const int tot = cnt[p] + (pl.need == p ? 1 : 0);
                         c.free_top[p] = tops[p] - min(tot, tops[p]);
                     }
+                    sync_close(sync, epoch);
                 }
                 int id = -1;
                 if (pl.need >= 0) {
@@ -388,13 +345,15 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const 
 
 }  // namespace
 
-// Scratch of the no-allocation append: the plan buffers (AppendWs) for up to
-// APPEND_SCRATCH_BYTES, in a file-scope device array.  Each GPU holds its own
-// copy for the life of the process; its device address is looked up once per
-// device (the array's name is only a host-side stand-in).  Every plan buffer
-// is written before it is read in the same call (the pop words carry the
-// call's epoch), so nothing needs clearing between calls; calls that overlap
-// on one GPU share the array and race.
+// Scratch of the no-allocation append: the sync words (AppendWs) for up to
+// APPEND_SCRATCH_BYTES, in a file-scope device array, zero when the code
+// object loads, as the sync region must be before its first call.  Each GPU
+// holds its own copy for the life of the process; its device address is
+// looked up once per device (the array's name is only a host-side
+// stand-in).  The words carry the epoch of the call that wrote them and the
+// epoch itself lives in the array, so nothing needs clearing between calls
+// (graph replays included); calls that overlap on one GPU share the array
+// and race.
 __device__ __align__(256) uint8_t scratch[APPEND_SCRATCH_BYTES];
 
 void *append_scratch() {
@@ -413,13 +372,9 @@ void *append_scratch() {
 
 bool launch_append(const kvq_cache &c, const void *k_new, const void *v_new, const uint8_t *tags,
                    void *ws_ptr, hipStream_t s) {
-    // a fresh epoch per call for the sequences' pop words (24 bits kept,
-    // never 0, so zeroed memory never matches)
-    static std::atomic<uint32_t> epochs{0};
-    uint32_t epoch = (epochs.fetch_add(1) % 0xffffffu) + 1;
     AppendWs ws(ws_ptr, c);
     hipLaunchKernelGGL(append_token, dim3(c.B), dim3(PLAN_THREADS), 0, s, c, static_cast<const uint16_t *>(k_new),
-                       static_cast<const uint16_t *>(v_new), tags, ws, epoch);
+                       static_cast<const uint16_t *>(v_new), tags, ws);
     return hipGetLastError() == hipSuccess;
 }
 

@@ -23,12 +23,14 @@
 // evict_tbe_prep / evict_tam_prep + evict_seg_drop + evict_seg_compact:
 //   segment-granular eviction, thought-adaptive (TBE) or by thought-aware
 //   budgets (TAM) (below).
-// evict_push: one workgroup per sequence pushes its freed ids at offsets
-//   ranked across sequences in batch order.
+// The compacting kernels (evict_select, evict_seg_compact) end by pushing
+// each sequence's freed ids onto the free stacks, ranked across sequences in
+// batch order (kvq_sync.h, push_freed).
 #include <limits.h>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_sync.h"
 
 namespace kvq {
 
@@ -85,9 +87,10 @@ __device__ inline int block_prefix(bool flag, int *wave_tot, int &total) {
 // entry's old and new masks; the entry's first slot's lane stores the new
 // mask if it changed, and parks it in that slot's word.  Then, thread per
 // entry, the entries that kept a slot are packed in order and the emptied
-// ones listed for the free-stack pushes.
+// ones listed for the free-stack pushes.  Returns how many were freed;
+// pool_cnt holds them per pool.
 template <class Keep>
-__device__ inline void clear_and_compact(const kvq_cache &c, int b, uint64_t *key, int nslot, int nb,
+__device__ inline int clear_and_compact(const kvq_cache &c, int b, uint64_t *key, int nslot, int nb,
                                          uint32_t *row, EvictWs &ws, int *wave_tot, int *pool_cnt,
                                          const Keep &keep) {
     const int tid = threadIdx.x, lane = tid & 63;
@@ -141,7 +144,77 @@ __device__ inline void clear_and_compact(const kvq_cache &c, int b, uint64_t *ke
         __syncthreads();
     }
     if (tid == 0) c.n_blocks[b] = kept_base;
-    if (tid < 4) ws.nfreed[b * 4 + tid] = tid < 3 ? pool_cnt[tid] : freed_base;
+    return freed_base;
+}
+
+// The start of a compacting kernel, before any of the workgroup's work: wave
+// 0 takes the call's epoch and thread p < 3 the free-stack top of pool p
+// (both read before the workgroup's counts are published; only the last
+// workgroup moves them, once every sequence's counts are in).
+__device__ inline uint32_t push_begin(const kvq_cache &c, const SyncWs &sync, int *top0) {
+    uint32_t epoch = 0;
+    if (threadIdx.x < 64) epoch = sync_epoch(sync);
+    if (threadIdx.x < 3) top0[threadIdx.x] = c.free_top[threadIdx.x];
+    return epoch;
+}
+
+// Push sequence b's freed ids (freed[0 .. nf), table order; pool_cnt per
+// pool) onto the free stacks, the sequences in batch order: publish the
+// counts, sum those of the sequences before b (wave 0), and push each id at
+// the pool's old top + that sum + its rank in table order.  The last
+// sequence raises the tops and closes the call.  top0 and epoch from
+// push_begin; every thread calls it after a barrier that follows the
+// compaction.
+__device__ inline void push_freed(const kvq_cache &c, int b, const uint32_t *freed, int nf, const int *pool_cnt,
+                                  const int *top0, const SyncWs &sync, uint32_t epoch) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    __shared__ int base[3];
+    __shared__ int wave_cnt[SEL_WAVES][3];
+    if (tid < 3) {
+        wait_loads_done();
+        sync_publish(sync, c.B, b, tid, epoch, (uint32_t)pool_cnt[tid]);
+    }
+    const bool last = b == c.B - 1;
+    if (nf == 0 && !last) return;
+    if (wv == 0) {
+        int cnt[3];
+        const uint32_t pm = last ? 7u : (pool_cnt[0] ? 1u : 0u) | (pool_cnt[1] ? 2u : 0u) | (pool_cnt[2] ? 4u : 0u);
+        const bool ok = sync_counts_before(sync, c.B, b, epoch, pm, cnt);
+        if (lane < 3) {
+            const int at = top0[lane] + (lane == 0 ? cnt[0] : lane == 1 ? cnt[1] : cnt[2]);
+            base[lane] = at;
+            if (last) c.free_top[lane] = at + pool_cnt[lane];
+        }
+        if (lane == 0) {
+            if (!ok) *c.status = KVQ_EHIP;
+            if (last) sync_close(sync, epoch);
+        }
+    }
+    __syncthreads();
+    for (int c0 = 0; c0 < nf; c0 += SEL_THREADS) {
+        const int i = c0 + tid;
+        const uint32_t ent = i < nf ? freed[i] : 0xffffffffu;
+        const int pool = i < nf ? (int)(ent >> 30) : 3;
+        int rank = 0;
+        for (int p = 0; p < 3; ++p) {
+            const uint64_t bal = __ballot(pool == p);
+            if (lane == 0) wave_cnt[wv][p] = __popcll(bal);
+            if (pool == p) rank = __popcll(bal & ((1ull << lane) - 1));
+        }
+        __syncthreads();
+        if (pool < 3) {
+            int before = 0;
+            for (int w = 0; w < wv; ++w) before += wave_cnt[w][pool];
+            c.free_ids[pool][base[pool] + before + rank] = ent & 0x3fffffffu;
+        }
+        __syncthreads();
+        if (tid < 3) {
+            int tot = 0;
+            for (int w = 0; w < SEL_WAVES; ++w) tot += wave_cnt[w][tid];
+            base[tid] += tot;
+        }
+        __syncthreads();
+    }
 }
 
 // One word per slot (slot s of entry e at 16 e + s), thread per slot, for
@@ -217,10 +290,12 @@ __global__ __launch_bounds__(KEY_THREADS) void evict_keys(kvq_cache c, const flo
 
 // Top-k, step 2 (one workgroup per sequence): the k-th largest key, then
 // the losers cleared and the row compacted.
-__global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const int32_t *keep_k, EvictWs ws) {
+__global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const int32_t *keep_k, EvictWs ws,
+                                                           SyncWs sync) {
     const int b = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
-    if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
+    __shared__ int top0[3];
+    const uint32_t epoch = push_begin(c, sync, top0);
     const int nb = c.n_blocks[b];
     const int nslot = nb * BLK;
     uint32_t *row = c.table + (size_t)b * c.max_blocks;
@@ -310,11 +385,13 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const i
         }
     }
 
-    // 3. clear losers, compact the table row, list freed entries
-    clear_and_compact(c, b, key, nslot, nb, row, ws, wave_tot, pool_cnt,
-                      [&](uint64_t kk) {
-                          return kk != 0 && !(evicting && kk > 1 && !(k > 0 && (kk >> thr_shift) >= (thr >> thr_shift)));
-                      });
+    // 3. clear losers, compact the table row, list freed entries, push them
+    const int nf = clear_and_compact(
+        c, b, key, nslot, nb, row, ws, wave_tot, pool_cnt, [&](uint64_t kk) {
+            return kk != 0 && !(evicting && kk > 1 && !(k > 0 && (kk >> thr_shift) >= (thr >> thr_shift)));
+        });
+    __syncthreads();
+    push_freed(c, b, ws.freed + (size_t)b * c.max_blocks, nf, pool_cnt, top0, sync, epoch);
 }
 
 // Exclusive prefix sum over the waves of a value each wave holds
@@ -531,8 +608,7 @@ __device__ inline uint64_t block_scan_u64(uint64_t x, uint64_t *wave_u64, uint64
 // cuts them into segments and gives each segment the number of its
 // droppable candidates it keeps (segkeep); evict_seg_drop then drops the
 // rest of each segment, lowest value first (ties: higher position first),
-// and evict_seg_compact clears and compacts; evict_push frees the emptied
-// blocks.
+// and evict_seg_compact clears, compacts and frees the emptied blocks.
 
 struct SegOrder {
     int n, nseg, n_t;
@@ -553,7 +629,6 @@ __device__ inline SegOrder seg_order(const kvq_cache &c, int b, const float *val
                                      int recent_window, EvictWs &ws, uint32_t *sfx, int *wave_tot,
                                      uint64_t *wave_u64) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
     const int nb = c.n_blocks[b];
     const int nslot = nb * BLK;
     const int lo = q_window, hi = min(c.seq_len[b] - recent_window, c.n_cap);
@@ -674,8 +749,6 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tbe_prep(kvq_cache c, const
                                                               EvictWs ws) {
     const int b = blockIdx.x, tid = threadIdx.x;
     if (seq_mask && seq_mask[b] == 0) {
-        // (the free-stack tops are still taken, by sequence 0's workgroup)
-        if (b == 0 && tid < 3) ws.top[tid] = c.free_top[tid];
         if (tid == 0) ws.segn[2 * b] = -1;
         return;
     }
@@ -936,66 +1009,27 @@ __global__ __launch_bounds__(DROP_THREADS) void evict_seg_drop(kvq_cache c, Evic
 }
 
 // evict_seg_compact: clear the dropped slots (word 2) and compact the table
-// row as evict_select does, one workgroup per sequence.
-__global__ __launch_bounds__(SEL_THREADS) void evict_seg_compact(kvq_cache c, EvictWs ws) {
+// row as evict_select does, one workgroup per sequence, then push the freed
+// ids.  A sequence left as it is frees nothing but still takes its part in
+// the batch-order push.
+__global__ __launch_bounds__(SEL_THREADS) void evict_seg_compact(kvq_cache c, EvictWs ws, SyncWs sync) {
     const int b = blockIdx.x, tid = threadIdx.x;
-    if (ws.segn[2 * b] < 0) {   // a sequence left as it is frees nothing
-        if (tid < 4) ws.nfreed[b * 4 + tid] = 0;
-        return;
-    }
-    const int nb = c.n_blocks[b];
-    uint32_t *row = c.table + (size_t)b * c.max_blocks;
-    uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
     __shared__ int wave_tot[SEL_WAVES];
     __shared__ int pool_cnt[4];
+    __shared__ int top0[3];
+    const uint32_t epoch = push_begin(c, sync, top0);
     if (tid < 4) pool_cnt[tid] = 0;
     __syncthreads();
-    clear_and_compact(c, b, key, nb * BLK, nb, row, ws, wave_tot, pool_cnt,
-                      [](uint64_t kk) { return kk != 0 && kk != 2; });
-}
-
-__global__ __launch_bounds__(256) void evict_push(kvq_cache c, EvictWs ws) {
-    const int b = blockIdx.x, tid = threadIdx.x;
-    __shared__ int base[3];
-    __shared__ int wave_cnt[4][3];
-    if (tid < 3) {
-        int s = ws.top[tid];
-        for (int bb = 0; bb < b; ++bb) s += ws.nfreed[bb * 4 + tid];
-        base[tid] = s;
-        if (b == 0) {
-            int tot = ws.top[tid];
-            for (int bb = 0; bb < c.B; ++bb) tot += ws.nfreed[bb * 4 + tid];
-            c.free_top[tid] = tot;
-        }
+    int nf = 0;
+    if (ws.segn[2 * b] >= 0) {
+        const int nb = c.n_blocks[b];
+        uint32_t *row = c.table + (size_t)b * c.max_blocks;
+        uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
+        nf = clear_and_compact(c, b, key, nb * BLK, nb, row, ws, wave_tot, pool_cnt,
+                               [](uint64_t kk) { return kk != 0 && kk != 2; });
     }
     __syncthreads();
-    const int nf = ws.nfreed[b * 4 + 3];
-    const uint32_t *freed = ws.freed + (size_t)b * c.max_blocks;
-    const int lane = tid & 63, wv = tid >> 6;
-    for (int c0 = 0; c0 < nf; c0 += 256) {
-        const int i = c0 + tid;
-        const uint32_t ent = i < nf ? freed[i] : 0xffffffffu;
-        const int pool = i < nf ? (int)(ent >> 30) : 3;
-        int rank = 0;
-        for (int p = 0; p < 3; ++p) {
-            const uint64_t bal = __ballot(pool == p);
-            if (lane == 0) wave_cnt[wv][p] = __popcll(bal);
-            if (pool == p) rank = __popcll(bal & ((1ull << lane) - 1));
-        }
-        __syncthreads();
-        if (pool < 3) {
-            int before = 0;
-            for (int w = 0; w < wv; ++w) before += wave_cnt[w][pool];
-            c.free_ids[pool][base[pool] + before + rank] = ent & 0x3fffffffu;
-        }
-        __syncthreads();
-        if (tid < 3) {
-            int tot = 0;
-            for (int w = 0; w < 4; ++w) tot += wave_cnt[w][tid];
-            base[tid] += tot;
-        }
-        __syncthreads();
-    }
+    push_freed(c, b, ws.freed + (size_t)b * c.max_blocks, nf, pool_cnt, top0, sync, epoch);
 }
 
 }  // namespace
@@ -1003,10 +1037,10 @@ __global__ __launch_bounds__(256) void evict_push(kvq_cache c, EvictWs ws) {
 bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *keep_k, int q_window,
                   int recent_window, void *ws_ptr, hipStream_t s) {
     EvictWs ws(ws_ptr, c);
+    SyncWs sync(ws_ptr, c);
     hipLaunchKernelGGL(evict_keys, dim3(KEY_WGS, c.B), dim3(KEY_THREADS), 0, s, c, importance, q_window,
                        recent_window, ws);
-    hipLaunchKernelGGL(evict_select, dim3(c.B), dim3(SEL_THREADS), 0, s, c, keep_k, ws);
-    hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_select, dim3(c.B), dim3(SEL_THREADS), 0, s, c, keep_k, ws, sync);
     return hipGetLastError() == hipSuccess;
 }
 
@@ -1016,8 +1050,7 @@ bool launch_evict_tbe(const kvq_cache &c, const float *importance, const uint8_t
     hipLaunchKernelGGL(evict_tbe_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, seq_mask, r0, r_min,
                        t_keep, q_window, recent_window, ws);
     hipLaunchKernelGGL(evict_seg_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, ws);
-    hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws);
-    hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws, SyncWs(ws_ptr, c));
     return hipGetLastError() == hipSuccess;
 }
 
@@ -1027,8 +1060,7 @@ bool launch_evict_tam(const kvq_cache &c, const float *score, const int32_t *kee
     hipLaunchKernelGGL(evict_tam_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, score, keep_k, pivot_c, min_seg,
                        q_window, recent_window, ws);
     hipLaunchKernelGGL(evict_seg_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, ws);
-    hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws);
-    hipLaunchKernelGGL(evict_push, dim3(c.B), dim3(256), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws, SyncWs(ws_ptr, c));
     return hipGetLastError() == hipSuccess;
 }
 

@@ -10,16 +10,30 @@ namespace kvq {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace carve-up.  Calls are stream-ordered, so they share one buffer.
-struct AppendWs {
-    unsigned long long *pops;   // [B] each sequence's pops per pool, tagged with the
-                                // call's epoch (no clearing needed between calls)
-    static size_t bytes(const kvq_cache &c) { return align256(8L * c.B); }
-    AppendWs(void *ws, const kvq_cache &c) { pops = (unsigned long long *)ws; }
+//
+// Its first SyncWs::bytes belong to the calls that rank work across
+// workgroups in batch order (append's pops, eviction's pushes) and no other
+// call writes them: the epoch of the last such call, then one word per pool
+// and sequence, (epoch << 32) | count, of the call that wrote it.  A call
+// takes epoch + 1 (never 0), so words of earlier calls and zeroed memory
+// never pass for its own; its last workgroup stores the new epoch once every
+// word is in.  The region must be zero before the first call.
+struct SyncWs {
+    uint32_t *epoch;           // [1] epoch of the last call that ended
+    unsigned long long *words; // [3][B] per pool, per sequence
+    static size_t bytes(const kvq_cache &c) { return 256 + align256(24L * c.B); }
+    SyncWs(void *ws, const kvq_cache &c) {
+        epoch = (uint32_t *)ws;
+        words = (unsigned long long *)((char *)ws + 256);
+    }
 };
+
+// The append needs nothing beyond the sync words.
+using AppendWs = SyncWs;
 
 // The no-allocation append keeps AppendWs in a static device array of this
 // size: enough for every batch the library accepts (B <= 1024).
-constexpr size_t APPEND_SCRATCH_BYTES = 16384;
+constexpr size_t APPEND_SCRATCH_BYTES = 32768;
 // Its device address on the current device (looked up once per device), or
 // null if the lookup failed.
 void *append_scratch();
@@ -48,12 +62,12 @@ struct DecodeWs {
     static size_t slots(const kvq_cache &c) { return MAX_SPLIT_WGS + (size_t)c.B * decode_n_packs(c); }
     static size_t bytes(const kvq_cache &c) {
         const size_t S = slots(c);
-        return align256(4L * (c.B + 1)) + align256(128L * S) + align256(8192L * S) +
+        return SyncWs::bytes(c) + align256(4L * (c.B + 1)) + align256(128L * S) + align256(8192L * S) +
                align256(1024L * c.B * c.max_blocks * decode_n_packs(c));
     }
     DecodeWs(void *ws, const kvq_cache &c) {
         const size_t S = slots(c);
-        char *p = (char *)ws;
+        char *p = (char *)ws + SyncWs::bytes(c);
         pre = (int32_t *)p;   p += align256(4L * (c.B + 1));
         ml = (float *)p;      p += align256(128L * S);
         o = (float *)p;       p += align256(8192L * S);
@@ -67,8 +81,6 @@ struct EvictWs {
     uint64_t *cand;    // [B][max_blocks*16] selection keys, one word per slot
     int32_t *kcnt;     // [B][EVICT_KEY_WGS] candidates per part of a row (top-k)
     uint32_t *freed;   // [B][max_blocks] freed table entries, table order
-    int32_t *nfreed;   // [B][4] freed per pool
-    int32_t *top;      // [4] free_top before the call
     // segment-granular eviction only: candidates in position order
     uint32_t *pmap;    // [B][n_cap] (pool << 30) | slot of the candidate at a position, or ~0
     int32_t *ord;      // [B][max_blocks*16] (pool << 30) | slot of the candidates, by position
@@ -84,20 +96,17 @@ struct EvictWs {
     int32_t *segn;     // [B][2] segments (-1: the sequence is left as it is), Transition segments
     static size_t bytes(const kvq_cache &c) {
         const size_t ms = (size_t)c.max_blocks * 16, slot4 = align256(4L * c.B * ms);
-        return align256(8L * c.B * ms) + align256(4L * EVICT_KEY_WGS * c.B) + align256(4L * c.B * c.max_blocks) +
-               align256(16L * c.B) +
-               align256(16) + align256(4L * c.B * c.n_cap) + 3 * slot4 + align256(4L * c.B * (ms + 1)) +
+        return SyncWs::bytes(c) + align256(8L * c.B * ms) + align256(4L * EVICT_KEY_WGS * c.B) +
+               align256(4L * c.B * c.max_blocks) + align256(4L * c.B * c.n_cap) + 3 * slot4 + align256(4L * c.B * (ms + 1)) +
                2 * slot4 + align256(8L * c.B * ms) + slot4 + align256(8L * c.B * (ms + 1)) +
                align256(4L * c.B * (ms + 1)) + align256(8L * c.B);
     }
     EvictWs(void *ws, const kvq_cache &c) {
         const size_t ms = (size_t)c.max_blocks * 16, slot4 = align256(4L * c.B * ms);
-        char *p = (char *)ws;
+        char *p = (char *)ws + SyncWs::bytes(c);
         cand = (uint64_t *)p;     p += align256(8L * c.B * ms);
         kcnt = (int32_t *)p;      p += align256(4L * EVICT_KEY_WGS * c.B);
         freed = (uint32_t *)p;    p += align256(4L * c.B * c.max_blocks);
-        nfreed = (int32_t *)p;    p += align256(16L * c.B);
-        top = (int32_t *)p;       p += align256(16);
         pmap = (uint32_t *)p;     p += align256(4L * c.B * c.n_cap);
         ord = (int32_t *)p;       p += slot4;
         ob = (uint32_t *)p;       p += slot4;

@@ -117,7 +117,8 @@ class Cache:
         self.ws_bytes = lib().kvq_workspace_bytes(ctypes.byref(s))
         if self.ws_bytes == 0:
             raise KvqError("kvq_workspace_bytes rejected the cache geometry")
-        self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+        # zero before the first call (the sync words of append and eviction)
+        self.ws = torch.zeros(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
         off = (-self.ws.data_ptr()) % 256
         self.ws_ptr = self.ws.data_ptr() + off
 

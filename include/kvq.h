@@ -126,9 +126,15 @@ typedef struct kvq_cache {
 size_t kvq_region_bytes(int pool);
 
 /* Workspace bytes that every call below needs for this cache, so that one
- * buffer serves them all (device memory, 256-byte aligned, contents need not
- * be initialised; calls ordered on one stream may share it).  0 if the cache
- * description is rejected. */
+ * buffer serves them all (device memory, 256-byte aligned; calls ordered on
+ * one stream may share it).  0 if the cache description is rejected.
+ * Zero-fill a workspace once, before its first call; from then on its
+ * contents belong to the library (do not write it between calls).  Its
+ * first bytes hold what the append and the evictions use to rank pops and
+ * pushes across sequences in batch order within one launch: the epoch of
+ * the last such call and, per pool and sequence, a count tagged with the
+ * epoch of the call that wrote it.  Each call takes the next epoch on the
+ * device, so the calls also work when captured in a graph and replayed. */
 size_t kvq_workspace_bytes(const kvq_cache *cache);
 
 /* Workspace bytes kvq_decode_attention needs for this cache (a buffer this
@@ -160,8 +166,9 @@ kvq_status kvq_append_quantize(const kvq_cache *cache, const void *k_new, const 
  * kvq_append_quantize without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same semantics and kernels; the plan
- * buffers live in a static device array of the library (16 KiB per GPU, held
- * until the process ends), enough for every B the library accepts (<= 1024).
+ * buffers live in a static device array of the library (32 KiB per GPU, zero
+ * when the library loads, held until the process ends), enough for every B
+ * the library accepts (<= 1024).
  * A cache whose plan buffers would not fit returns KVQ_EUNSUPPORTED.  Nothing
  * is allocated or freed.  Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (concurrent streams) race and must not be
