@@ -38,9 +38,10 @@ namespace {
 
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int SEL_UNROLL = 16;  // slots a thread takes per batch
+constexpr int SEL_UNROLL = 17;  // slots a thread takes per batch (17 x 1024: rows of up to 1088 entries at once)
 constexpr int RADIX_BITS = 11;  // digit width of the radix select
 constexpr int RADIX = 1 << RADIX_BITS;
+static_assert(RADIX == EVICT_RADIX, "top-k's first-digit histograms");
 // segment eviction's selection: DROP_WGS workgroups of DROP_THREADS per
 // sequence, DROP_WAVES waves in all
 constexpr int DROP_THREADS = 256;
@@ -51,6 +52,20 @@ constexpr int TBE_RUN = 16;  // chunks of 64 positions / candidates a wave takes
 constexpr int KEY_WGS = EVICT_KEY_WGS;
 constexpr int KEY_THREADS = 256;
 constexpr int KEY_UNROLL = 8;
+
+// Grids of `per` workgroups per sequence are laid out so that all of
+// sequence b's run on the XCD that runs workgroup b of a grid of one per
+// sequence (workgroups go to the 8 XCDs round-robin by id): id = 8 per
+// (b / 8) + 8 j + b % 8 for the sequence's j-th workgroup.  What one kernel
+// writes for a sequence is then read by the next from the same L2.
+constexpr int XCDS = 8;
+inline int xcd_grid(int per, int B) { return XCDS * per * ((B + XCDS - 1) / XCDS); }
+__device__ inline bool xcd_part(int per, int B, int &b, int &j) {
+    const int id = blockIdx.x, grp = id / (XCDS * per), r = id % (XCDS * per);
+    j = r / XCDS;
+    b = grp * XCDS + r % XCDS;
+    return b < B;
+}
 
 __device__ inline uint32_t order_bits(float f) {
     uint32_t u = __float_as_uint(f);
@@ -81,72 +96,6 @@ __device__ inline int block_prefix(bool flag, int *wave_tot, int &total) {
     return before + in_wave;
 }
 
-// Clear the slots the rule drops and compact the table row (one workgroup
-// per sequence).  key holds one word per slot (0: cleared); keep(word) says
-// whether a valid slot survives.  Thread per slot: 16-lane ballots give each
-// entry's old and new masks; the entry's first slot's lane stores the new
-// mask if it changed, and parks it in that slot's word.  Then, thread per
-// entry, the entries that kept a slot are packed in order and the emptied
-// ones listed for the free-stack pushes.  Returns how many were freed;
-// pool_cnt holds them per pool.
-template <class Keep>
-__device__ inline int clear_and_compact(const kvq_cache &c, int b, uint64_t *key, int nslot, int nb,
-                                         uint32_t *row, EvictWs &ws, int *wave_tot, int *pool_cnt,
-                                         const Keep &keep) {
-    const int tid = threadIdx.x, lane = tid & 63;
-#pragma unroll 1
-    for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
-        uint32_t ent[SEL_UNROLL];
-        uint64_t kk[SEL_UNROLL];
-#pragma unroll
-        for (int u = 0; u < SEL_UNROLL; ++u) {
-            const int i = i0 + u * SEL_THREADS + tid;
-            ent[u] = i < nslot ? row[i >> 4] : 0u;
-            kk[u] = i < nslot ? key[i] : 0ull;
-        }
-#pragma unroll
-        for (int u = 0; u < SEL_UNROLL; ++u) {
-            const int i = i0 + u * SEL_THREADS + tid;
-            const bool bit = keep(kk[u]);
-            const uint32_t oldm = (uint32_t)(__ballot(kk[u] != 0) >> (lane & 48)) & 0xffffu;
-            const uint32_t newm = (uint32_t)(__ballot(bit) >> (lane & 48)) & 0xffffu;
-            if (i < nslot && (i & 15) == 0) {
-                if (newm != oldm) c.mask[ent[u] >> 30][ent[u] & 0x3fffffffu] = (uint16_t)newm;
-                key[i] = newm;
-            }
-        }
-    }
-    __syncthreads();
-
-    int kept_base = 0, freed_base = 0;
-    uint32_t *freed = ws.freed + (size_t)b * c.max_blocks;
-    for (int c0 = 0; c0 < nb; c0 += SEL_THREADS) {
-        const int e = c0 + tid;
-        const bool has = e < nb;
-        uint32_t ent = 0, newm = 0;
-        if (has) {
-            ent = row[e];
-            newm = (uint32_t)key[(size_t)e * BLK];
-        }
-        int nkept, nfreed;
-        const int kr = block_prefix(has && newm != 0, wave_tot, nkept);
-        const int fr = block_prefix(has && newm == 0, wave_tot, nfreed);
-        if (has) {
-            if (newm != 0) {
-                row[kept_base + kr] = ent;
-            } else {
-                freed[freed_base + fr] = ent;
-                atomicAdd(&pool_cnt[ent >> 30], 1);
-            }
-        }
-        kept_base += nkept;
-        freed_base += nfreed;
-        __syncthreads();
-    }
-    if (tid == 0) c.n_blocks[b] = kept_base;
-    return freed_base;
-}
-
 // The start of a compacting kernel, before any of the workgroup's work: wave
 // 0 takes the call's epoch and thread p < 3 the free-stack top of pool p
 // (both read before the workgroup's counts are published; only the last
@@ -158,22 +107,27 @@ __device__ inline uint32_t push_begin(const kvq_cache &c, const SyncWs &sync, in
     return epoch;
 }
 
+// Publish sequence b's freed count per pool (pool_cnt, complete): threads
+// 0 .. 2, after a barrier.
+__device__ inline void push_publish(const kvq_cache &c, int b, const int *pool_cnt, const SyncWs &sync,
+                                    uint32_t epoch) {
+    if (threadIdx.x < 3) {
+        wait_loads_done();   // this workgroup's reads of the tops are in
+        sync_publish(sync, c.B, b, threadIdx.x, epoch, (uint32_t)pool_cnt[threadIdx.x]);
+    }
+}
+
 // Push sequence b's freed ids (freed[0 .. nf), table order; pool_cnt per
-// pool) onto the free stacks, the sequences in batch order: publish the
-// counts, sum those of the sequences before b (wave 0), and push each id at
-// the pool's old top + that sum + its rank in table order.  The last
+// pool, already published) onto the free stacks, the sequences in batch
+// order: sum the counts of the sequences before b (wave 0) and push each id
+// at the pool's old top + that sum + its rank in table order.  The last
 // sequence raises the tops and closes the call.  top0 and epoch from
-// push_begin; every thread calls it after a barrier that follows the
-// compaction.
+// push_begin; every thread calls it, after a barrier.
 __device__ inline void push_freed(const kvq_cache &c, int b, const uint32_t *freed, int nf, const int *pool_cnt,
                                   const int *top0, const SyncWs &sync, uint32_t epoch) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     __shared__ int base[3];
     __shared__ int wave_cnt[SEL_WAVES][3];
-    if (tid < 3) {
-        wait_loads_done();
-        sync_publish(sync, c.B, b, tid, epoch, (uint32_t)pool_cnt[tid]);
-    }
     const bool last = b == c.B - 1;
     if (nf == 0 && !last) return;
     if (wv == 0) {
@@ -217,17 +171,88 @@ __device__ inline void push_freed(const kvq_cache &c, int b, const uint32_t *fre
     }
 }
 
+// Clear the slots the rule drops, compact the table row and push the freed
+// ids (one workgroup per sequence).  key holds one word per slot (0:
+// cleared); keep(word) says whether a valid slot survives.  Thread per
+// slot: 16-lane ballots give each entry's old and new masks; the entry's
+// first slot's lane stores the new mask if it changed, parks it in that
+// slot's word and, if it is 0, counts the entry as freed in its pool.  The
+// counts are published at once; then, thread per entry, the entries that
+// kept a slot are packed in order and the emptied ones listed, and the list
+// is pushed (push_freed) once the earlier sequences' counts are in.
+// pool_cnt must be zero and top0 / epoch taken (push_begin) before.  The
+// row's entries are read from row_in (the row itself, or a copy) and the
+// compacted row is written to row.
+template <class Keep>
+__device__ inline void clear_compact_push(const kvq_cache &c, int b, uint64_t *key, int nslot, int nb,
+                                          const uint32_t *row_in, uint32_t *row, EvictWs &ws, int *wave_tot,
+                                          int *pool_cnt, const int *top0, const SyncWs &sync, uint32_t epoch,
+                                          const Keep &keep) {
+    const int tid = threadIdx.x, lane = tid & 63;
+#pragma unroll 1
+    for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
+        uint32_t ent[SEL_UNROLL];
+        uint64_t kk[SEL_UNROLL];
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u) {
+            const int i = i0 + u * SEL_THREADS + tid;
+            ent[u] = i < nslot ? row_in[i >> 4] : 0u;
+            kk[u] = i < nslot ? key[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < SEL_UNROLL; ++u) {
+            const int i = i0 + u * SEL_THREADS + tid;
+            const bool bit = keep(kk[u]);
+            const uint32_t oldm = (uint32_t)(__ballot(kk[u] != 0) >> (lane & 48)) & 0xffffu;
+            const uint32_t newm = (uint32_t)(__ballot(bit) >> (lane & 48)) & 0xffffu;
+            if (i < nslot && (i & 15) == 0) {
+                if (newm != oldm) c.mask[ent[u] >> 30][ent[u] & 0x3fffffffu] = (uint16_t)newm;
+                key[i] = newm;
+                if (newm == 0) atomicAdd(&pool_cnt[ent[u] >> 30], 1);
+            }
+        }
+    }
+    __syncthreads();
+    push_publish(c, b, pool_cnt, sync, epoch);
+
+    int kept_base = 0, freed_base = 0;
+    uint32_t *freed = ws.freed + (size_t)b * c.max_blocks;
+    for (int c0 = 0; c0 < nb; c0 += SEL_THREADS) {
+        const int e = c0 + tid;
+        const bool has = e < nb;
+        uint32_t ent = 0, newm = 0;
+        if (has) {
+            ent = row_in[e];
+            newm = (uint32_t)key[(size_t)e * BLK];
+        }
+        int nkept, nfreed;
+        const int kr = block_prefix(has && newm != 0, wave_tot, nkept);
+        const int fr = block_prefix(has && newm == 0, wave_tot, nfreed);
+        if (has) {
+            if (newm != 0) row[kept_base + kr] = ent;
+            else freed[freed_base + fr] = ent;
+        }
+        kept_base += nkept;
+        freed_base += nfreed;
+        __syncthreads();
+    }
+    if (tid == 0) c.n_blocks[b] = kept_base;
+    push_freed(c, b, freed, freed_base, pool_cnt, top0, sync, epoch);
+}
+
 // One word per slot (slot s of entry e at 16 e + s), thread per slot, for
 // the slots [i_begin, i_end) of a row: 0 for a cleared slot, 1 for a valid
 // slot outside [lo, hi), else the candidate's key (a finite importance gives
 // a key >= 2^55).  UNROLL slots per thread and batch of NT threads; the
 // entry, then its mask and positions, then the importance, each level's
 // loads issued together.  Without an importance a candidate's word is 3.
-// pmap, if given, receives (pool << 30) | slot for each candidate position.
-// Returns this thread's candidate count.
+// pmap, if given, receives (pool << 30) | slot for each candidate position;
+// hist1, if given (LDS), counts the candidates by their key's top
+// RADIX_BITS bits.  Returns this thread's candidate count.
 template <int NT, int UNROLL>
 __device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const float *imp, int i_begin,
-                                int i_end, int lo, int hi, uint64_t *key, uint32_t *pmap) {
+                                int i_end, int lo, int hi, uint64_t *key, uint32_t *pmap,
+                                uint32_t *hist1 = nullptr) {
     const int tid = threadIdx.x;
     int my_cand = 0;
     for (int i0 = i_begin; i0 < i_end; i0 += NT * UNROLL) {
@@ -253,6 +278,7 @@ __device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const f
                 if (p[u] >= lo && p[u] < hi) {
                     kk = imp ? sel_key(imp[p[u]], p[u]) : 3ull;
                     ++my_cand;
+                    if (hist1) atomicAdd(&hist1[(uint32_t)(kk >> (64 - RADIX_BITS))], 1u);
                     if (pmap) pmap[p[u]] = (uint32_t)i | (ent[u] & 0xc0000000u);
                 }
             }
@@ -263,18 +289,24 @@ __device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const f
 }
 
 // Top-k, step 1: one word per slot (slot_keys), a sequence's row shared by
-// KEY_WGS workgroups (grid KEY_WGS x B) in contiguous parts; each part's
-// candidate count goes to ws.kcnt.
+// KEY_WGS workgroups (xcd_grid) in contiguous parts; each part's candidate
+// count goes to ws.kcnt and its histogram of the candidates' first radix
+// digit to ws.khist (the select's first pass, spread over the parts).
 __global__ __launch_bounds__(KEY_THREADS) void evict_keys(kvq_cache c, const float *importance, int q_window,
                                                           int recent_window, EvictWs ws) {
-    const int part = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int tid = threadIdx.x;
+    int b, part;
+    if (!xcd_part(KEY_WGS, c.B, b, part)) return;
     const int nslot = c.n_blocks[b] * BLK;
     const int share = (nslot + KEY_WGS - 1) / KEY_WGS;
     const int i0 = min(nslot, part * share), i1 = min(nslot, i0 + share);
     const int lo = q_window, hi = c.seq_len[b] - recent_window;
+    __shared__ uint32_t hist1[RADIX];
+    for (int i = tid; i < RADIX; i += KEY_THREADS) hist1[i] = 0;
+    __syncthreads();
     int my_cand = slot_keys<KEY_THREADS, KEY_UNROLL>(c, c.table + (size_t)b * c.max_blocks,
                                                      importance + (size_t)b * c.n_cap, i0, i1, lo, hi,
-                                                     ws.cand + (size_t)b * c.max_blocks * BLK, nullptr);
+                                                     ws.cand + (size_t)b * c.max_blocks * BLK, nullptr, hist1);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) my_cand += __shfl_xor(my_cand, off);
     __shared__ int wsum[KEY_THREADS / 64];
@@ -286,58 +318,53 @@ __global__ __launch_bounds__(KEY_THREADS) void evict_keys(kvq_cache c, const flo
         for (int w = 0; w < KEY_THREADS / 64; ++w) n += wsum[w];
         ws.kcnt[b * KEY_WGS + part] = n;
     }
+    uint32_t *h = ws.khist + ((size_t)b * KEY_WGS + part) * RADIX;
+    for (int i = tid; i < RADIX; i += KEY_THREADS) h[i] = hist1[i];
 }
 
-// Top-k, step 2 (one workgroup per sequence): the k-th largest key, then
-// the losers cleared and the row compacted.
-__global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const int32_t *keep_k, EvictWs ws,
-                                                           SyncWs sync) {
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
-    __shared__ int top0[3];
-    const uint32_t epoch = push_begin(c, sync, top0);
-    const int nb = c.n_blocks[b];
-    const int nslot = nb * BLK;
-    uint32_t *row = c.table + (size_t)b * c.max_blocks;
-    uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
-
-    __shared__ uint32_t hist[RADIX];
-    __shared__ int s_digit, s_cum;
-    __shared__ int wave_tot[SEL_WAVES];
-    __shared__ int pool_cnt[4];
-    if (tid < 4) pool_cnt[tid] = 0;
-    __syncthreads();
-
-    // 1. the candidates counted by evict_keys
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j < KEY_WGS; ++j) n += ws.kcnt[b * KEY_WGS + j];
-    const int k = max(keep_k[b], 0);
-    const bool evicting = n > k;
-
-    // 2. radix-select the k-th largest key, RADIX_BITS at a time from the
-    //    top (the last digit is narrower), stopping as soon as the boundary
-    //    digit's whole bin is kept.  Wide digits spread the keys, whose top
-    //    bits (sign and exponent of the importance) take few values, over
-    //    many bins: fewer passes and fewer same-bin atomics.
+// Top-k, step 2, on the row's slot keys at `keys` (in memory, or a copy in
+// LDS): radix-select the k-th largest candidate key, RADIX_BITS at a time
+// from the top, stopping as soon as the boundary digit's whole bin is kept;
+// then clear the losers, compact the table row and push the freed ids
+// (clear_compact_push).  Wide digits spread the keys, whose top bits (sign
+// and exponent of the importance) take few values, over many bins: fewer
+// passes and fewer same-bin atomics.  The digits split each 32-bit half of
+// the key as 11 + 11 + 10 bits.
+__device__ __attribute__((always_inline)) inline void select_and_compact(
+    const kvq_cache &c, int b, uint64_t *keys, int nslot, int nb, const uint32_t *row_in, uint32_t *row,
+    EvictWs &ws, int k,
+    bool evicting, uint32_t *hist, int *s_digit, int *s_cum, int *wave_tot, int *pool_cnt, const int *top0,
+    const SyncWs &sync, uint32_t epoch) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     uint64_t thr = 0;
     int thr_shift = 0;
     if (evicting && k > 0) {
         uint64_t prefix = 0;
         uint32_t need = (uint32_t)k;
         for (int top = 64;;) {
-            const int width = top < RADIX_BITS ? top : RADIX_BITS;
+            const int width = min(RADIX_BITS, top > 32 ? top - 32 : top);
             const int shift = top - width;
             const uint32_t dmask = (1u << width) - 1u;
-            for (int i = tid; i < RADIX; i += SEL_THREADS) hist[i] = 0;
+            if (top == 64) {
+                // the first digit: the parts' histograms from evict_keys
+                const uint32_t *kh = ws.khist + (size_t)b * KEY_WGS * RADIX;
+                for (int i = tid; i < RADIX; i += SEL_THREADS) {
+                    uint32_t h = 0;
+#pragma unroll
+                    for (int j = 0; j < KEY_WGS; ++j) h += kh[j * RADIX + i];
+                    hist[i] = h;
+                }
+            } else {
+                for (int i = tid; i < RADIX; i += SEL_THREADS) hist[i] = 0;
+            }
             __syncthreads();
             const uint64_t hmask = top == 64 ? 0ull : (~0ull << top);
-            for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
+            for (int i0 = 0; i0 < nslot && top < 64; i0 += SEL_THREADS * SEL_UNROLL) {
                 uint64_t kk[SEL_UNROLL];
 #pragma unroll
                 for (int u = 0; u < SEL_UNROLL; ++u) {
                     const int i = i0 + u * SEL_THREADS + tid;
-                    kk[u] = i < nslot ? key[i] : 0ull;
+                    kk[u] = i < nslot ? keys[i] : 0ull;
                 }
 #pragma unroll
                 for (int u = 0; u < SEL_UNROLL; ++u)
@@ -366,13 +393,13 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const i
                         if (cum + h >= need) break;
                         cum += h;
                     }
-                    s_digit = RADIX - 1 - BPL * lane - j;
-                    s_cum = (int)cum;
+                    *s_digit = RADIX - 1 - BPL * lane - j;
+                    *s_cum = (int)cum;
                 }
             }
             __syncthreads();
-            const int dgt = s_digit;
-            need -= (uint32_t)s_cum;
+            const int dgt = *s_digit;
+            need -= (uint32_t)*s_cum;
             prefix |= (uint64_t)dgt << shift;
             const bool done = hist[dgt] == need || shift == 0;
             __syncthreads();
@@ -384,14 +411,68 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const i
             top = shift;
         }
     }
+    clear_compact_push(c, b, keys, nslot, nb, row_in, row, ws, wave_tot, pool_cnt, top0, sync, epoch,
+                       [&](uint64_t kk) {
+        return kk != 0 && !(evicting && kk > 1 && !(k > 0 && (kk >> thr_shift) >= (thr >> thr_shift)));
+    });
+}
 
-    // 3. clear losers, compact the table row, list freed entries, push them
-    const int nf = clear_and_compact(
-        c, b, key, nslot, nb, row, ws, wave_tot, pool_cnt, [&](uint64_t kk) {
-            return kk != 0 && !(evicting && kk > 1 && !(k > 0 && (kk >> thr_shift) >= (thr >> thr_shift)));
-        });
-    __syncthreads();
-    push_freed(c, b, ws.freed + (size_t)b * c.max_blocks, nf, pool_cnt, top0, sync, epoch);
+// Rows of up to this many slots (one batch of the workgroup) are selected
+// from a copy of their keys in LDS (136 KiB); longer rows from the keys in
+// memory.
+constexpr int SEL_LDS_SLOTS = SEL_THREADS * SEL_UNROLL;
+
+// Top-k, step 2 (one workgroup per sequence): the k-th largest key, then
+// the losers cleared, the row compacted and the freed ids pushed.
+__global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const int32_t *keep_k, EvictWs ws,
+                                                           SyncWs sync) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    __shared__ int top0[3];
+    const uint32_t epoch = push_begin(c, sync, top0);
+    const int nb = c.n_blocks[b];
+    const int nslot = nb * BLK;
+    uint32_t *row = c.table + (size_t)b * c.max_blocks;
+    uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
+
+    __shared__ uint64_t lkeys[SEL_LDS_SLOTS];
+    __shared__ uint32_t lrow[SEL_LDS_SLOTS / BLK];
+    __shared__ uint32_t hist[RADIX];
+    __shared__ int s_digit, s_cum;
+    __shared__ int wave_tot[SEL_WAVES];
+    __shared__ int pool_cnt[4];
+    if (tid < 4) pool_cnt[tid] = 0;
+
+    // 1. the candidates counted by evict_keys
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < KEY_WGS; ++j) n += ws.kcnt[b * KEY_WGS + j];
+    const int k = max(keep_k[b], 0);
+    const bool evicting = n > k;
+
+    // 2, 3. select, clear, compact, push
+    if (nslot <= SEL_LDS_SLOTS) {
+        for (int i0 = 0; i0 < nslot; i0 += SEL_THREADS * SEL_UNROLL) {
+            uint64_t kk[SEL_UNROLL];
+#pragma unroll
+            for (int u = 0; u < SEL_UNROLL; ++u) {
+                const int i = i0 + u * SEL_THREADS + tid;
+                kk[u] = i < nslot ? key[i] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < SEL_UNROLL; ++u) {
+                const int i = i0 + u * SEL_THREADS + tid;
+                if (i < nslot) lkeys[i] = kk[u];
+            }
+        }
+        for (int e = tid; e < nb; e += SEL_THREADS) lrow[e] = row[e];
+        __syncthreads();
+        select_and_compact(c, b, lkeys, nslot, nb, lrow, row, ws, k, evicting, hist, &s_digit, &s_cum, wave_tot,
+                           pool_cnt, top0, sync, epoch);
+    } else {
+        __syncthreads();
+        select_and_compact(c, b, key, nslot, nb, row, row, ws, k, evicting, hist, &s_digit, &s_cum, wave_tot,
+                           pool_cnt, top0, sync, epoch);
+    }
 }
 
 // Exclusive prefix sum over the waves of a value each wave holds
@@ -972,15 +1053,16 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
     if (tid == 0) ws.segn[2 * b] = nseg;
 }
 
-// evict_seg_drop: DROP_WGS workgroups per sequence, one wave per segment
-// (segments gw, gw + DROP_WAVES, ... for the sequence's wave gw): each lane
+// evict_seg_drop: DROP_WGS workgroups per sequence (xcd_grid), one wave per
+// segment (segments gw, gw + DROP_WAVES, ... for the sequence's wave gw): each lane
 // loads the bounds and retention of one of the wave's next 64 segments,
 // then the wave takes them in turn (tbe_segment_any).  Spreading a
 // sequence's segments over many workgroups puts the selection, which is
 // bound by instruction issue, on every compute unit.
 __global__ __launch_bounds__(DROP_THREADS) void evict_seg_drop(kvq_cache c, EvictWs ws) {
-    const int b = blockIdx.x / DROP_WGS;
-    const int gw = (blockIdx.x % DROP_WGS) * (DROP_THREADS / 64) + (threadIdx.x >> 6);
+    int b, j;
+    if (!xcd_part(DROP_WGS, c.B, b, j)) return;
+    const int gw = j * (DROP_THREADS / 64) + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const size_t ms = (size_t)c.max_blocks * BLK;
     uint64_t *key = ws.cand + (size_t)b * ms;
@@ -1020,16 +1102,17 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_seg_compact(kvq_cache c, Ev
     const uint32_t epoch = push_begin(c, sync, top0);
     if (tid < 4) pool_cnt[tid] = 0;
     __syncthreads();
-    int nf = 0;
     if (ws.segn[2 * b] >= 0) {
         const int nb = c.n_blocks[b];
         uint32_t *row = c.table + (size_t)b * c.max_blocks;
         uint64_t *key = ws.cand + (size_t)b * c.max_blocks * BLK;
-        nf = clear_and_compact(c, b, key, nb * BLK, nb, row, ws, wave_tot, pool_cnt,
-                               [](uint64_t kk) { return kk != 0 && kk != 2; });
+        clear_compact_push(c, b, key, nb * BLK, nb, row, row, ws, wave_tot, pool_cnt, top0, sync, epoch,
+                           [](uint64_t kk) { return kk != 0 && kk != 2; });
+    } else {
+        // nothing freed (pool_cnt zero)
+        push_publish(c, b, pool_cnt, sync, epoch);
+        push_freed(c, b, nullptr, 0, pool_cnt, top0, sync, epoch);
     }
-    __syncthreads();
-    push_freed(c, b, ws.freed + (size_t)b * c.max_blocks, nf, pool_cnt, top0, sync, epoch);
 }
 
 }  // namespace
@@ -1038,7 +1121,7 @@ bool launch_evict(const kvq_cache &c, const float *importance, const int32_t *ke
                   int recent_window, void *ws_ptr, hipStream_t s) {
     EvictWs ws(ws_ptr, c);
     SyncWs sync(ws_ptr, c);
-    hipLaunchKernelGGL(evict_keys, dim3(KEY_WGS, c.B), dim3(KEY_THREADS), 0, s, c, importance, q_window,
+    hipLaunchKernelGGL(evict_keys, dim3(xcd_grid(KEY_WGS, c.B)), dim3(KEY_THREADS), 0, s, c, importance, q_window,
                        recent_window, ws);
     hipLaunchKernelGGL(evict_select, dim3(c.B), dim3(SEL_THREADS), 0, s, c, keep_k, ws, sync);
     return hipGetLastError() == hipSuccess;
@@ -1049,7 +1132,7 @@ bool launch_evict_tbe(const kvq_cache &c, const float *importance, const uint8_t
     EvictWs ws(ws_ptr, c);
     hipLaunchKernelGGL(evict_tbe_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, importance, seq_mask, r0, r_min,
                        t_keep, q_window, recent_window, ws);
-    hipLaunchKernelGGL(evict_seg_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_seg_drop, dim3(xcd_grid(DROP_WGS, c.B)), dim3(DROP_THREADS), 0, s, c, ws);
     hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws, SyncWs(ws_ptr, c));
     return hipGetLastError() == hipSuccess;
 }
@@ -1059,7 +1142,7 @@ bool launch_evict_tam(const kvq_cache &c, const float *score, const int32_t *kee
     EvictWs ws(ws_ptr, c);
     hipLaunchKernelGGL(evict_tam_prep, dim3(c.B), dim3(SEL_THREADS), 0, s, c, score, keep_k, pivot_c, min_seg,
                        q_window, recent_window, ws);
-    hipLaunchKernelGGL(evict_seg_drop, dim3(c.B * DROP_WGS), dim3(DROP_THREADS), 0, s, c, ws);
+    hipLaunchKernelGGL(evict_seg_drop, dim3(xcd_grid(DROP_WGS, c.B)), dim3(DROP_THREADS), 0, s, c, ws);
     hipLaunchKernelGGL(evict_seg_compact, dim3(c.B), dim3(SEL_THREADS), 0, s, c, ws, SyncWs(ws_ptr, c));
     return hipGetLastError() == hipSuccess;
 }

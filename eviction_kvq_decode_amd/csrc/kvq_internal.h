@@ -76,10 +76,12 @@ struct DecodeWs {
 };
 
 constexpr int EVICT_KEY_WGS = 8;   // workgroups per sequence building top-k's slot keys
+constexpr int EVICT_RADIX = 2048;  // bins of top-k's radix select (11-bit digits)
 
 struct EvictWs {
     uint64_t *cand;    // [B][max_blocks*16] selection keys, one word per slot
     int32_t *kcnt;     // [B][EVICT_KEY_WGS] candidates per part of a row (top-k)
+    uint32_t *khist;   // [B][EVICT_KEY_WGS][EVICT_RADIX] per part, candidates by their key's top 11 bits
     uint32_t *freed;   // [B][max_blocks] freed table entries, table order
     // segment-granular eviction only: candidates in position order
     uint32_t *pmap;    // [B][n_cap] (pool << 30) | slot of the candidate at a position, or ~0
@@ -97,6 +99,7 @@ struct EvictWs {
     static size_t bytes(const kvq_cache &c) {
         const size_t ms = (size_t)c.max_blocks * 16, slot4 = align256(4L * c.B * ms);
         return SyncWs::bytes(c) + align256(8L * c.B * ms) + align256(4L * EVICT_KEY_WGS * c.B) +
+               align256(4L * EVICT_KEY_WGS * EVICT_RADIX * c.B) +
                align256(4L * c.B * c.max_blocks) + align256(4L * c.B * c.n_cap) + 3 * slot4 + align256(4L * c.B * (ms + 1)) +
                2 * slot4 + align256(8L * c.B * ms) + slot4 + align256(8L * c.B * (ms + 1)) +
                align256(4L * c.B * (ms + 1)) + align256(8L * c.B);
@@ -106,6 +109,7 @@ struct EvictWs {
         char *p = (char *)ws + SyncWs::bytes(c);
         cand = (uint64_t *)p;     p += align256(8L * c.B * ms);
         kcnt = (int32_t *)p;      p += align256(4L * EVICT_KEY_WGS * c.B);
+        khist = (uint32_t *)p;    p += align256(4L * EVICT_KEY_WGS * EVICT_RADIX * c.B);
         freed = (uint32_t *)p;    p += align256(4L * c.B * c.max_blocks);
         pmap = (uint32_t *)p;     p += align256(4L * c.B * c.n_cap);
         ord = (int32_t *)p;       p += slot4;

@@ -27,7 +27,7 @@ def test_graph_replays_match_eager(noalloc):
 
     from eviction_kvq_decode_amd import kvq
 
-    w = wl.scaled(wl.WORKLOADS["ct_loop"], B=3, n_min=600, n_max=600, keep=300, q_window=32,
+    w = wl.scaled(wl.WORKLOADS["ct_loop"], B=16, n_min=600, n_max=600, keep=300, q_window=32,
                   recent_window=64, period=16, loop_steps=64, extra_steps=64 + 16)
     log(f"[gpu graph] noalloc={noalloc} B={w.B} Hq={w.Hq} Hkv={w.Hkv} cached={w.n_min} "
         f"budget={w.keep} period={w.period} steps={w.loop_steps}")
