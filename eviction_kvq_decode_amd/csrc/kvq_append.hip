@@ -49,7 +49,7 @@ __device__ inline Plan plan_slot(const kvq_cache &c, int b, int tag, int *first,
     __syncthreads();
     const int nb = c.n_blocks[b];
     const uint32_t *row = c.table + (size_t)b * c.max_blocks;
-    const uint16_t *mask = c.mask[tag];
+    const uint16_t *mask = pool_sel(c.mask, tag);
     for (int base = 0; base < nb; base += PLAN_THREADS * PLAN_UNROLL) {
         uint32_t ent[PLAN_UNROLL];
         uint32_t m[PLAN_UNROLL];
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const 
                 if (pl.need >= 0) {
                     const int top = tops[pl.need], rank = cnt[pl.need];
                     if (rank >= top) *c.status = KVQ_ENOSPC;
-                    else id = (int)c.free_ids[pl.need][top - 1 - rank];
+                    else id = (int)pool_sel(c.free_ids, pl.need)[top - 1 - rank];
                 }
                 s_id = id;
             }
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const 
             k_two = reinterpret_cast<const uint32_t *>(k_new + row_off)[lane];
             v_two = reinterpret_cast<const uint32_t *>(v_new + row_off)[lane];
         }
-        write_head(c, region_ptr(c.kv[pool], id, c.Hkv, h, pool), pool, slot, k_two, v_two, kcode[wave],
+        write_head(c, region_ptr(pool_sel(c.kv, pool), id, c.Hkv, h, pool), pool, slot, k_two, v_two, kcode[wave],
                    vcode[wave]);
     }
     if (tid == 0) {
@@ -333,12 +333,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const 
             const int nb = c.n_blocks[b];
             c.table[(size_t)b * c.max_blocks + nb] = ((uint32_t)pool << 30) | id;
             c.n_blocks[b] = nb + 1;
-            c.mask[pool][id] = 1;
+            pool_sel(c.mask, pool)[id] = 1;
         } else {
-            c.mask[pool][id] = (uint16_t)(c.mask[pool][id] | (1u << slot));
+            pool_sel(c.mask, pool)[id] = (uint16_t)(pool_sel(c.mask, pool)[id] | (1u << slot));
         }
         const int p = c.seq_len[b];
-        c.pos[pool][(size_t)id * BLK + slot] = p;
+        pool_sel(c.pos, pool)[(size_t)id * BLK + slot] = p;
         c.seq_len[b] = p + 1;
     }
 }

@@ -664,7 +664,7 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, floa
             uint32_t ent = 0, m = 0;
             if (k < cnt) {
                 ent = c.table[(size_t)b * c.max_blocks + base + k];
-                m = c.mask[ent >> 30][ent & 0x3fffffffu];
+                m = pool_sel(c.mask, ent >> 30)[ent & 0x3fffffffu];
             }
             const uint64_t bal = __ballot(m != 0);
             if (lane == 0) sh.wcnt[wave] = __popcll(bal);
@@ -1000,8 +1000,8 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
                     const uint32_t ent = c.table[(size_t)b * c.max_blocks + e0 + q];
                     const int pool = (int)(ent >> 30);
                     const uint32_t id = ent & 0x3fffffffu;
-                    valid[q] = (c.mask[pool][id] >> t) & 1u;
-                    pos[q] = c.pos[pool][(size_t)id * BLK + t];
+                    valid[q] = (pool_sel(c.mask, pool)[id] >> t) & 1u;
+                    pos[q] = pool_sel(c.pos, pool)[(size_t)id * BLK + t];
                 }
                 // a position outside the row stride (a corrupt cache) is skipped
                 if (pos[q] < 0 || pos[q] >= c.n_cap) valid[q] = false;

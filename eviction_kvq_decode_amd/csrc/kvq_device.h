@@ -55,6 +55,15 @@ __device__ inline uint8_t *region_ptr(uint8_t *base, uint32_t id, int Hkv, int h
     return base + ((long)id * Hkv + h) * region_bytes_of(pool);
 }
 
+// One of a cache's three per-pool pointers for a pool index held in a
+// vector register: a select among the three (kept in scalar registers), not
+// an indexed read of the kernel-argument array, which costs a dependent
+// memory load.
+template <class T>
+__device__ inline T *pool_sel(T *const (&a)[3], uint32_t pool) {
+    return pool == 0 ? a[0] : (pool == 1 ? a[1] : a[2]);
+}
+
 __device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 __device__ inline uint16_t f2h_rn(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 

@@ -67,6 +67,15 @@ __device__ inline bool xcd_part(int per, int B, int &b, int &j) {
     return b < B;
 }
 
+// Batched loads: element i of a[0 .. n) for i < n, else dflt, loaded from
+// the clamped index (n >= 1) so that the load has no branch around it and
+// a thread's loads of one batch are all issued before the first wait.
+template <class T>
+__device__ inline T ld_clamped(const T *a, int i, int n, T dflt) {
+    const T v = a[min(i, n - 1)];
+    return i < n ? v : dflt;
+}
+
 __device__ inline uint32_t order_bits(float f) {
     uint32_t u = __float_as_uint(f);
     if (f == 0.0f) u = 0u;  // -0 counts as +0
@@ -159,7 +168,7 @@ __device__ inline void push_freed(const kvq_cache &c, int b, const uint32_t *fre
         if (pool < 3) {
             int before = 0;
             for (int w = 0; w < wv; ++w) before += wave_cnt[w][pool];
-            c.free_ids[pool][base[pool] + before + rank] = ent & 0x3fffffffu;
+            pool_sel(c.free_ids, pool)[base[pool] + before + rank] = ent & 0x3fffffffu;
         }
         __syncthreads();
         if (tid < 3) {
@@ -196,8 +205,8 @@ __device__ inline void clear_compact_push(const kvq_cache &c, int b, uint64_t *k
 #pragma unroll
         for (int u = 0; u < SEL_UNROLL; ++u) {
             const int i = i0 + u * SEL_THREADS + tid;
-            ent[u] = i < nslot ? row_in[i >> 4] : 0u;
-            kk[u] = i < nslot ? key[i] : 0ull;
+            ent[u] = ld_clamped(row_in, i >> 4, (nslot + BLK - 1) >> 4, 0u);
+            kk[u] = ld_clamped(key, i, nslot, (uint64_t)0);
         }
 #pragma unroll
         for (int u = 0; u < SEL_UNROLL; ++u) {
@@ -206,7 +215,7 @@ __device__ inline void clear_compact_push(const kvq_cache &c, int b, uint64_t *k
             const uint32_t oldm = (uint32_t)(__ballot(kk[u] != 0) >> (lane & 48)) & 0xffffu;
             const uint32_t newm = (uint32_t)(__ballot(bit) >> (lane & 48)) & 0xffffu;
             if (i < nslot && (i & 15) == 0) {
-                if (newm != oldm) c.mask[ent[u] >> 30][ent[u] & 0x3fffffffu] = (uint16_t)newm;
+                if (newm != oldm) pool_sel(c.mask, ent[u] >> 30)[ent[u] & 0x3fffffffu] = (uint16_t)newm;
                 key[i] = newm;
                 if (newm == 0) atomicAdd(&pool_cnt[ent[u] >> 30], 1);
             }
@@ -258,25 +267,32 @@ __device__ inline int slot_keys(const kvq_cache &c, const uint32_t *row, const f
     for (int i0 = i_begin; i0 < i_end; i0 += NT * UNROLL) {
         uint32_t ent[UNROLL], m[UNROLL];
         int p[UNROLL];
+        // every level's loads unconditional (clamped slot, clamped
+        // position), so that each level is issued as one batch
+        float f[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int i = i0 + u * NT + tid;
-            ent[u] = i < i_end ? row[i >> 4] : 0u;
+            const int i = min(i0 + u * NT + tid, i_end - 1);
+            ent[u] = row[i >> 4];
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int i = i0 + u * NT + tid;
-            m[u] = i < i_end ? c.mask[ent[u] >> 30][ent[u] & 0x3fffffffu] : 0u;
-            p[u] = i < i_end ? c.pos[ent[u] >> 30][(size_t)(ent[u] & 0x3fffffffu) * BLK + (i & 15)] : -1;
+            const int i = min(i0 + u * NT + tid, i_end - 1);
+            m[u] = pool_sel(c.mask, ent[u] >> 30)[ent[u] & 0x3fffffffu];
+            p[u] = pool_sel(c.pos, ent[u] >> 30)[(size_t)(ent[u] & 0x3fffffffu) * BLK + (i & 15)];
+        }
+        if (imp) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) f[u] = imp[min(max(p[u], 0), c.n_cap - 1)];
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int i = i0 + u * NT + tid;
             uint64_t kk = 0;
-            if ((m[u] >> (i & 15)) & 1u) {
+            if (i < i_end && ((m[u] >> (i & 15)) & 1u)) {
                 kk = 1;
                 if (p[u] >= lo && p[u] < hi) {
-                    kk = imp ? sel_key(imp[p[u]], p[u]) : 3ull;
+                    kk = imp ? sel_key(f[u], p[u]) : 3ull;
                     ++my_cand;
                     if (hist1) atomicAdd(&hist1[(uint32_t)(kk >> (64 - RADIX_BITS))], 1u);
                     if (pmap) pmap[p[u]] = (uint32_t)i | (ent[u] & 0xc0000000u);
@@ -364,7 +380,7 @@ __device__ __attribute__((always_inline)) inline void select_and_compact(
 #pragma unroll
                 for (int u = 0; u < SEL_UNROLL; ++u) {
                     const int i = i0 + u * SEL_THREADS + tid;
-                    kk[u] = i < nslot ? keys[i] : 0ull;
+                    kk[u] = ld_clamped(keys, i, nslot, (uint64_t)0);
                 }
 #pragma unroll
                 for (int u = 0; u < SEL_UNROLL; ++u)
@@ -456,7 +472,7 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select(kvq_cache c, const i
 #pragma unroll
             for (int u = 0; u < SEL_UNROLL; ++u) {
                 const int i = i0 + u * SEL_THREADS + tid;
-                kk[u] = i < nslot ? key[i] : 0ull;
+                kk[u] = ld_clamped(key, i, nslot, (uint64_t)0);
             }
 #pragma unroll
             for (int u = 0; u < SEL_UNROLL; ++u) {
@@ -741,8 +757,8 @@ __device__ inline SegOrder seg_order(const kvq_cache &c, int b, const float *val
 #pragma unroll
         for (int u = 0; u < TBE_RUN; ++u) {
             const int p = wb + 64 * u + lane;
-            v[u] = p < hi ? pmap[p] : 0xffffffffu;
-            im[u] = p < hi ? val[p] : 0.0f;
+            v[u] = ld_clamped(pmap, p, hi, 0xffffffffu);
+            im[u] = ld_clamped(val, p, hi, 0.0f);
         }
         int cnt = 0;
 #pragma unroll
@@ -779,7 +795,8 @@ __device__ inline SegOrder seg_order(const kvq_cache &c, int b, const float *val
 #pragma unroll
         for (int u = 0; u < TBE_RUN; ++u) {
             const int k = wb + 64 * u + lane;
-            pool[u] = k < n ? (int)((uint32_t)ord[k] >> 30) : -1;
+            const int32_t o = ld_clamped(ord, k, n, 0);
+            pool[u] = k < n ? (int)((uint32_t)o >> 30) : -1;
         }
         const int before0 = wb > 0 && wb <= n ? (int)((uint32_t)ord[wb - 1] >> 30) : -1;
         uint32_t stm = 0;  // bit u: candidate of chunk u starts a run
