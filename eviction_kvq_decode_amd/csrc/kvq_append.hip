@@ -30,43 +30,42 @@ constexpr int PLAN_THREADS = 512;
 constexpr int PLAN_UNROLL = 4;
 
 // The plan of sequence b: -2 nothing to do (tag none, or the sequence cannot
-// be served: status set), -1 reuse (entry, slot), p >= 0 pop a block of
-// pool p.  The workgroup scans the table in rounds; each thread issues
-// PLAN_UNROLL independent loads per round so the dependent table -> mask
-// chain overlaps, and the first entry of the tag with a free slot wins.
+// be served: status set), -1 reuse (entry, slot; m the entry's mask), p >= 0
+// pop a block of pool p.  nb and len: the sequence's table length and
+// seq_len, read once here for the metadata update.  The workgroup scans the
+// table in rounds; each thread issues PLAN_UNROLL independent loads per
+// round (unconditional, from clamped indices, so that they go out as one
+// batch and the dependent table -> mask chain overlaps), and the first
+// entry of the tag with a free slot wins.
 struct Plan {
     int need;
     uint32_t entry;
     int slot;
+    uint32_t m;
+    int nb, len;
 };
 __device__ inline Plan plan_slot(const kvq_cache &c, int b, int tag, int *first, Plan *sh_plan) {
     const int tid = threadIdx.x;
-    if (tag == TAG_NONE || tag > 2 || c.seq_len[b] >= c.n_cap) {
+    const int len = c.seq_len[b], nb = c.n_blocks[b];
+    if (tag == TAG_NONE || tag > 2 || len >= c.n_cap) {
         if (tid == 0 && tag != TAG_NONE) *c.status = tag > 2 ? KVQ_EINVAL : KVQ_ENOSPC;
-        return Plan{-2, 0u, 0};
+        return Plan{-2, 0u, 0, 0u, nb, len};
     }
     if (tid == 0) *first = INT_MAX;
     __syncthreads();
-    const int nb = c.n_blocks[b];
     const uint32_t *row = c.table + (size_t)b * c.max_blocks;
-    const uint16_t *mask = pool_sel(c.mask, tag);
     for (int base = 0; base < nb; base += PLAN_THREADS * PLAN_UNROLL) {
         uint32_t ent[PLAN_UNROLL];
         uint32_t m[PLAN_UNROLL];
 #pragma unroll
-        for (int u = 0; u < PLAN_UNROLL; ++u) {
-            const int e = base + u * PLAN_THREADS + tid;
-            ent[u] = e < nb ? row[e] : 0xffffffffu;
-        }
+        for (int u = 0; u < PLAN_UNROLL; ++u) ent[u] = row[min(base + u * PLAN_THREADS + tid, nb - 1)];
+#pragma unroll
+        for (int u = 0; u < PLAN_UNROLL; ++u) m[u] = pool_sel(c.mask, ent[u] >> 30)[ent[u] & 0x3fffffffu];
         int mine = INT_MAX;
 #pragma unroll
         for (int u = 0; u < PLAN_UNROLL; ++u) {
             const int e = base + u * PLAN_THREADS + tid;
-            m[u] = 0xffffu;
-            if (e < nb && (int)(ent[u] >> 30) == tag) {
-                m[u] = mask[ent[u] & 0x3fffffffu];
-                if (m[u] != 0xffffu) mine = min(mine, e);
-            }
+            if (e < nb && (int)(ent[u] >> 30) == tag && m[u] != 0xffffu) mine = min(mine, e);
         }
         if (mine != INT_MAX) atomicMin(first, mine);
         __syncthreads();
@@ -75,7 +74,8 @@ __device__ inline Plan plan_slot(const kvq_cache &c, int b, int tag, int *first,
             // the thread holding the first free entry passes it on
 #pragma unroll
             for (int u = 0; u < PLAN_UNROLL; ++u)
-                if (base + u * PLAN_THREADS + tid == f) *sh_plan = Plan{-1, ent[u], __builtin_ctz(~m[u])};
+                if (base + u * PLAN_THREADS + tid == f)
+                    *sh_plan = Plan{-1, ent[u], __builtin_ctz(~m[u]), m[u], nb, len};
             __syncthreads();
             return *sh_plan;
         }
@@ -85,9 +85,9 @@ __device__ inline Plan plan_slot(const kvq_cache &c, int b, int tag, int *first,
     }
     if (nb >= c.max_blocks) {
         if (tid == 0) *c.status = KVQ_ENOSPC;
-        return Plan{-2, 0u, 0};
+        return Plan{-2, 0u, 0, 0u, nb, len};
     }
-    return Plan{tag, 0u, 0};
+    return Plan{tag, 0u, 0, 0u, nb, len};
 }
 
 // Group-quantise one 128-channel fp16 row held two channels per lane
@@ -223,22 +223,26 @@ __device__ inline void write_head(const kvq_cache &c, uint8_t *reg, int pool, in
         for (int i = 0; i < per; ++i) w |= (uint32_t)kcode[lane * per + i] << (i * bits);
         reinterpret_cast<uint32_t *>(reg + slot * 16 * bits)[lane] = w;
     }
-    // V: the 16*bits dwords holding this token's codes; read-modify-write,
-    // other tokens' codes in the same dwords are preserved.
+    // V: the 16*bits dwords holding this token's codes, whose other bits
+    // are other tokens' codes: the token's fields are cleared and set with
+    // two atomics per dword (in that order: same lane, same address), which
+    // need no read back.
     uint8_t *vbase = reg + 256 * bits;
     const int tiles_per_dword = 8 / bits;
     for (int qd = lane; qd < 16 * bits; qd += 64) {
         const int j = qd & 15, w = qd >> 4;
         const int d_first = 16 * (w * tiles_per_dword) + j;
         uint32_t *dw = reinterpret_cast<uint32_t *>(vbase + v_dword_byte(bits, slot, d_first));
-        uint32_t val = *dw;
         const uint32_t lvmask = (1u << bits) - 1;
+        uint32_t clr = 0, set = 0;
         for (int m = 0; m < tiles_per_dword; ++m) {
             const int d = 16 * (w * tiles_per_dword + m) + j;
             const int sh = v_code_slot(bits, slot, d) * bits;
-            val = (val & ~(lvmask << sh)) | ((uint32_t)vcode[d] << sh);
+            clr |= lvmask << sh;
+            set |= (uint32_t)vcode[d] << sh;
         }
-        *dw = val;
+        __hip_atomic_fetch_and(dw, ~clr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(dw, set, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // the buffers are reused by the wave's next head
     wave_sync();
@@ -330,16 +334,14 @@ __global__ __launch_bounds__(PLAN_THREADS) void append_token(kvq_cache c, const 
     }
     if (tid == 0) {
         if (fresh) {
-            const int nb = c.n_blocks[b];
-            c.table[(size_t)b * c.max_blocks + nb] = ((uint32_t)pool << 30) | id;
-            c.n_blocks[b] = nb + 1;
+            c.table[(size_t)b * c.max_blocks + pl.nb] = ((uint32_t)pool << 30) | id;
+            c.n_blocks[b] = pl.nb + 1;
             pool_sel(c.mask, pool)[id] = 1;
         } else {
-            pool_sel(c.mask, pool)[id] = (uint16_t)(pool_sel(c.mask, pool)[id] | (1u << slot));
+            pool_sel(c.mask, pool)[id] = (uint16_t)(pl.m | (1u << slot));
         }
-        const int p = c.seq_len[b];
-        pool_sel(c.pos, pool)[(size_t)id * BLK + slot] = p;
-        c.seq_len[b] = p + 1;
+        pool_sel(c.pos, pool)[(size_t)id * BLK + slot] = pl.len;
+        c.seq_len[b] = pl.len + 1;
     }
 }
 

@@ -439,6 +439,12 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
             acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<BITS, NAT>(kw, g, vb), qb, acc[g], 0, 0, 0);
         }
     }
+    // -- the K reads have landed: the next block-pack's K part, while the
+    //    last products, the scores and their tile store proceed.  No stage
+    //    read follows in this block; the next block waits for all of its
+    //    wave's memory operations.
+    wait_lgkm0();
+    next(PART_K);
 
     // -- scores of tokens 4hi..4hi+3 for head lo: fold the group scales and
     //    zeros, base-2 scale, mask cleared slots (a cleared slot's stage
@@ -472,21 +478,18 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
             s[i] = row_ok && tv[i] ? v[i] * scale2 : -INFINITY;
         }
     }
-    // -- the block's scores: the entry's 1 KB tile is [slot][head] (cleared
-    //    slots -inf; heads past the pack unspecified).  Lane (head lo = 4a +
-    //    i, hi) holds head lo's slots 4hi..4hi+3; a 4x4 transpose inside each
-    //    group of four lanes gives it slot 4hi + i's heads 4a..4a+3, stored
-    //    with one 16-byte write, so the wave writes the whole tile at once.
+    // -- the block's scores: the entry's 1 KB tile is [slot][head] (rows of
+    //    cleared slots not written; heads past the pack unspecified).  Lane
+    //    (head lo = 4a + i, hi) holds head lo's slots 4hi..4hi+3; a 4x4
+    //    transpose inside each group of four lanes gives it slot 4hi + i's
+    //    heads 4a..4a+3, stored with one 16-byte write, so the wave writes
+    //    the tile's valid rows at once (the mass pass reads only those).
     {
         const float4 v = quad_transpose(make_float4(s[0], s[1], s[2], s[3]), lo);
-        *reinterpret_cast<float4 *>(tile + (4 * hi + (lo & 3)) * 16 + 4 * (lo >> 2)) = v;
+        const int slot = 4 * hi + (lo & 3);
+        if ((m16 >> slot) & 1u) *reinterpret_cast<float4 *>(tile + slot * 16 + 4 * (lo >> 2)) = v;
     }
 
-    // -- the K reads have landed: the next block-pack's K part.  No LDS read
-    //    follows in this block, and the stores above were issued before it,
-    //    so the next block waits for all of its wave's memory operations.
-    wait_lgkm0();
-    next(PART_K);
     // -- online softmax.  The PV accumulators hold this lane's own head (lo),
     //    so a rescale is a multiply by the lane's own factor; it is done on
     //    every block (a branch around it makes the compiler copy the
