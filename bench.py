@@ -125,6 +125,52 @@ def committed_traffic(workload: str):
     return d["hbm_bytes_per_call"] if h.hexdigest() == d["sources_sha256"] else None
 
 
+TRAFFIC_SOURCES = ["eviction_kvq_decode_amd/csrc/kvq_attn.hip", "eviction_kvq_decode_amd/csrc/kvq_internal.h",
+                   "eviction_kvq_decode_amd/csrc/kvq_device.h"]
+
+
+def traffic_record(fetch_csv: str, write_csv: str, copy_mb: int) -> dict:
+    """The committed traffic record from two rocprofv3 --pmc runs of this
+    script (FETCH_SIZE, then WRITE_SIZE, each with --copy-probe-mb copy_mb):
+    per-dispatch KiB of the decode kernels, scaled by what the same counter
+    reads for the probe's copies (copy_mb MiB read and written each)."""
+    import csv
+    from collections import defaultdict
+
+    def means(path, counter):
+        vals = defaultdict(list)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = ("copy" if "copyBuffer" in name else "split" if "attn_split" in name
+                       else "finalize" if "attn_finalize" in name else None)
+                if key:
+                    vals[key].append(float(row["Counter_Value"]))
+        probe = sorted(vals["copy"])[-3:]   # the three probe copies are the largest
+        return {k: float(np.mean(v)) for k, v in vals.items() if k != "copy"}, float(np.mean(probe))
+
+    copy_bytes = copy_mb << 20
+    fetch, fetch_copy = means(fetch_csv, "FETCH_SIZE")
+    write, write_copy = means(write_csv, "WRITE_SIZE")
+    rs, ws = copy_bytes / (fetch_copy * 1024), copy_bytes / (write_copy * 1024)
+    h = hashlib.sha256()
+    for src in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    rd = (fetch["split"] + fetch["finalize"]) * 1024 * rs
+    wr = (write["split"] + write["finalize"]) * 1024 * ws
+    return {"workload": "long_evicted: B=32 Hq=32 Hkv=8 D=128, 32768 positions, 60% evicted",
+            "kernel": "kvq_decode_attention (attn_split + attn_finalize)",
+            "sources_sha256": h.hexdigest(), "sources": TRAFFIC_SOURCES,
+            "copy_probe_bytes": copy_bytes, "fetch_kib_per_copy": fetch_copy, "write_kib_per_copy": write_copy,
+            "read_scale": rs, "write_scale": ws,
+            "split_fetch_kib": fetch["split"], "split_write_kib": write["split"],
+            "finalize_fetch_kib": fetch["finalize"], "finalize_write_kib": write["finalize"],
+            "hbm_read_bytes": rd, "hbm_write_bytes": wr, "hbm_bytes_per_call": rd + wr}
+
+
 def host_cpu(units: int) -> dict:
     """The host the oracle runs on: cores this process may use, the CPU
     model, and the OpenMP threads the oracle's decode can keep busy (it runs
@@ -453,7 +499,17 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run 3 device-to-device copies of this many MiB before the steps "
                          "(a kernel of known traffic, to scale hardware byte counters)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/decode_long_evicted_traffic.json from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of runs with "
+                         "--copy-probe-mb 1024, and exit (no GPU use)")
     args = ap.parse_args()
+    if args.traffic_record:
+        rec = traffic_record(*args.traffic_record, copy_mb=1024)
+        with open(os.path.join(ROOT, "profiles", "decode_long_evicted_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the path shards by sequence "
                                    "with no exchange (see the design notes)", "n_gpus": args.gpus}))
