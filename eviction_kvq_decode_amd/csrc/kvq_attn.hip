@@ -28,6 +28,7 @@ namespace {
 
 constexpr int E = 256;  // table entries a segment walks at a time (64 per wave)
 constexpr int MAX_HQ = 256;
+constexpr int MAX_B = 1024;   // the largest batch the library accepts
 constexpr float LOG2E = 1.4426950408889634f;
 
 // Table entries of a sequence, as the kernels read them (a count outside
@@ -197,7 +198,21 @@ struct WaveState {
     floatx4 o[8];    // sum P' * (B + code), P' = p * v_scale * mult: head rho, channels
                      // 16 n + 4 r .. + 3 of tile n
     float mult;      // power-of-two headroom factor applied to P'
+    float4 sc;       // the last block's scores in tile layout (slot 4 r + rho % 4,
+                     // heads 4 (rho / 4) ..), stored once the next block has landed
 };
+
+// The score rows of a block whose entry's tile is `tile` and valid slots m16:
+// lane (lo, hi) writes the 16 bytes of slot 4 hi + lo % 4, heads 4 (lo / 4)
+// .. + 3.  A block's rows are written at the start of the wave's next block,
+// right after its loads have landed, so the write completes under that
+// block's work instead of holding up the wait for its loads (the wait counts
+// stores too).
+__device__ inline void store_scores(float *tile, uint32_t m16, float4 v) {
+    const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
+    const int slot = 4 * hi + (lo & 3);
+    if ((m16 >> slot) & 1u) *reinterpret_cast<float4 *>(tile + slot * 16 + 4 * (lo >> 2)) = v;
+}
 
 // ---------------------------------------------------------------------------
 // Block staging.  Each wave owns an LDS stage that holds one block-pack: the
@@ -353,8 +368,7 @@ struct NoNext {
 
 // NAT: the block holds native E4M3 / E2M1 codes (symmetric, zero 0).
 template <int G, int BITS, bool NAT, class Next>
-__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, float *tile,
-                                    const uint4 *const *qa, const float *qsum, float scale2, WaveState &st,
+__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, const uint4 *const *qa, const float *qsum, float scale2, WaveState &st,
                                     const Next &next) {
     constexpr int P = PACK(G);
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
@@ -482,13 +496,10 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
     //    cleared slots not written; heads past the pack unspecified).  Lane
     //    (head lo = 4a + i, hi) holds head lo's slots 4hi..4hi+3; a 4x4
     //    transpose inside each group of four lanes gives it slot 4hi + i's
-    //    heads 4a..4a+3, stored with one 16-byte write, so the wave writes
-    //    the tile's valid rows at once (the mass pass reads only those).
-    {
-        const float4 v = quad_transpose(make_float4(s[0], s[1], s[2], s[3]), lo);
-        const int slot = 4 * hi + (lo & 3);
-        if ((m16 >> slot) & 1u) *reinterpret_cast<float4 *>(tile + slot * 16 + 4 * (lo >> 2)) = v;
-    }
+    //    heads 4a..4a+3, kept for one 16-byte write (store_scores), so the
+    //    wave writes the tile's valid rows at once (the mass pass reads only
+    //    those).
+    st.sc = quad_transpose(make_float4(s[0], s[1], s[2], s[3]), lo);
 
     // -- online softmax.  The PV accumulators hold this lane's own head (lo),
     //    so a rescale is a multiply by the lane's own factor; it is done on
@@ -709,10 +720,13 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, floa
             issue(wv, PART_V);
             issue(wv, PART_K);
         }
+        float *pend = nullptr;   // tile of the scores held in st.sc (wave-uniform)
+        uint32_t pend_m = 0;
         for (int k = wv; k < n_ent; k += WAVES) {
             // entry k is in the stage once its wave's memory operations are done
             // (the last ones issued are its K part)
             wait_vm0();
+            if (pend) store_scores(pend, pend_m, st.sc);
             const uint32_t ent = __builtin_amdgcn_readfirstlane(sh.ent[k]);
             const uint32_t msk = __builtin_amdgcn_readfirstlane(sh.msk[k]);
             const int e = __builtin_amdgcn_readfirstlane(sh.eix[k]);
@@ -721,14 +735,16 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, floa
             auto next = [&](int part) {
                 if (kn < n_ent) issue(kn, part);
             };
-            float *tile = score_u + (size_t)e * 256;
             if (pool == 0)
-                attend_block<G, 8, NATIVE>(stg, np, msk, tile, qa, qsum, scale2, st, next);
+                attend_block<G, 8, NATIVE>(stg, np, msk, qa, qsum, scale2, st, next);
             else if (pool == 1)
-                attend_block<G, 4, NATIVE>(stg, np, msk, tile, qa, qsum, scale2, st, next);
+                attend_block<G, 4, NATIVE>(stg, np, msk, qa, qsum, scale2, st, next);
             else
-                attend_block<G, 2, false>(stg, np, msk, tile, qa, qsum, scale2, st, next);
+                attend_block<G, 2, false>(stg, np, msk, qa, qsum, scale2, st, next);
+            pend = score_u + (size_t)e * 256;
+            pend_m = msk;
         }
+        if (pend) store_scores(pend, pend_m, st.sc);
         // every wave is done with the chunk's entries before the next chunk's
         // walk overwrites them
         __syncthreads();
@@ -800,21 +816,40 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, floa
     __syncthreads();
 }
 
+// Split of the flat entry list over the grid.  With two workgroups per
+// compute unit, workgroup j and j + n_first (n_first = the compute units)
+// share one, and the first-dispatched one issues ahead of the other: on the
+// long evicted trace it finished its equal share about 14% sooner, and the
+// unit then ran the later one alone.  So the first n_first workgroups take
+// (64 + SPLIT_SKEW) / 64 of the mean share and the rest (64 - SPLIT_SKEW) / 64
+// (n_first = NW: equal shares).  Any split that keeps the ranges in
+// workgroup order is correct: the finalize reads the starts the split kernel
+// records.
+constexpr long SPLIT_SKEW = 6;
+__device__ inline int split_start(long N, int NW, int n_first, int j) {
+    if (n_first >= NW) return (int)(N * j / NW);
+    const long A = 64 + SPLIT_SKEW, Bw = 64 - SPLIT_SKEW;
+    const long tot = n_first * A + (long)(NW - n_first) * Bw;
+    const long u = j <= n_first ? (long)j * A : n_first * A + (long)(j - n_first) * Bw;
+    return (int)(N * u / tot);
+}
+
 // The work is the flat list of (sequence b, kv-head pack p, table entry e),
 // in that order: sequence b's entries for pack p sit at
 // pre(b) + p nb(b) + e, where nb(b) is its table length and pre(b) =
 // n_packs * (table entries of the sequences before it).  Workgroup j of the
 // NW in the grid (what fits on the GPU at once) takes the contiguous range
-// [N j / NW, N (j + 1) / NW) of the N entries: every workgroup streams the
-// same number of block-packs, with no scheduling traffic.  Where its range
-// crosses a (sequence, pack) boundary it writes one partial per side; the
-// partial of workgroup j for unit u = b n_packs + p sits in slot j + u
-// (unique, since both j and u grow along the list).
+// [split_start(j), split_start(j + 1)) of the N entries, with no scheduling
+// traffic, and records its start for the finalize.  Where its range crosses
+// a (sequence, pack) boundary it writes one partial per side; the partial
+// of workgroup j for unit u = b n_packs + p sits in slot j + u (unique,
+// since both j and u grow along the list).
 // NATIVE: the cache holds the native codec (Reasoning and Execution blocks
 // in E4M3 / E2M1; Transition blocks are integer-coded in both codecs).
 template <int G, bool NATIVE>
 __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split(kvq_cache c, const uint16_t *q,
-                                                                                 float *mass, DecodeWs ws, float scale2) {
+                                                                                 float *mass, DecodeWs ws, float scale2,
+                                                                                 int n_first) {
     constexpr int P = PACK(G);
     const int n_packs = (c.Hkv + P - 1) / P;
     const int tid = threadIdx.x;
@@ -854,8 +889,10 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
         for (int bb = tid; bb < c.B; bb += NT) ws.pre[bb] = s_pre[bb];
         if (tid == 0) ws.pre[c.B] = (int)N;
     }
-    const int f0 = (int)(N * j / NW), f1 = (int)(N * (j + 1) / NW);
+    const int f0 = split_start(N, NW, n_first, j), f1 = split_start(N, NW, n_first, j + 1);
     if (tid == 0) {
+        ws.rstart[j] = f0;
+        if (j == NW - 1) ws.rstart[NW] = f1;
         // the sequence holding entry f0: the last b with pre(b) <= f0
         int lo_b = 0, hi_b = c.B - 1;
         while (lo_b < hi_b) {
@@ -895,56 +932,45 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     }
 }
 
-// Sum of x over the 16 lanes of this lane's row, in lane 15 of the row
-// (other lanes hold partial sums): four DPP row shifts, in a fixed order.
-__device__ inline float row_sum16(float x) {
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
-    return x;
-}
-
-// Start of workgroup j's range of the flat entry list, and the workgroup
-// whose range holds entry f: the last j with start(j) <= f (a workgroup
-// with an empty range is never the answer).
-__device__ inline int range_start(long N, int NW, int j) { return (int)(N * j / NW); }
-__device__ inline int range_owner(long N, int NW, int f) {
-    int j = (int)(((long)f * NW) / N);
-    while (j + 1 < NW && range_start(N, NW, j + 1) <= f) ++j;
-    return j;
-}
-
-// Finalize: grid (X, B); workgroup x of row b
-//  - merges, per head of sequence b, the partials of its unit's segments
-//    (the workgroups whose ranges met the unit, in order) into M_h, 1 / L_h;
-//  - takes b's table entries FB per wave, workgroups and waves in turn: lanes
-//    4t .. 4t + 3 load slot t's row of every pack's tile (16 B each, four
-//    heads), sum exp2(s - M_h) / L_h over their heads, and a fixed two-step
-//    butterfly totals the slot; mass and importance are written at the slot's
-//    position;
-//  - writes the output rows of heads x, x + X, ...
-constexpr int FT = 256;
-constexpr int FB = 4;   // entries a wave takes per round
-
-__global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
-                                                    float decay, DecodeWs ws, int NW, int G, int P, int n_packs) {
-    const int x = blockIdx.x, b = blockIdx.y, X = gridDim.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nb = table_entries(c, b);
-    const int Hq = c.Hq, PG = P * G;
-    __shared__ float Mh[MAX_HQ], Rh[MAX_HQ];
-    __shared__ float4 red[FT];
-    const long pre = nb > 0 ? ws.pre[b] : 0, N = ws.pre[c.B];
-    if (nb == 0) {
-        // no table entries, so no split segment zeroed this sequence's
-        // positions: every one below seq_len has mass 0
-        const int len = min(c.seq_len[b], c.n_cap);
-        for (int p = x * FT + tid; p < len; p += X * FT) mass[(size_t)b * c.n_cap + p] = 0.f;
+// The split workgroup whose range holds entry f of its list: the last j
+// with rs[j] <= f, from the recorded starts rs[0..NW] (a workgroup with an
+// empty range is never the answer).
+__device__ inline int range_owner(const int *rs, int NW, int f) {
+    int lo = 0, hi = NW - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (rs[mid] <= f) lo = mid; else hi = mid - 1;
     }
+    return lo;
+}
 
-    // -- global max / sum per head: tpg lanes of one wave per head, each over
-    //    a stride of its unit's segments, then a butterfly
+// Finalize: a grid of W workgroups that all fit on the device at once.
+//  - Items: runs of FC consecutive table entries of one sequence, sequence
+//    by sequence (ceil(nb / FC) each), taken in turn: item j, j + W, ...
+//  - Per item, each wave loads the table entries, masks and positions of its
+//    FB entries first; then, while they are in flight, the workgroup merges
+//    (into the statistics buffer of the item's parity), per head of the sequence,
+//    the partials of the head's unit (the split ranges that met the unit, in
+//    order) into M_h, 1 / L_h; then lanes 4t .. 4t + 3 load slot t's row of
+//    every pack's tile (16 B each, four heads), sum exp2(s - M_h) / L_h over
+//    their heads, and a fixed two-step butterfly totals the slot; mass and
+//    importance are written at the slot's position.
+//  - Item k of a sequence also writes its output rows h = k, k + K, ...
+//    (K = the sequence's items): channels merged over the unit's partials in
+//    a fixed order.
+//  - Sequences without table entries get mass 0 below their length and zero
+//    output rows, by workgroup b mod W.
+constexpr int FT = 256;
+constexpr int FB = 4;                 // entries a wave takes per item
+constexpr int FC = FB * (FT / 64);    // entries per item
+
+// M_h and 1 / L_h of every head of sequence b (whose split-list entries
+// start at pre and number n_packs x nb), into Mh / Rh: tpg lanes per head,
+// each over a stride of the unit's segments, then a butterfly.  Called by
+// the whole workgroup.
+__device__ inline void head_stats(const DecodeWs &ws, const int *rs, int NW, int b, long pre, int nb, int Hq,
+                                  int PG, int n_packs, float *Mh, float *Rh) {
+    const int tid = threadIdx.x;
     int tpg = 64;
     while (tpg > 1 && tpg * Hq > FT) tpg >>= 1;
     for (int h0 = 0; h0 < Hq; h0 += FT / tpg) {
@@ -953,13 +979,13 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
         if (h < Hq && nb > 0) {
             const int p = h / PG, hh = h % PG, u = b * n_packs + p;
             const long U0 = pre + (long)p * nb;
-            const int j0 = range_owner(N, NW, (int)U0), j1 = range_owner(N, NW, (int)(U0 + nb - 1));
+            const int j0 = range_owner(rs, NW, (int)U0), j1 = range_owner(rs, NW, (int)(U0 + nb - 1));
             for (int jb = j0 + jj; jb <= j1; jb += 4 * tpg) {
                 float2 v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int jx = jb + q * tpg;
-                    const bool live = jx <= j1 && range_start(N, NW, jx) < range_start(N, NW, jx + 1);
+                    const bool live = jx <= j1 && rs[jx] < rs[jx + 1];
                     v[q] = live ? reinterpret_cast<const float2 *>(ws.ml)[((size_t)jx + u) * 16 + hh]
                                 : make_float2(-INFINITY, 0.f);
                 }
@@ -986,36 +1012,114 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
             Rh[h] = L > 0.f ? 1.0f / L : 0.f;
         }
     }
-    __syncthreads();
+}
 
-    // -- mass (and importance) of the valid slots of b's entries
+__global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
+                                                    float decay, DecodeWs ws, int NW, int G, int P, int n_packs) {
+    const int j = blockIdx.x, W = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Hq = c.Hq, PG = P * G;
+    __shared__ float Mh2[2][MAX_HQ], Rh2[2][MAX_HQ];   // by item parity
+    __shared__ float4 red[FT];
+    __shared__ int s_pre[MAX_B + 1];          // sequences' first entries (no pack factor)
+    __shared__ int s_item[MAX_B + 1];         // sequences' first items
+    __shared__ int s_rs[MAX_SPLIT_WGS + 1];   // split ranges' starts
+    __shared__ int s_wsum[FT / 64];
+
+    // -- the sequences' entry prefix, the split ranges, and the item prefix
+    //    (a block scan over ceil(nb / FC), SPT consecutive sequences per
+    //    thread, so that the prefix at B is written too)
+    constexpr int SPT = (MAX_B + FT) / FT;
+    for (int bb = tid; bb <= c.B; bb += FT) s_pre[bb] = ws.pre[bb] / n_packs;
+    for (int k = tid; k <= NW; k += FT) s_rs[k] = ws.rstart[k];
+    __syncthreads();
     {
-        const int t = lane >> 2, hq = lane & 3;
-        const float *const score_b = ws.score + (size_t)b * n_packs * c.max_blocks * 256;
-        for (int e0 = (x * (FT / 64) + wave) * FB; e0 < nb; e0 += X * (FT / 64) * FB) {
-            bool valid[FB];
-            int pos[FB];
+        int cnt[SPT], tot = 0;
 #pragma unroll
-            for (int q = 0; q < FB; ++q) {
-                valid[q] = false;
-                pos[q] = -1;
-                if (e0 + q < nb) {
-                    const uint32_t ent = c.table[(size_t)b * c.max_blocks + e0 + q];
-                    const int pool = (int)(ent >> 30);
-                    const uint32_t id = ent & 0x3fffffffu;
-                    valid[q] = (pool_sel(c.mask, pool)[id] >> t) & 1u;
-                    pos[q] = pool_sel(c.pos, pool)[(size_t)id * BLK + t];
-                }
-                // a position outside the row stride (a corrupt cache) is skipped
-                if (pos[q] < 0 || pos[q] >= c.n_cap) valid[q] = false;
+        for (int i = 0; i < SPT; ++i) {
+            const int bb = SPT * tid + i;
+            cnt[i] = bb < c.B ? (s_pre[bb + 1] - s_pre[bb] + FC - 1) / FC : 0;
+            tot += cnt[i];
+        }
+        int incl = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        if (lane == 63) s_wsum[wave] = incl;
+        __syncthreads();
+        int run = incl - tot;
+        for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int bb = SPT * tid + i;
+            if (bb <= c.B) s_item[bb] = run;
+            run += cnt[i];
+        }
+        __syncthreads();
+    }
+    const int n_items = s_item[c.B];
+
+    // -- sequences with no table entries: no split segment zeroed their
+    //    positions, so every one below seq_len gets mass 0 here, and their
+    //    output rows are 0
+    for (int bb = j; bb < c.B; bb += W) {
+        if (s_pre[bb + 1] > s_pre[bb]) continue;
+        const int len = min(c.seq_len[bb], c.n_cap);
+        for (int p = tid; p < len; p += FT) mass[(size_t)bb * c.n_cap + p] = 0.f;
+        for (int i = tid; i < Hq * HD; i += FT) out[(size_t)bb * Hq * HD + i] = 0.f;
+    }
+
+    const int t = lane >> 2, hq = lane & 3;
+    for (int it = j, par = 0; it < n_items; it += W, par ^= 1) {
+        float *const Mh = Mh2[par], *const Rh = Rh2[par];
+        // the sequence of item it: the last b with s_item[b] <= it
+        int b = 0;
+        {
+            int lo_b = 0, hi_b = c.B - 1;
+            while (lo_b < hi_b) {
+                const int mid = (lo_b + hi_b + 1) >> 1;
+                if (s_item[mid] <= it) lo_b = mid; else hi_b = mid - 1;
             }
-            // the importance of these positions, loaded with the scores so
-            // that its latency overlaps theirs
+            b = lo_b;
+        }
+        const int nb = s_pre[b + 1] - s_pre[b], k = it - s_item[b], K = s_item[b + 1] - s_item[b];
+        const int e0 = k * FC + wave * FB;   // this wave's first entry
+        const long pre = (long)s_pre[b] * n_packs;
+
+        // -- this wave's entries: table, then masks and positions, issued
+        //    before the head statistics so their latency overlaps
+        bool valid[FB];
+        int pos[FB];
+#pragma unroll
+        for (int q = 0; q < FB; ++q) {
+            valid[q] = false;
+            pos[q] = -1;
+            if (e0 + q < nb) {
+                const uint32_t ent = c.table[(size_t)b * c.max_blocks + e0 + q];
+                const int pool = (int)(ent >> 30);
+                const uint32_t id = ent & 0x3fffffffu;
+                valid[q] = (pool_sel(c.mask, pool)[id] >> t) & 1u;
+                pos[q] = pool_sel(c.pos, pool)[(size_t)id * BLK + t];
+            }
+            // a position outside the row stride (a corrupt cache) is skipped
+            if (pos[q] < 0 || pos[q] >= c.n_cap) valid[q] = false;
+        }
+        // (no barrier before: the statistics of the item before last, in
+        // this buffer, were read before the last item's barrier below, so
+        // the loads above stay in flight while the partials are merged)
+        head_stats(ws, s_rs, NW, b, pre, nb, Hq, PG, n_packs, Mh, Rh);
+        __syncthreads();
+
+        // -- mass (and importance) of the valid slots
+        {
             float imp_old[FB];
             if (importance && hq == 0) {
 #pragma unroll
                 for (int q = 0; q < FB; ++q) imp_old[q] = valid[q] ? importance[(size_t)b * c.n_cap + pos[q]] : 0.f;
             }
+            const float *const score_b = ws.score + (size_t)b * n_packs * c.max_blocks * 256;
             float acc[FB];
 #pragma unroll
             for (int q = 0; q < FB; ++q) acc[q] = 0.f;
@@ -1055,74 +1159,92 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
                 }
             }
         }
-    }
 
-    // -- output rows of the heads this workgroup owns: 32 channel quads x
-    //    8 segment groups, merged in a fixed order
-    for (int h = x; h < Hq; h += X) {
-        const int c4 = tid & 31, sg = tid >> 5;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float Mx = Mh[h];
-        if (nb > 0 && Mx != -INFINITY) {
-            const int p = h / PG, hh = h % PG, u = b * n_packs + p;
-            const long U0 = pre + (long)p * nb;
-            const int j0 = range_owner(N, NW, (int)U0), j1 = range_owner(N, NW, (int)(U0 + nb - 1));
-            for (int jb = j0 + sg; jb <= j1; jb += 4 * 8) {
-                float mv[4];
-                float4 ov[4];
+        // -- output rows h = k, k + K, ...: 32 channel quads x 8 segment
+        //    groups, merged in a fixed order
+        for (int h = k; h < Hq; h += K) {
+            const int c4 = tid & 31, sg = tid >> 5;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float Mx = Mh[h];
+            if (Mx != -INFINITY) {
+                const int p = h / PG, hh = h % PG, u = b * n_packs + p;
+                const long U0 = pre + (long)p * nb;
+                const int j0 = range_owner(s_rs, NW, (int)U0), j1 = range_owner(s_rs, NW, (int)(U0 + nb - 1));
+                for (int jb = j0 + sg; jb <= j1; jb += 4 * 8) {
+                    float mv[4];
+                    float4 ov[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int jx = jb + 8 * q;
-                    const bool live = jx <= j1 && range_start(N, NW, jx) < range_start(N, NW, jx + 1);
-                    const size_t row = ((size_t)jx + u) * 16 + hh;
-                    mv[q] = live ? ws.ml[row * 2] : -INFINITY;
-                    ov[q] = live ? reinterpret_cast<const float4 *>(ws.o + row * HD)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const int jx = jb + 8 * q;
+                        const bool live = jx <= j1 && s_rs[jx] < s_rs[jx + 1];
+                        const size_t r = ((size_t)jx + u) * 16 + hh;
+                        mv[q] = live ? ws.ml[r * 2] : -INFINITY;
+                        ov[q] = live ? reinterpret_cast<const float4 *>(ws.o + r * HD)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (mv[q] == -INFINITY) continue;
-                    const float f = exp2f(mv[q] - Mx);
-                    acc.x = fmaf(ov[q].x, f, acc.x);
-                    acc.y = fmaf(ov[q].y, f, acc.y);
-                    acc.z = fmaf(ov[q].z, f, acc.z);
-                    acc.w = fmaf(ov[q].w, f, acc.w);
+                    for (int q = 0; q < 4; ++q) {
+                        if (mv[q] == -INFINITY) continue;
+                        const float fq = exp2f(mv[q] - Mx);
+                        acc.x = fmaf(ov[q].x, fq, acc.x);
+                        acc.y = fmaf(ov[q].y, fq, acc.y);
+                        acc.z = fmaf(ov[q].z, fq, acc.z);
+                        acc.w = fmaf(ov[q].w, fq, acc.w);
+                    }
                 }
             }
-        }
-        red[tid] = acc;
-        __syncthreads();
-        if (tid < 32) {
-            float4 sum = red[tid];
+            red[tid] = acc;
+            __syncthreads();
+            if (tid < 32) {
+                float4 sum = red[tid];
 #pragma unroll
-            for (int q = 1; q < 8; ++q) {
-                const float4 rr = red[q * 32 + tid];
-                sum.x += rr.x; sum.y += rr.y; sum.z += rr.z; sum.w += rr.w;
+                for (int q = 1; q < 8; ++q) {
+                    const float4 rr = red[q * 32 + tid];
+                    sum.x += rr.x; sum.y += rr.y; sum.z += rr.z; sum.w += rr.w;
+                }
+                const float R = Rh[h];
+                reinterpret_cast<float4 *>(out + ((size_t)b * Hq + h) * HD)[tid] =
+                    make_float4(sum.x * R, sum.y * R, sum.z * R, sum.w * R);
             }
-            const float R = Rh[h];
-            reinterpret_cast<float4 *>(out + ((size_t)b * Hq + h) * HD)[tid] =
-                make_float4(sum.x * R, sum.y * R, sum.z * R, sum.w * R);
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
 }  // namespace
 
-// Workgroups of attn_split<G, native> that fit on the device at once, for a
-// given dynamic LDS size (cached per device, G and codec).
-int persistent_grid(int G, bool native, const void *kernel, size_t dyn_lds) {
-    static int cache[64][2][KVQ_MAX_GQA + 1];
-    static size_t cache_lds[64][2][KVQ_MAX_GQA + 1];
+// Workgroups of attn_split<G, native> that fit on the device at once, and
+// per compute unit (cached per device, G and codec).
+int persistent_grid(int G, bool native, const void *kernel, int *per_cu_out) {
+    static int cache[64][2][KVQ_MAX_GQA + 1], cache_cu[64][2][KVQ_MAX_GQA + 1];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     int &v = cache[dev][native][G];
-    if (v == 0 || cache_lds[dev][native][G] != dyn_lds) {
+    if (v == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WAVES * 64, dyn_lds) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WAVES * 64, 0) != hipSuccess)
             return 0;
-        v = cus * (per_cu > 0 ? per_cu : 1);
-        cache_lds[dev][native][G] = dyn_lds;
+        cache_cu[dev][native][G] = per_cu > 0 ? per_cu : 1;
+        v = cus * cache_cu[dev][native][G];
+    }
+    *per_cu_out = cache_cu[dev][native][G];
+    return v;
+}
+
+// Finalize workgroups that fit on the device at once, at most six per
+// compute unit (cached per device).
+int finalize_grid() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int &v = cache[dev];
+    if (v == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(attn_finalize),
+                                                         FT, 0) != hipSuccess)
+            return 0;
+        v = cus * std::max(1, std::min(per_cu, 6));
     }
     return v;
 }
@@ -1134,12 +1256,18 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     const float scale2 = sm_scale * LOG2E;
     int NW = 0;
+    // the split's workgroups j and j + NW / 2 share a compute unit when two fit
+    // on one; the first-dispatched half takes the larger shares (split_start)
     switch (G) {
 #define KVQ_GN(g, nat)                                                                                   \
     {                                                                                                    \
-        NW = std::min(persistent_grid(g, nat, reinterpret_cast<const void *>(attn_split<g, nat>), 0), MAX_SPLIT_WGS); \
+        int per_cu = 0;                                                                                  \
+        const int fit = persistent_grid(g, nat, reinterpret_cast<const void *>(attn_split<g, nat>), &per_cu); \
+        NW = std::min(fit, MAX_SPLIT_WGS);                                                               \
         if (NW <= 0) return false;                                                                       \
-        hipLaunchKernelGGL((attn_split<g, nat>), dim3(NW), dim3(WAVES * 64), 0, s, c, qq, mass, ws, scale2); \
+        const int n_first = per_cu == 2 && NW == fit ? NW / 2 : NW;                                      \
+        hipLaunchKernelGGL((attn_split<g, nat>), dim3(NW), dim3(WAVES * 64), 0, s, c, qq, mass, ws, scale2, \
+                           n_first);                                                                     \
     }
 #define KVQ_G(g)                                                    \
     case g:                                                         \
@@ -1152,13 +1280,11 @@ bool launch_decode(const kvq_cache &c, const void *q, float *out, float *mass, f
         default: return false;
     }
     {
-        // enough workgroups per sequence that a full table takes two rounds
-        // of FB entries per wave, and at least one per output head (up to
-        // 64); an odd row keeps the rows' busy workgroups off the same
-        // compute units
-        const int per_round = FB * (FT / 64);
-        const int X = std::max((c.max_blocks + 2 * per_round - 1) / (2 * per_round), std::min(c.Hq, 64)) | 1;
-        hipLaunchKernelGGL(attn_finalize, dim3(X, c.B), dim3(FT), 0, s, c, out, mass, importance, decay, ws, NW, G,
+        // every finalize workgroup resident at once, at most six per compute
+        // unit, and no more than the items a full table would give
+        const int W = std::min(finalize_grid(), c.B * ((c.max_blocks + FC - 1) / FC));
+        if (W <= 0) return false;
+        hipLaunchKernelGGL(attn_finalize, dim3(W), dim3(FT), 0, s, c, out, mass, importance, decay, ws, NW, G,
                            decode_pack(G), decode_n_packs(c));
     }
     return hipGetLastError() == hipSuccess;

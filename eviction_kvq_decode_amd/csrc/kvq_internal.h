@@ -59,16 +59,19 @@ struct DecodeWs {
                        // written by the split kernel, read by the finalize
     int32_t *pre;      // [B + 1] where each sequence's entries start in the split
                        // kernel's flat list (n_packs x the entries before it); [B]: N
+    int32_t *rstart;   // [grid + 1] where each split workgroup's range of that list
+                       // starts; [grid]: N
     static size_t slots(const kvq_cache &c) { return MAX_SPLIT_WGS + (size_t)c.B * decode_n_packs(c); }
     static size_t bytes(const kvq_cache &c) {
         const size_t S = slots(c);
-        return SyncWs::bytes(c) + align256(4L * (c.B + 1)) + align256(128L * S) + align256(8192L * S) +
-               align256(1024L * c.B * c.max_blocks * decode_n_packs(c));
+        return SyncWs::bytes(c) + align256(4L * (c.B + 1)) + align256(4L * (MAX_SPLIT_WGS + 1)) +
+               align256(128L * S) + align256(8192L * S) + align256(1024L * c.B * c.max_blocks * decode_n_packs(c));
     }
     DecodeWs(void *ws, const kvq_cache &c) {
         const size_t S = slots(c);
         char *p = (char *)ws + SyncWs::bytes(c);
         pre = (int32_t *)p;   p += align256(4L * (c.B + 1));
+        rstart = (int32_t *)p; p += align256(4L * (MAX_SPLIT_WGS + 1));
         ml = (float *)p;      p += align256(128L * S);
         o = (float *)p;       p += align256(8192L * S);
         score = (float *)p;
