@@ -140,7 +140,8 @@ size_t kvq_workspace_bytes(const kvq_cache *cache);
 /* Workspace bytes kvq_decode_attention needs for this cache (a buffer this
  * size serves the decode alone; <= kvq_workspace_bytes).  It holds the split
  * partials (max, sum, output per head), the base-2 scores of every table
- * entry's slots for the mass pass, and the sequence prefix of the work list.
+ * entry's slots for the mass pass, the sequence prefix of the work list and
+ * where each split workgroup's part of it starts.
  * 0 if the cache description is rejected. */
 size_t kvq_decode_workspace_bytes(const kvq_cache *cache);
 
@@ -165,11 +166,13 @@ kvq_status kvq_append_quantize(const kvq_cache *cache, const void *k_new, const 
 /*
  * kvq_append_quantize without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid hipMalloc).  Same semantics and kernels; the plan
- * buffers live in a static device array of the library (32 KiB per GPU, zero
- * when the library loads, held until the process ends), enough for every B
- * the library accepts (<= 1024).
- * A cache whose plan buffers would not fit returns KVQ_EUNSUPPORTED.  Nothing
+ * harnesses that forbid hipMalloc).  Same semantics and kernel; the words
+ * that rank pops across sequences in batch order (an epoch, and one tagged
+ * count per pool and sequence) live in a static device array of the library
+ * (32 KiB per GPU, zero when the library loads, held until the process
+ * ends), enough for every B the library accepts (<= 1024).  The words carry
+ * the epoch of the call that wrote them, so nothing is cleared between calls.
+ * A cache whose words would not fit returns KVQ_EUNSUPPORTED.  Nothing
  * is allocated or freed.  Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (concurrent streams) race and must not be
  * issued; calls ordered on one stream are safe.
