@@ -628,15 +628,28 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, floa
     const int kh0 = pack * P, np = min(P, c.Hkv - kh0);
     const bool row_ok = lo < np * G;
 
+    // -- the first chunk's table entries are loaded with q, and their masks
+    //    once the entries are in, so that the walk below does not start a
+    //    chain of its own after q
+    const int k0 = 64 * wave + lane;
+    const bool in0 = k0 < min(E, e_end - e_begin);
+    uint32_t ent0 = 0, m0 = 0;
+    if (in0) ent0 = c.table[(size_t)b * c.max_blocks + e_begin + k0];
     // -- q of the pack's heads into LDS (zero past the pack), and the
     //    per-group q sums of head lo in registers
     float qsum[NGRP];
     {
         const int h = kh0 * G + lo;
+        uint4 qraw[NGRP];
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
-            uint4 raw = make_uint4(0, 0, 0, 0);
-            if (row_ok) raw = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + h) * HD + 32 * g + 8 * hi);
+            qraw[g] = make_uint4(0, 0, 0, 0);
+            if (row_ok) qraw[g] = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + h) * HD + 32 * g + 8 * hi);
+        }
+        if (in0) m0 = pool_sel(c.mask, ent0 >> 30)[ent0 & 0x3fffffffu];
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) {
+            const uint4 raw = qraw[g];
             if (wave == 0) {
                 sh.qb[g][lane] = raw;
                 if (lane == 0) sh.qb[g][64] = make_uint4(0, 0, 0, 0);
@@ -675,10 +688,13 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, floa
         {
             const int cnt = min(E, e_end - base);
             const int k = 64 * wave + lane;
-            uint32_t ent = 0, m = 0;
-            if (k < cnt) {
-                ent = c.table[(size_t)b * c.max_blocks + base + k];
-                m = pool_sel(c.mask, ent >> 30)[ent & 0x3fffffffu];
+            uint32_t ent = ent0, m = m0;
+            if (base != e_begin) {
+                ent = 0, m = 0;
+                if (k < cnt) {
+                    ent = c.table[(size_t)b * c.max_blocks + base + k];
+                    m = pool_sel(c.mask, ent >> 30)[ent & 0x3fffffffu];
+                }
             }
             const uint64_t bal = __ballot(m != 0);
             if (lane == 0) sh.wcnt[wave] = __popcll(bal);
@@ -826,6 +842,14 @@ __device__ inline void split_segment(const kvq_cache &c, const uint16_t *q, floa
 // workgroup order is correct: the finalize reads the starts the split kernel
 // records.
 constexpr long SPLIT_SKEW = 6;
+// A range that crosses into another (sequence, pack) unit starts a second
+// segment: its table walk, q and first blocks form a new chain of loads,
+// which cost a workgroup about as much as SPLIT_GAP table entries (10.6 us
+// on the long evicted trace, where a workgroup streams about one entry per
+// us).  The list is therefore split in cost space, where each unit is
+// followed by a gap of SPLIT_GAP: a range that takes in a unit boundary
+// takes that many fewer entries.
+constexpr long SPLIT_GAP = 10;
 __device__ inline int split_start(long N, int NW, int n_first, int j) {
     if (n_first >= NW) return (int)(N * j / NW);
     const long A = 64 + SPLIT_SKEW, Bw = 64 - SPLIT_SKEW;
@@ -855,7 +879,7 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     const int tid = threadIdx.x;
     constexpr int NT = WAVES * 64;
     __shared__ SplitLds<P> lds;
-    __shared__ int s_carry, s_loc[2];
+    __shared__ int s_carry, s_loc[6];
 
     // -- pre(b) for every sequence (a scan over table lengths in the stage
     //    area), the total N, and where this workgroup's range starts
@@ -889,21 +913,58 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
         for (int bb = tid; bb < c.B; bb += NT) ws.pre[bb] = s_pre[bb];
         if (tid == 0) ws.pre[c.B] = (int)N;
     }
-    const int f0 = split_start(N, NW, n_first, j), f1 = split_start(N, NW, n_first, j + 1);
-    if (tid == 0) {
-        ws.rstart[j] = f0;
-        if (j == NW - 1) ws.rstart[NW] = f1;
-        // the sequence holding entry f0: the last b with pre(b) <= f0
-        int lo_b = 0, hi_b = c.B - 1;
-        while (lo_b < hi_b) {
-            const int mid = (lo_b + hi_b + 1) >> 1;
-            if (s_pre[mid] <= f0) lo_b = mid; else hi_b = mid - 1;
+    // -- this workgroup's range, found by two waves (wave w for its end w):
+    //    the entry at cost position cpos, where unit (b, p) takes
+    //    [cpre(b) + p (nb + gap), + nb) of cost space, cpre(b) = pre(b) +
+    //    b n_packs gap, and a position in a gap maps to the next unit's first
+    //    entry.  Both prefixes never decrease, so "the last b with prefix <=
+    //    x" is the count of such b less one: a ballot per 64 sequences.
+    //    Wave 0 also finds the sequence holding the range's first entry and
+    //    the table lengths of it and the next (the stage area that holds the
+    //    prefix is cleared below).
+    if (tid < 128) {
+        const int wv = tid >> 6, lane = tid & 63;
+        const int NC = (int)N + c.B * n_packs * (int)SPLIT_GAP;
+        const int cpos = split_start(NC, NW, n_first, j + wv);
+        int cnt = 0;
+        for (int b0 = 0; b0 < c.B; b0 += 64) {
+            const int bb = b0 + lane;
+            cnt += __popcll(__ballot(bb < c.B && s_pre[bb] + bb * n_packs * (int)SPLIT_GAP <= cpos));
         }
-        s_loc[0] = lo_b;
-        s_loc[1] = f0 - s_pre[lo_b];
+        const int sb = max(cnt - 1, 0);
+        const int next = sb + 1 < c.B ? s_pre[sb + 1] : (int)N;
+        const int nbb = (next - s_pre[sb]) / n_packs;
+        const int off = cpos - (s_pre[sb] + sb * n_packs * (int)SPLIT_GAP);
+        const int pp = off / (nbb + (int)SPLIT_GAP), o = off % (nbb + (int)SPLIT_GAP);
+        const int f = min(s_pre[sb] + pp * nbb + min(o, nbb), (int)N);
+        if (wv == 0) {
+            // the sequence holding entry f: the last b with pre(b) <= f
+            int cnt2 = 0;
+            for (int b0 = 0; b0 < c.B; b0 += 64) {
+                const int bb = b0 + lane;
+                cnt2 += __popcll(__ballot(bb < c.B && s_pre[bb] <= f));
+            }
+            const int lb = max(cnt2 - 1, 0);
+            if (lane == 0) {
+                ws.rstart[j] = f;
+                s_loc[0] = lb;
+                s_loc[1] = f - s_pre[lb];
+                s_loc[2] = f;
+                const int n1 = lb + 1 < c.B ? s_pre[lb + 1] : (int)N;
+                const int n2 = lb + 2 < c.B ? s_pre[lb + 2] : (int)N;
+                s_loc[4] = (n1 - s_pre[lb]) / n_packs;
+                s_loc[5] = lb + 1 < c.B ? (n2 - n1) / n_packs : 0;
+            }
+        } else if (lane == 0) {
+            s_loc[3] = f;
+            if (j == NW - 1) ws.rstart[NW] = f;
+        }
     }
     __syncthreads();
     int b = __builtin_amdgcn_readfirstlane(s_loc[0]), r = __builtin_amdgcn_readfirstlane(s_loc[1]);
+    const int f0 = __builtin_amdgcn_readfirstlane(s_loc[2]), f1 = __builtin_amdgcn_readfirstlane(s_loc[3]);
+    const int b_first = b, nb_first = __builtin_amdgcn_readfirstlane(s_loc[4]),
+              nb_second = __builtin_amdgcn_readfirstlane(s_loc[5]);
     __syncthreads();   // s_loc read before the stage area is cleared
 
     // -- stage bytes start finite: zero the shared area once (the scan used it;
@@ -915,7 +976,8 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
 
     // -- the range's segments
     for (int f = f0; f < f1 && b < c.B;) {
-        const int nb = table_entries(c, b);
+        // table lengths of the first two sequences come from the prefix
+        const int nb = b == b_first ? nb_first : b == b_first + 1 ? nb_second : table_entries(c, b);
         if (nb == 0) {   // an empty sequence holds no entries of the list
             ++b;
             continue;
