@@ -59,17 +59,23 @@ constexpr float P_HEADROOM = 60000.0f;    // P' = p * v_scale * mult must stay b
 // power-of-two bias B whose exponent puts the code's bits at the top of the
 // mantissa: B = 1024 for 8-bit codes (0x64 high byte, code in the low byte),
 // 16 for 4-bit codes (0x4C00 | c << 6) and 4 for 2-bit codes (0x4400 |
-// c << 8).  B is then about the size of the codes, so the bias can stay in
-// the operand and be taken out of the fp32 sums at no cost in precision:
-// through the q sums for K (B * sum q) and through the zero-point sums for
-// V (B * sum P').  Only 8-bit K codes are unbiased before the product (one
-// packed fp16 subtract), because the scores feed the per-token mass, whose
-// tolerance is tighter than the 8 : 1 bias-to-code ratio allows.  (Operands
+// c << 8).  B is then about the size of the codes, so for K the bias can
+// stay in the operand and be taken out of the fp32 sums at no cost in
+// precision, through the q sums (B * sum q).  Only 8-bit K codes are
+// unbiased before the product (one packed fp16 subtract), because the
+// scores feed the per-token mass, whose tolerance is tighter than the 8 : 1
+// bias-to-code ratio allows.  V codes are centred instead (Code::MID).  (Operands
 // with a zero exponent, c * 2^-24 subnormals, would need no bias but lose
 // precision in the MFMA products on this hardware.)
 template <int BITS>
 struct Code {
     static constexpr float BIAS = BITS == 8 ? 1024.0f : BITS == 4 ? 16.0f : 4.0f;
+    // V operands are centred: c - MID, MID = 2^(BITS - 1), from B + c by one
+    // exact packed subtract of B + MID (both sides and the result are exact
+    // fp16).  The rounding of P' then multiplies a code of either sign and
+    // half the magnitude, so with few tokens it stays inside the output
+    // tolerance (with B + c, or c alone, it multiplies x - min >= 0).
+    static constexpr float MID = BITS == 8 ? 128.0f : BITS == 4 ? 8.0f : 2.0f;
     static constexpr uint32_t BIAS2 = BITS == 8 ? 0x64006400u : BITS == 4 ? 0x4C004C00u : 0x44004400u;
     static constexpr uint32_t FIELDS = BITS == 4 ? 0x03C003C0u : 0x03000300u;   // mantissa top field
     static constexpr int TOP = BITS == 4 ? 6 : 8;                              // its lowest bit
@@ -152,8 +158,17 @@ __device__ inline half8 k_operand(const uint32_t *kw, int g, uint32_t vb) {
     return __builtin_bit_cast(half8, r);
 }
 
+// (B + c0, B + c1) -> (c0 - MID, c1 - MID), exact
+template <int BITS>
+__device__ inline uint32_t center_pair(uint32_t x) {
+    constexpr _Float16 k = (_Float16)(Code<BITS>::BIAS + Code<BITS>::MID);
+    half2v h = __builtin_bit_cast(half2v, x);
+    h = h - (half2v){k, k};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
 // PV B operand: codes of tokens 4r..4r+3 at this lane's channel of tile n,
-// as B + c (native E4M3 / E2M1 codes: their values).
+// as c - MID (native E4M3 / E2M1 codes: their values).
 template <int BITS, bool NAT>
 __device__ inline half4 v_operand(const uint32_t *vw, int n, uint32_t vb) {
     uint32_t r[2];
@@ -177,6 +192,10 @@ __device__ inline half4 v_operand(const uint32_t *vw, int n, uint32_t vb) {
         r[0] = field_pair<2>(vw[n >> 2], 4 * m, vb);
         r[1] = field_pair<2>(vw[n >> 2], 4 * m + 2, vb);
     }
+    if constexpr (!NAT) {
+        r[0] = center_pair<BITS>(r[0]);
+        r[1] = center_pair<BITS>(r[1]);
+    }
     return __builtin_bit_cast(half4, r);
 }
 
@@ -194,8 +213,8 @@ __device__ inline float hi_h(uint32_t x) { return h2f((uint16_t)(x >> 16)); }
 struct WaveState {
     float m;         // running max of head rho (base-2 scaled scores)
     float l;         // this lane's share of the running sum
-    float z[NGRP];   // this lane's share of sum p * v_zero - B * P' / mult per group
-    floatx4 o[8];    // sum P' * (B + code), P' = p * v_scale * mult: head rho, channels
+    float z[NGRP];   // this lane's share of sum p * (v_zero + MID * v_scale) per group
+    floatx4 o[8];    // sum P' * (code - MID), P' = p * v_scale * mult: head rho, channels
                      // 16 n + 4 r .. + 3 of tile n
     float mult;      // power-of-two headroom factor applied to P'
     float4 sc;       // the last block's scores in tile layout (slot 4 r + rho % 4,
@@ -556,18 +575,15 @@ __device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, 
     for (int g = 0; g < NGRP; ++g)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pop[g][i] = (_Float16)(pm[i] * lo_h(vsz[4 * i + g]));
-    // zero-point term sum p * v_zero, less the V operands' bias share
-    // B * P' / mult (native codes: neither)
+    // zero-point term sum p * (v_zero + MID * v_scale): the centred
+    // operands' offset joins the zero point (native codes: neither)
     if constexpr (!NAT) {
-        const float kb = -Code<BITS>::BIAS / st.mult;
 #pragma unroll
         for (int g = 0; g < NGRP; ++g) {
             float zg = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                zg = fmaf(p[i], hi_h(vsz[4 * i + g]), zg);
-                zg = fmaf(kb, (float)pop[g][i], zg);
-            }
+            for (int i = 0; i < 4; ++i)
+                zg = fmaf(p[i], fmaf(Code<BITS>::MID, lo_h(vsz[4 * i + g]), hi_h(vsz[4 * i + g])), zg);
             st.z[g] += zg;
         }
     }

@@ -270,3 +270,39 @@ def test_append_first_free_slot_past_a_scan_round():
         for e in free_at[b]:
             ent = int(oc.table_row(b)[e])
             assert ent >> 30 == 1 and oc.st["mask1"][ent & 0x3FFFFFFF] == 0xFFFF
+
+
+def test_maximum_batch_many_short_sequences():
+    """The largest batch the library takes (B = 1024) of short sequences,
+    some empty: each split workgroup's range crosses many (sequence, pack)
+    units, and the finalize's sequence and item prefixes run to their last
+    slot.  Decode with importance, then a top-k evict ranked across all
+    1024 sequences, then decode again over the holes."""
+    log("[edge] B=1024 short sequences")
+    B, n = 1024, 48
+    g = small_geometry(B, 32, 8, n)
+    oc, gc = _mk(g, identity=False)
+    rng = np.random.default_rng(1024)
+    lens = rng.integers(0, n + 1, B)
+    lens[rng.choice(B, 40, replace=False)] = 0
+    tags_all = rng.integers(0, 3, (n, B)).astype(np.uint8)
+    tags_all[np.arange(n)[:, None] >= lens[None, :]] = 255
+    _fill(oc, gc, rng, n, lambda i: tags_all[i])
+    assert_same_cache(oc, gc.state_numpy())
+    assert (gc.state_numpy()["seq_len"] == lens).all()
+    q = rng.standard_normal((B, 32, HD)).astype(np.float16)
+    imp = rng.exponential(0.1, (B, g.n_cap)).astype(np.float32)
+    ref, got = _decode(oc, gc, q, imp, 0.9)
+    assert np.all(got[0][lens == 0] == 0.0)
+    assert_attention_close(ref, got)
+    assert_mass_close(oc.st["seq_len"], ref, got)
+    # evict with the GPU's importance on both sides, so no near-tie differs
+    imp_gpu = got[2]
+    kk = rng.integers(0, 20, B).astype(np.int32)
+    oc.evict(imp_gpu, kk, 2, 4)
+    gc.evict(_dev(imp_gpu), _dev(kk), 2, 4)
+    assert_same_cache(oc, gc.state_numpy())
+    q2 = rng.standard_normal((B, 32, HD)).astype(np.float16)
+    ref2, got2 = _decode(oc, gc, q2)
+    assert_attention_close(ref2, got2)
+    assert_mass_close(oc.st["seq_len"], ref2, got2)
