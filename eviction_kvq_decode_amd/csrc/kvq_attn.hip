@@ -7,14 +7,16 @@
 // accumulated H2O-style with a decay.  "ThinKV", Continuous Thinking: the
 // kernel walks a block table whose blocks carry an eviction mask.
 //
-// attn_split: persistent workgroups over (sequence, kv-head pack, run of
-//   table entries) items; runs are shortened when a small batch would leave
-//   workgroups idle.  Online softmax in base 2; writes the run's (max, sum,
-//   unnormalised output) and every score it computed (needed later for the
-//   mass, whose normaliser is only known once all runs are done).
-// attn_finalize: two workgroups per (sequence, run of table entries): merges
-//   the runs (log-sum-exp), writes the output rows, and turns the stored
-//   scores into mass / importance in a fixed head order (no float atomics).
+// attn_split: a persistent grid; each workgroup takes one contiguous range
+//   of the flat (sequence, kv-head pack, table entry) list and records where
+//   it starts.  Online softmax in base 2; writes one partial (max, sum,
+//   unnormalised output) per (sequence, pack) unit its range meets, and every
+//   score it computed (needed later for the mass, whose normaliser is only
+//   known once all ranges are done).
+// attn_finalize: a resident grid over items of 16 table entries of one
+//   sequence: merges each head's partials (log-sum-exp), turns the stored
+//   scores into mass / importance in a fixed head order (no float atomics),
+//   and writes the output rows.
 #include <math.h>
 
 #include <algorithm>
@@ -387,7 +389,8 @@ struct NoNext {
 
 // NAT: the block holds native E4M3 / E2M1 codes (symmetric, zero 0).
 template <int G, int BITS, bool NAT, class Next>
-__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, const uint4 *const *qa, const float *qsum, float scale2, WaveState &st,
+__device__ inline void attend_block(const uint8_t *stage, int np, uint32_t m16, const uint4 *const *qa,
+                                    const float *qsum, float scale2, WaveState &st,
                                     const Next &next) {
     constexpr int P = PACK(G);
     const int lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
