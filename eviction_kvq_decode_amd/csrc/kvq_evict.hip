@@ -48,6 +48,7 @@ constexpr int DROP_THREADS = 256;
 constexpr int DROP_WGS = 16;
 constexpr int DROP_WAVES = DROP_WGS * DROP_THREADS / 64;
 constexpr int TBE_RUN = 16;  // chunks of 64 positions / candidates a wave takes per pass
+constexpr int TAM_FAST = 32768;  // budgets: rows up to this many candidates take the one-pass sums
 // top-k's slot keys: KEY_WGS workgroups of KEY_THREADS per sequence
 constexpr int KEY_WGS = EVICT_KEY_WGS;
 constexpr int KEY_THREADS = 256;
@@ -652,6 +653,27 @@ __device__ inline uint32_t tam_fix(float score) {
     return (uint32_t)(score * 65536.0f);
 }
 
+// One DPP step of a 64-bit wave scan: x of the lane CTRL selects (0 where
+// there is none, or in a row outside RM).
+template <int CTRL, int RM>
+__device__ inline uint64_t dpp_u64(uint64_t x) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, RM, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, RM, 0xf, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Inclusive sum of x over lanes 0 .. this one (all 64 lanes active): shifts
+// of 1, 2, 4, 8 inside each 16-lane row, then each row's last lane added to
+// the rows after it (row broadcasts of lanes 15 and 31).
+__device__ inline uint64_t wave_incl_scan_u64(uint64_t x) {
+    x += dpp_u64<0x111, 0xf>(x);
+    x += dpp_u64<0x112, 0xf>(x);
+    x += dpp_u64<0x114, 0xf>(x);
+    x += dpp_u64<0x118, 0xf>(x);
+    x += dpp_u64<0x142, 0xa>(x);
+    x += dpp_u64<0x143, 0xc>(x);
+    return x;
+}
+
 // floor(sqrt(x)), by bisection on the root (exact integer arithmetic).
 __device__ inline uint64_t isqrt_u64(uint64_t x) {
     uint64_t lo = 0, hi = 1ull << 32;
@@ -950,15 +972,58 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
         __syncthreads();
     }
 
-    // B. weights from running sums over the candidates: psum[k] = sum of s
-    //    before candidate k, pcnt[k] = droppable candidates before it, packed
-    //    within a pass in one word (s in the low 48 bits, the count above).  Each wave takes
-    //    TBE_RUN coalesced chunks of 64 candidates: its total, one scan of the
-    //    wave totals, then a wave scan per chunk.  Then a thread per segment.
-    {
-        // packed words stay inside one pass (16384 candidates: sums below
-        // 2^46); the totals carried across passes are kept apart
-        constexpr uint64_t LOW = (1ull << 48) - 1;
+    // B. weights from running sums over the candidates, packed in one word
+    //    (s in the low 48 bits, the droppable count above), at the segments'
+    //    first candidates only (the weights read nothing else).
+    //    Rows of up to TAM_FAST candidates, one pass: each wave takes TBE_RUN
+    //    coalesced chunks of 64 candidates, loads them at once, scans each
+    //    chunk (DPP), stores the in-chunk prefix at segment starts (marked in
+    //    an LDS bitmap) and the chunk's total in LDS; a block scan of the
+    //    chunk totals then gives each chunk's offset (sums stay below 2^47,
+    //    counts below 2^15).
+    //    Longer rows: psum[k] = sum of s before candidate k, pcnt[k] =
+    //    droppable candidates before it, for every candidate, in passes of
+    //    SEL_THREADS * TBE_RUN (the totals carried across passes kept apart).
+    //    Then a thread per segment.
+    constexpr uint64_t LOW = (1ull << 48) - 1;
+    __shared__ uint32_t segbits[TAM_FAST / 32];
+    __shared__ uint64_t chunk_ex[TAM_FAST / 64];
+    const bool fast = n <= TAM_FAST;
+    uint64_t total_packed = 0;
+    if (fast) {
+        for (int i = tid; i < (n + 31) / 32; i += SEL_THREADS) segbits[i] = 0u;
+        __syncthreads();
+        for (int sg = tid; sg < nseg; sg += SEL_THREADS) {
+            const int k = segstart[sg];
+            atomicOr(&segbits[k >> 5], 1u << (k & 31));
+        }
+        __syncthreads();
+        constexpr int HALF = TBE_RUN / 2;   // chunks loaded at once (registers)
+        for (int k0 = 0; k0 < n; k0 += SEL_THREADS * TBE_RUN) {
+            const int wb = k0 + wv * 64 * TBE_RUN;
+            for (int h = 0; h < TBE_RUN; h += HALF) {
+                uint64_t v[HALF];
+#pragma unroll
+                for (int u = 0; u < HALF; ++u) {
+                    const int k = wb + 64 * (h + u) + lane;
+                    const uint32_t sv = ld_clamped(sfx, k, n, 0u), ov = ld_clamped(ob, k, n, 0u);
+                    v[u] = k < n ? ((uint64_t)sv | ((uint64_t)(ov != 0u ? 1 : 0) << 48)) : 0ull;
+                }
+#pragma unroll
+                for (int u = 0; u < HALF; ++u) {
+                    const int k = wb + 64 * (h + u) + lane;
+                    const uint64_t incl = wave_incl_scan_u64(v[u]);
+                    if (k < n && ((segbits[k >> 5] >> (k & 31)) & 1u)) psum[k] = incl - v[u];
+                    if (lane == 63 && wb + 64 * (h + u) < n) chunk_ex[(wb + 64 * (h + u)) >> 6] = incl;
+                }
+            }
+        }
+        __syncthreads();
+        const int nch = (n + 63) >> 6;   // <= TAM_FAST / 64 <= SEL_THREADS
+        const uint64_t x = tid < nch ? chunk_ex[tid] : 0ull;
+        const uint64_t incl = block_scan_u64(x, wave_u64, total_packed);
+        if (tid < nch) chunk_ex[tid] = incl - x;
+    } else {
         uint64_t carry_s = 0;
         int carry_c = 0;
         for (int k0 = 0; k0 < n; k0 += SEL_THREADS * TBE_RUN) {
@@ -984,18 +1049,14 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
             for (int u = 0; u < TBE_RUN; ++u) {
                 const int k = wb + 64 * u + lane;
                 const uint64_t v = k < n ? ((uint64_t)sfx[k] | ((uint64_t)(ob[k] != 0u ? 1 : 0) << 48)) : 0ull;
-                uint64_t incl = v;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const uint64_t y = __shfl_up(incl, d);
-                    incl += lane >= d ? y : 0ull;
-                }
+                const uint64_t incl = wave_incl_scan_u64(v);
                 if (k < n) {
                     const uint64_t ex = run + incl - v;
                     psum[k] = carry_s + (ex & LOW);
                     pcnt[k] = carry_c + (int32_t)(ex >> 48);
                 }
-                run += __shfl(incl, 63);
+                run += ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), 63) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
             }
             carry_s += tot & LOW;
             carry_c += (int32_t)(tot >> 48);
@@ -1006,10 +1067,25 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
         }
     }
     __syncthreads();
+    // (sum of s, droppable count) before candidate k, k a segment start or n
+    auto prefix = [&](int k, uint64_t &sum, int &cnt) {
+        if (fast) {
+            const uint64_t w = k < n ? chunk_ex[k >> 6] + psum[k] : total_packed;
+            sum = w & LOW;
+            cnt = (int)(w >> 48);
+        } else {
+            sum = psum[k];
+            cnt = pcnt[k];
+        }
+    };
     for (int sg = tid; sg < nseg; sg += SEL_THREADS) {
         const int a = segstart[sg], e = segstart[sg + 1];
-        const uint64_t ssum = psum[e] - psum[a];
-        const int m = pcnt[e] - pcnt[a];
+        uint64_t sa, se;
+        int ca, ce;
+        prefix(a, sa, ca);
+        prefix(e, se, ce);
+        const uint64_t ssum = se - sa;
+        const int m = ce - ca;
         sega[sg] = isqrt_u64((ssum / (uint64_t)(e - a)) << 16) * (uint64_t)m;
         segm[sg] = m > 0 ? m : -1;  // -m-1: capped (an empty segment keeps its 0)
     }
