@@ -938,16 +938,6 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
     uint64_t *psum = ws.psum + (size_t)b * (ms + 1);
     int32_t *pcnt = ws.pcnt + (size_t)b * (ms + 1);
 
-    // C. pivotal candidates
-    int my_piv = 0;
-    for (int k = tid; k < n; k += SEL_THREADS) {
-        if ((double)sfx[k] * (double)n > (double)pivot_c * (double)so.s_all) {
-            ob[k] = 0u;
-            ++my_piv;
-        }
-    }
-    const long n_piv = (long)block_sum_u64((uint64_t)my_piv, wave_u64);
-    const long T = max((long)keep_k[b] - n_piv, 0L);
 
     // A. a run of at least min_seg candidates opens a segment, a shorter one
     //    merges into the segment before it: a block prefix over the runs
@@ -990,6 +980,20 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
     __shared__ uint64_t chunk_ex[TAM_FAST / 64];
     const bool fast = n <= TAM_FAST;
     uint64_t total_packed = 0;
+    // C. pivotal candidates (s N > c S, in doubles): their order bits become
+    //    0, so they are neither dropped nor counted as droppable.  In the
+    //    one-pass sums the test is taken as each candidate is loaded.
+    const double piv_rhs = (double)pivot_c * (double)so.s_all;
+    int my_piv = 0;
+    if (!fast) {
+        for (int k = tid; k < n; k += SEL_THREADS) {
+            if ((double)sfx[k] * (double)n > piv_rhs) {
+                ob[k] = 0u;
+                ++my_piv;
+            }
+        }
+        __syncthreads();
+    }
     if (fast) {
         for (int i = tid; i < (n + 31) / 32; i += SEL_THREADS) segbits[i] = 0u;
         __syncthreads();
@@ -1007,7 +1011,12 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
                 for (int u = 0; u < HALF; ++u) {
                     const int k = wb + 64 * (h + u) + lane;
                     const uint32_t sv = ld_clamped(sfx, k, n, 0u), ov = ld_clamped(ob, k, n, 0u);
-                    v[u] = k < n ? ((uint64_t)sv | ((uint64_t)(ov != 0u ? 1 : 0) << 48)) : 0ull;
+                    const bool piv = k < n && (double)sv * (double)n > piv_rhs;
+                    if (piv) {
+                        ob[k] = 0u;
+                        ++my_piv;
+                    }
+                    v[u] = k < n ? ((uint64_t)sv | ((uint64_t)(ov != 0u && !piv ? 1 : 0) << 48)) : 0ull;
                 }
 #pragma unroll
                 for (int u = 0; u < HALF; ++u) {
@@ -1067,6 +1076,8 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_tam_prep(kvq_cache c, const
         }
     }
     __syncthreads();
+    const long n_piv = (long)block_sum_u64((uint64_t)my_piv, wave_u64);
+    const long T = max((long)keep_k[b] - n_piv, 0L);
     // (sum of s, droppable count) before candidate k, k a segment start or n
     auto prefix = [&](int k, uint64_t &sum, int &cnt) {
         if (fast) {
