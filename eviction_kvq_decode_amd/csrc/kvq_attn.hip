@@ -873,8 +873,13 @@ constexpr long SPLIT_GAP = 10;
 // SPLIT_MIN units of cost space; the rest get empty ranges.  Every range adds
 // a partial that the finalize merges per head, in rounds of dependent loads:
 // a 64-entry list over 512 ranges of one entry or none cost the finalize
-// about 14 such rounds per output row.
+// about 14 such rounds per output row.  And below SPLIT_SHARED units per
+// workgroup of the full grid, a second workgroup on a compute unit gains
+// less than its partials cost: the list goes to the first-dispatched
+// workgroups only, one per unit (a 32768-position sequence 48.6 -> 38.3 us;
+// 16 to 32 units per workgroup lost 3-4 us when capped).
 constexpr int SPLIT_MIN = 4;
+constexpr int SPLIT_SHARED = 16;
 __device__ inline int split_start(long N, int NW, int n_first, int j) {
     if (n_first >= NW) return (int)(N * j / NW);
     const long A = 64 + SPLIT_SKEW, Bw = 64 - SPLIT_SKEW;
@@ -889,8 +894,8 @@ __device__ inline int split_start(long N, int NW, int n_first, int j) {
 // n_packs * (table entries of the sequences before it).  Workgroup j of the
 // NW in the grid (what fits on the GPU at once) takes the contiguous range
 // [split_start(j), split_start(j + 1)) of the N entries (over the first
-// NWe <= NW workgroups, see SPLIT_MIN; the others take empty ranges at the
-// end), with no scheduling traffic, and records its start for the finalize.  Where its range crosses
+// NWe <= NW workgroups, see SPLIT_MIN and SPLIT_SHARED; the others take
+// empty ranges at the end), with no scheduling traffic, and records its start for the finalize.  Where its range crosses
 // a (sequence, pack) boundary it writes one partial per side; the partial
 // of workgroup j for unit u = b n_packs + p sits in slot j + u (unique,
 // since both j and u grow along the list).
@@ -951,7 +956,8 @@ __global__ __launch_bounds__(WAVES * 64, KVQ_MIN_WAVES_PER_SIMD) void attn_split
     if (tid < 128) {
         const int wv = tid >> 6, lane = tid & 63;
         const int NC = (int)N + c.B * n_packs * (int)SPLIT_GAP;
-        const int NWe = min(NW, max(1, (NC + SPLIT_MIN - 1) / SPLIT_MIN));
+        int NWe = min(NW, max(1, (NC + SPLIT_MIN - 1) / SPLIT_MIN));
+        if (NC < SPLIT_SHARED * NW) NWe = min(NWe, n_first);
         const int cpos = j + wv >= NWe ? NC : split_start(NC, NWe, min(n_first, NWe), j + wv);
         int cnt = 0;
         for (int b0 = 0; b0 < c.B; b0 += 64) {
