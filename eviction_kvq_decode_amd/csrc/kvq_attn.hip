@@ -1109,7 +1109,7 @@ __device__ inline void head_stats(const DecodeWs &ws, const int *rs, int NW, int
     }
 }
 
-__global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
+__global__ __launch_bounds__(FT, 6) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
                                                     float decay, DecodeWs ws, int NW, int G, int P, int n_packs) {
     const int j = blockIdx.x, W = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1201,6 +1201,20 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
             // a position outside the row stride (a corrupt cache) is skipped
             if (pos[q] < 0 || pos[q] >= c.n_cap) valid[q] = false;
         }
+        // -- the first pack's score rows and the old importance of the valid
+        //    slots, issued before the partials are merged so that the two
+        //    sets of loads are in flight together
+        const float *const score_b = ws.score + (size_t)b * n_packs * c.max_blocks * 256;
+        float4 sv0[FB];
+        float imp_old[FB];
+#pragma unroll
+        for (int q = 0; q < FB; ++q)
+            sv0[q] = valid[q] ? reinterpret_cast<const float4 *>(score_b + (size_t)(e0 + q) * 256)[t * 4 + hq]
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (importance && hq == 0) {
+#pragma unroll
+            for (int q = 0; q < FB; ++q) imp_old[q] = valid[q] ? importance[(size_t)b * c.n_cap + pos[q]] : 0.f;
+        }
         // (no barrier before: the statistics of the item before last, in
         // this buffer, were read before the last item's barrier below, so
         // the loads above stay in flight while the partials are merged)
@@ -1209,12 +1223,6 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
 
         // -- mass (and importance) of the valid slots
         {
-            float imp_old[FB];
-            if (importance && hq == 0) {
-#pragma unroll
-                for (int q = 0; q < FB; ++q) imp_old[q] = valid[q] ? importance[(size_t)b * c.n_cap + pos[q]] : 0.f;
-            }
-            const float *const score_b = ws.score + (size_t)b * n_packs * c.max_blocks * 256;
             float acc[FB];
 #pragma unroll
             for (int q = 0; q < FB; ++q) acc[q] = 0.f;
@@ -1222,7 +1230,8 @@ __global__ __launch_bounds__(FT) void attn_finalize(kvq_cache c, float *out, flo
                 float4 sv[FB];
 #pragma unroll
                 for (int q = 0; q < FB; ++q)
-                    sv[q] = valid[q] ? reinterpret_cast<const float4 *>(
+                    sv[q] = p == 0 ? sv0[q]
+                          : valid[q] ? reinterpret_cast<const float4 *>(
                                            score_b + ((size_t)p * c.max_blocks + e0 + q) * 256)[t * 4 + hq]
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
                 const int np = min(P, c.Hkv - p * P);
