@@ -895,8 +895,9 @@ __device__ inline int split_start(long N, int NW, int n_first, int j) {
 // NW in the grid (what fits on the GPU at once) takes the contiguous range
 // [split_start(j), split_start(j + 1)) of the N entries (over the first
 // NWe <= NW workgroups, see SPLIT_MIN and SPLIT_SHARED; the others take
-// empty ranges at the end), with no scheduling traffic, and records its start for the finalize.  Where its range crosses
-// a (sequence, pack) boundary it writes one partial per side; the partial
+// empty ranges at the end), with no scheduling traffic, and records its
+// start for the finalize.  Where its range crosses a (sequence, pack)
+// boundary it writes one partial per side; the partial
 // of workgroup j for unit u = b n_packs + p sits in slot j + u (unique,
 // since both j and u grow along the list).
 // NATIVE: the cache holds the native codec (Reasoning and Execution blocks
@@ -1058,6 +1059,10 @@ __device__ inline int range_owner(const int *rs, int NW, int f) {
 constexpr int FT = 256;
 constexpr int FB = 4;                 // entries a wave takes per item
 constexpr int FC = FB * (FT / 64);    // entries per item
+// resident finalize workgroups per compute unit at most; a workgroup's FT / 64
+// waves spread over the unit's four SIMDs, so this is also the waves per SIMD
+// the kernel's registers must allow
+constexpr int FIN_PER_CU = 6;
 
 // M_h and 1 / L_h of every head of sequence b (whose split-list entries
 // start at pre and number n_packs x nb), into Mh / Rh: tpg lanes per head,
@@ -1109,7 +1114,7 @@ __device__ inline void head_stats(const DecodeWs &ws, const int *rs, int NW, int
     }
 }
 
-__global__ __launch_bounds__(FT, 6) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
+__global__ __launch_bounds__(FT, FIN_PER_CU) void attn_finalize(kvq_cache c, float *out, float *mass, float *importance,
                                                     float decay, DecodeWs ws, int NW, int G, int P, int n_packs) {
     const int j = blockIdx.x, W = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1348,7 +1353,7 @@ int finalize_grid() {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(attn_finalize),
                                                          FT, 0) != hipSuccess)
             return 0;
-        v = cus * std::max(1, std::min(per_cu, 6));
+        v = cus * std::max(1, std::min(per_cu, FIN_PER_CU));
     }
     return v;
 }
