@@ -306,3 +306,31 @@ def test_maximum_batch_many_short_sequences():
     ref2, got2 = _decode(oc, gc, q2)
     assert_attention_close(ref2, got2)
     assert_mass_close(oc.st["seq_len"], ref2, got2)
+
+
+def test_one_long_sequence_many_ranges():
+    """One 16384-position sequence with 60% of its slots evicted (B=1, Hq=32,
+    Hkv=8: two kv-head packs of about 490 table entries after the blocks the
+    eviction emptied are freed).  The list is short against the split grid,
+    so it goes to at most one workgroup per compute unit in ranges of at
+    least 4 entries, about 125 ranges per pack, and the finalize merges each
+    head's partials over 4 rounds of loads, in the head statistics and in the
+    output rows.  Output, mass and importance against the oracle, then again
+    after an append into the holes."""
+    from pairs import Pair
+
+    log("[edge] one long sequence, many split ranges")
+    w = wl.scaled(wl.WORKLOADS["long_evicted"], B=1, n_min=16384, n_max=16384)
+    p = Pair(w)
+    p.fill()
+    assert_same_cache(p.oc, p.gc.state_numpy())
+    rng = np.random.default_rng(16384)
+    imp = rng.exponential(1.0, size=(1, p.g.n_cap)).astype(np.float32)
+    ref, got = p.decode(wl.queries(w, 0), imp, 0.9)
+    assert_attention_close(ref, got)
+    assert_mass_close(p.oc.st["seq_len"], ref, got)
+    assert abs(got[1][0, : p.oc.st["seq_len"][0]].sum() - w.Hq) < 1e-3
+    p.append_step(0)
+    ref, got = p.decode(wl.queries(w, 1))
+    assert_attention_close(ref, got)
+    assert_mass_close(p.oc.st["seq_len"], ref, got)
