@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
         assert re.search(rf"\bT {n}$", nm, re.M), n
 
 
-def test_survey_boundary_calls_exported():
+def test_boundary_calls_exported():
     """The calls the hot path's boundary is drawn with: append + quantise,
     the decode with its workspace size, windowed top-k eviction."""
     L = kvq.lib()
