@@ -559,7 +559,7 @@ __device__ inline void tbe_segment(const uint32_t *ob, const int32_t *ord, uint6
     } else {
         // any length: radix select on 8-bit digits from the top, one
         // 256-bin LDS histogram per wave (hist), 4 passes over the values
-        // and one for the verdicts.  need = how many of the values that
+        // and one for the keep or drop decisions.  need = how many of the values that
         // match the digits chosen so far are still to be kept.
         int need = keep;
         uint32_t pre = 0, pre_mask = 0;
